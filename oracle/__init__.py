@@ -1,0 +1,148 @@
+"""CPU oracle for the KDA verify-row scan (test infrastructure only).
+
+Only the tests, the smoke check and the bench's CPU-baseline leg use this
+package.  It wraps ``kda_oracle.c`` -- a plain, scalar, f64 restatement of the
+recurrence (see that file's header for the definition and its sources) --
+with numpy arrays in and out.  It imports nothing from the HIP library and
+the HIP library imports nothing from it.
+
+Functions
+---------
+scan_rows(s_in, q, k, v, g, beta, T=None, want_o=True, threads=1)
+    Scan rows 0..T-1 of every (layer, head) chain; returns (s_out, o).
+replay(snap, q, k, v, g, beta, keep, threads=1)
+    The state after rows 0..keep-1, rebuilt from the pre-round snapshot.
+batched(states, q, k, v, g, beta, want_o=True, threads=1)
+    B independent sessions, one row each; returns (new_states, o).
+
+Inputs are float32 arrays, or uint16 arrays holding bf16 bit patterns (all
+five row inputs in the same dtype); the oracle widens bf16 itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+
+D = 128
+
+_lib = None
+
+
+def build(out: str = _LIB) -> str:
+    """Compile the oracle with gcc (strict IEEE: no fast-math, no contraction)."""
+    cmd = [
+        "gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-pthread",
+        "-fno-fast-math", "-ffp-contract=off", "-fno-strict-aliasing",
+        _SRC, "-o", out + ".tmp", "-lm", "-lpthread",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def load():
+    """Load the built oracle library, building it first only if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    p = ctypes.c_void_p
+    i = ctypes.c_int
+    lib.kda_oracle_scan_rows.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, i, i, i]
+    lib.kda_oracle_scan_rows.restype = i
+    lib.kda_oracle_batched.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i]
+    lib.kda_oracle_batched.restype = i
+    lib.kda_oracle_version.restype = i
+    lib.kda_oracle_max_threads.restype = i
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rows(q, k, v, g, beta):
+    arrs = [np.ascontiguousarray(x) for x in (q, k, v, g, beta)]
+    dt = arrs[0].dtype
+    if any(a.dtype != dt for a in arrs):
+        raise TypeError("q, k, v, g, beta must share one dtype")
+    if dt == np.float32:
+        bf16 = 0
+    elif dt == np.uint16:
+        bf16 = 1
+    else:
+        raise TypeError(f"oracle inputs must be float32 or uint16 (bf16 bits), got {dt}")
+    return arrs, bf16
+
+
+def scan_rows(s_in, q, k, v, g, beta, T=None, want_o=True, threads=1):
+    """Scan the first T rows of q/k/v/g [L][T_stride][H][d] and beta [L][T_stride][H].
+
+    s_in: [L][H][d][d] float32 (not modified).  Returns (s_out, o) with o of
+    shape [L][T][H][d] (None when want_o is False).
+    """
+    lib = load()
+    (q, k, v, g, beta), bf16 = _rows(q, k, v, g, beta)
+    s_in = np.ascontiguousarray(s_in, dtype=np.float32)
+    L, T_stride, H, d = q.shape
+    if T is None:
+        T = T_stride
+    if not (0 <= T <= T_stride):
+        raise ValueError("T outside 0..T_stride")
+    if s_in.shape != (L, H, d, d) or beta.shape != (L, T_stride, H):
+        raise ValueError("shape mismatch")
+    for x in (k, v, g):
+        if x.shape != q.shape:
+            raise ValueError("shape mismatch")
+    s_out = np.empty_like(s_in)
+    o = np.empty((L, T, H, d), np.float32) if want_o else None
+    rc = lib.kda_oracle_scan_rows(
+        _ptr(s_in), _ptr(s_out), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o),
+        L, T_stride, T, H, d, bf16, int(threads))
+    if rc != 0:
+        raise MemoryError("oracle work buffer allocation failed")
+    return s_out, o
+
+
+def replay(snap, q, k, v, g, beta, keep, threads=1):
+    """State after rows 0..keep-1 of the round, rebuilt from the snapshot; no outputs."""
+    s_out, _ = scan_rows(snap, q, k, v, g, beta, T=keep, want_o=False, threads=threads)
+    return s_out
+
+
+def batched(states, q, k, v, g, beta, want_o=True, threads=1):
+    """Batched arm.  states: [L][B][H][d][d] float32; rows [L][B][H][d]; beta [L][B][H].
+
+    Returns (new_states, o) without modifying the input array.
+    """
+    lib = load()
+    (q, k, v, g, beta), bf16 = _rows(q, k, v, g, beta)
+    L, B, H, d = q.shape
+    st = np.array(states, dtype=np.float32, copy=True, order="C")
+    if st.shape != (L, B, H, d, d) or beta.shape != (L, B, H):
+        raise ValueError("shape mismatch")
+    table = (ctypes.c_void_p * (L * B))()
+    base = st.ctypes.data
+    for lb in range(L * B):
+        table[lb] = base + lb * H * d * d * 4
+    o = np.empty((L, B, H, d), np.float32) if want_o else None
+    rc = lib.kda_oracle_batched(
+        ctypes.cast(table, ctypes.c_void_p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(o), L, B, H, d, bf16, int(threads))
+    if rc != 0:
+        raise MemoryError("oracle work buffer allocation failed")
+    return st, o
+
+
+def max_threads() -> int:
+    return int(load().kda_oracle_max_threads())

@@ -1,0 +1,272 @@
+/*
+ * kda_oracle.c -- plain sequential CPU reference for the KDA verify-row scan.
+ *
+ * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only the test suite, the
+ * smoke check and the bench's CPU-baseline leg may load this library.  It
+ * shares no source, header, table or helper with the HIP library: it is the
+ * recurrence written out from its definition, scalar, one row after another.
+ *
+ * What it computes (one chain = one (session, layer, head)):
+ *   The state S is a d x d f32 matrix, S[i][j], i = key channel (decayed and
+ *   reduced over), j = value channel.  Each verify row t with inputs
+ *   q_t, k_t, v_t, g_t (d-vectors) and beta_t (scalar) does
+ *       gc_i  = min(max(g_t[i], -5), 0)            (clamp in f32)
+ *       S'    = diag(exp(gc)) S                    (decay per key channel)
+ *       u     = S'^T k_t                           (u_j = sum_i k_i S'_ij)
+ *       S_new = S' + beta_t k_t (v_t - u)^T        (delta-rule write)
+ *       o_t   = S_new^T q_t / sqrt(d)              (read from the updated S)
+ *   all in f64, with S rounded to f32 at the end of every row.
+ *
+ *   Sources.  memra-engine 0.123.0 glm_spec.rs (docs.rs source page): the
+ *   module doc's VERIFY-ROW BATCHING section says the t=K+1 recurrence runs
+ *   sequentially and equals the chained t=1 program; its ROLLBACK section and
+ *   the Glm5VerifyCkpt doc give the snapshot-before-row-0 plus replay of rows
+ *   0..keep-1.  glm5_spec_ppn_gate.rs (same crate) fixes head_dim 128 and
+ *   gate_lower_bound -5.0 in its mini fixture config.  The pages name the scan
+ *   kernel but never print its recurrence; the update rule, the upper clamp
+ *   bound 0 and the 1/sqrt(d) output scale are the delta-rule reading stated
+ *   above (plain reading; the pages are silent).
+ *
+ *   bf16 inputs are widened exactly, bits << 16, as dflash.rs (memra-engine
+ *   0.98.0, fn bf16_to_f32) does on the host.
+ *
+ * Layouts (row-major, contiguous):
+ *   state           [L][H][d][d] f32
+ *   q, k, v, g      [L][T_stride][H][d]   f32 or bf16 bits
+ *   beta            [L][T_stride][H]      f32 or bf16 bits
+ *   o               [L][T][H][d] f32 (T rows scanned; may be NULL)
+ *   batched arm:    rows [L][B][H][d], beta [L][B][H], o [L][B][H][d],
+ *                   states given as a host pointer table [L*B] -> [H][d][d].
+ *
+ * Threads: chains are independent, so the multi-chain entry points may run
+ * chains on several POSIX threads; each chain's rows stay strictly
+ * sequential on one thread.
+ */
+#define _POSIX_C_SOURCE 200809L
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <pthread.h>
+#include <unistd.h>
+
+#define ORACLE_GATE_LO (-5.0f) /* gate_lower_bound of the glm5_next fixture */
+#define ORACLE_GATE_HI (0.0f)  /* a log-decay never grows the state */
+
+/* Exact bf16 -> f32: the 16 bf16 bits become the high half of the f32. */
+static float widen_bf16(uint16_t bits) {
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static float fetch(const void* base, long idx, int in_bf16) {
+    if (in_bf16) return widen_bf16(((const uint16_t*)base)[idx]);
+    return ((const float*)base)[idx];
+}
+
+/* Clamp in f32, as the gate bound is an f32 constant of the model config. */
+static float clamp_gate(float g) {
+    float x = g;
+    if (x < ORACLE_GATE_LO) x = ORACLE_GATE_LO;
+    if (x > ORACLE_GATE_HI) x = ORACLE_GATE_HI;
+    return x;
+}
+
+/*
+ * One chain: T rows, sequential.  S (d*d f32) is read and written in place.
+ * Row t's vectors start at element offset t*row_stride of q/k/v/g and its
+ * beta at t*beta_stride.  o (if not NULL) gets row t at o + t*o_stride.
+ * work must hold d*d + 3*d doubles.
+ */
+static void chain(float* S, const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, int in_bf16, long row_stride, long beta_stride, int T,
+                  int d, float* o, long o_stride, double* work) {
+    double* Sp = work;            /* d*d: decayed, then updated state (f64) */
+    double* u = work + (long)d * d;
+    double* e = u + d;
+    double* dec = e + d;
+    const double inv_norm = 1.0 / sqrt((double)d);
+    for (int t = 0; t < T; ++t) {
+        const long rb = (long)t * row_stride;
+        const double b = (double)fetch(beta, (long)t * beta_stride, in_bf16);
+        /* decay per key channel */
+        for (int i = 0; i < d; ++i) dec[i] = exp((double)clamp_gate(fetch(g, rb + i, in_bf16)));
+        for (int i = 0; i < d; ++i)
+            for (int j = 0; j < d; ++j) Sp[(long)i * d + j] = dec[i] * (double)S[(long)i * d + j];
+        /* u = S'^T k, summed over ascending key index */
+        for (int j = 0; j < d; ++j) u[j] = 0.0;
+        for (int i = 0; i < d; ++i) {
+            const double ki = (double)fetch(k, rb + i, in_bf16);
+            for (int j = 0; j < d; ++j) u[j] += ki * Sp[(long)i * d + j];
+        }
+        /* e = beta (v - u) */
+        for (int j = 0; j < d; ++j) e[j] = b * ((double)fetch(v, rb + j, in_bf16) - u[j]);
+        /* S_new = S' + k e^T */
+        for (int i = 0; i < d; ++i) {
+            const double ki = (double)fetch(k, rb + i, in_bf16);
+            for (int j = 0; j < d; ++j) Sp[(long)i * d + j] += ki * e[j];
+        }
+        /* o = S_new^T q / sqrt(d), from the updated state */
+        if (o) {
+            for (int j = 0; j < d; ++j) u[j] = 0.0;
+            for (int i = 0; i < d; ++i) {
+                const double qi = (double)fetch(q, rb + i, in_bf16);
+                for (int j = 0; j < d; ++j) u[j] += qi * Sp[(long)i * d + j];
+            }
+            for (int j = 0; j < d; ++j) o[(long)t * o_stride + j] = (float)(u[j] * inv_norm);
+        }
+        /* the state is f32: round once per row */
+        for (long x = 0; x < (long)d * d; ++x) S[x] = (float)Sp[x];
+    }
+}
+
+int kda_oracle_version(void) { return 1; }
+
+/* Element size in bytes of an input tensor. */
+static long esz(int in_bf16) { return in_bf16 ? 2 : 4; }
+
+/* Where one chain's data lives. */
+typedef struct {
+    float* S;
+    const char *q, *k, *v, *g, *beta;
+    long row_stride, beta_stride;
+    int T;
+    float* o;
+    long o_stride;
+} chain_ref;
+
+/* A chain set: either the [L][H] scan layout or the batched [L][B][H] layout. */
+typedef struct {
+    int batched;
+    float* s_out;
+    float* const* states;
+    const void *q, *k, *v, *g, *beta;
+    float* o;
+    int L, T_stride, T, B, H, d, in_bf16;
+} chain_set;
+
+static chain_ref locate(const chain_set* cs, long c) {
+    chain_ref r;
+    const long d = cs->d, dd = d * d, e = esz(cs->in_bf16);
+    if (!cs->batched) {
+        const long l = c / cs->H, h = c % cs->H;
+        const long row0 = (l * cs->T_stride * cs->H + h) * d; /* element offset of row 0 */
+        const long b0 = l * cs->T_stride * cs->H + h;
+        r.S = cs->s_out + c * dd;
+        r.q = (const char*)cs->q + row0 * e;
+        r.k = (const char*)cs->k + row0 * e;
+        r.v = (const char*)cs->v + row0 * e;
+        r.g = (const char*)cs->g + row0 * e;
+        r.beta = (const char*)cs->beta + b0 * e;
+        r.row_stride = (long)cs->H * d;
+        r.beta_stride = cs->H;
+        r.T = cs->T;
+        r.o = cs->o ? cs->o + (l * cs->T * cs->H + h) * d : NULL;
+        r.o_stride = (long)cs->H * d;
+    } else {
+        const long lb = c / cs->H, h = c % cs->H;
+        const long row0 = c * d;
+        r.S = cs->states[lb] + h * dd;
+        r.q = (const char*)cs->q + row0 * e;
+        r.k = (const char*)cs->k + row0 * e;
+        r.v = (const char*)cs->v + row0 * e;
+        r.g = (const char*)cs->g + row0 * e;
+        r.beta = (const char*)cs->beta + c * e;
+        r.row_stride = d;
+        r.beta_stride = 1;
+        r.T = 1;
+        r.o = cs->o ? cs->o + row0 : NULL;
+        r.o_stride = d;
+    }
+    return r;
+}
+
+typedef struct {
+    const chain_set* cs;
+    long nchain;
+    int tid, nthreads;
+    int fail;
+} worker_arg;
+
+/* Thread `tid` runs chains tid, tid + n, tid + 2n, ...; each chain on one thread. */
+static void* worker(void* p) {
+    worker_arg* a = (worker_arg*)p;
+    const long d = a->cs->d;
+    double* work = (double*)malloc(sizeof(double) * (d * d + 3 * d));
+    if (!work) {
+        a->fail = 1;
+        return NULL;
+    }
+    for (long c = a->tid; c < a->nchain; c += a->nthreads) {
+        chain_ref r = locate(a->cs, c);
+        chain(r.S, r.q, r.k, r.v, r.g, r.beta, a->cs->in_bf16, r.row_stride, r.beta_stride, r.T,
+              (int)d, r.o, r.o_stride, work);
+    }
+    free(work);
+    return NULL;
+}
+
+static int run_chains(const chain_set* cs, long nchain, int threads) {
+    if (threads < 1) threads = 1;
+    if (threads > 256) threads = 256;
+    if ((long)threads > nchain) threads = nchain > 0 ? (int)nchain : 1;
+    worker_arg args[256];
+    pthread_t tids[256];
+    int started[256];
+    int fail = 0;
+    for (int t = 0; t < threads; ++t) {
+        args[t].cs = cs;
+        args[t].nchain = nchain;
+        args[t].tid = t;
+        args[t].nthreads = threads;
+        args[t].fail = 0;
+        started[t] = 0;
+    }
+    for (int t = 1; t < threads; ++t)
+        started[t] = pthread_create(&tids[t], NULL, worker, &args[t]) == 0;
+    /* chains of a thread that failed to start run here, after thread 0's own */
+    worker(&args[0]);
+    for (int t = 1; t < threads; ++t) {
+        if (started[t])
+            pthread_join(tids[t], NULL);
+        else
+            worker(&args[t]);
+        fail |= args[t].fail;
+    }
+    fail |= args[0].fail;
+    return fail ? -1 : 0;
+}
+
+/*
+ * Scan T rows (T <= T_stride) of L x H independent chains.
+ * s_out receives the state after the T rows (s_in is left untouched unless
+ * s_out == s_in).  o may be NULL.  Returns 0, or -1 if a work buffer could
+ * not be allocated.
+ */
+int kda_oracle_scan_rows(const float* s_in, float* s_out, const void* q, const void* k,
+                         const void* v, const void* g, const void* beta, float* o, int L,
+                         int T_stride, int T, int H, int d, int in_bf16, int threads) {
+    const long nchain = (long)L * H;
+    if (s_out != s_in) memcpy(s_out, s_in, sizeof(float) * (long)d * d * nchain);
+    chain_set cs = {0, s_out, NULL, q, k, v, g, beta, o, L, T_stride, T, 0, H, d, in_bf16};
+    return run_chains(&cs, nchain, threads);
+}
+
+/*
+ * Batched arm: B sessions, one row each, per layer.  states[l*B + b] points at
+ * session b's layer-l state [H][d][d], updated in place.
+ */
+int kda_oracle_batched(float* const* states, const void* q, const void* k, const void* v,
+                       const void* g, const void* beta, float* o, int L, int B, int H, int d,
+                       int in_bf16, int threads) {
+    chain_set cs = {1, NULL, states, q, k, v, g, beta, o, L, 1, 1, B, H, d, in_bf16};
+    return run_chains(&cs, (long)L * B * H, threads);
+}
+
+/* Host threads available to the multi-chain entry points. */
+int kda_oracle_max_threads(void) {
+    long n = sysconf(_SC_NPROCESSORS_ONLN);
+    return n > 0 ? (int)n : 1;
+}

@@ -1,0 +1,87 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each case edits one line of the oracle's C source (a dropped term, a wrong
+sign, a transposed operand, a wrong bound, scale or stride), compiles that
+mutant into a temporary library on the CPU, swaps it in, and checks that at
+least one pin in test_oracle_pins fails.  The real oracle is never touched.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "kda_oracle.c")
+
+# (name, original text, mutated text)
+MUTANTS = [
+    ("decay dropped", "dec[i] = exp((double)clamp_gate(fetch(g, rb + i, in_bf16)));", "dec[i] = 1.0;"),
+    ("lower clamp -4", "#define ORACLE_GATE_LO (-5.0f)", "#define ORACLE_GATE_LO (-4.0f)"),
+    ("upper clamp missing", "if (x > ORACLE_GATE_HI) x = ORACLE_GATE_HI;", ""),
+    ("delta sign", "((double)fetch(v, rb + j, in_bf16) - u[j])", "((double)fetch(v, rb + j, in_bf16) + u[j])"),
+    ("beta dropped", "e[j] = b * (", "e[j] = ("),
+    ("u transposed", "for (int j = 0; j < d; ++j) u[j] += ki * Sp[(long)i * d + j];",
+     "for (int j = 0; j < d; ++j) u[j] += ki * Sp[(long)j * d + i];"),
+    ("update transposed", "Sp[(long)i * d + j] += ki * e[j];", "Sp[(long)j * d + i] += ki * e[j];"),
+    ("o from pre-update state", "u[j] += qi * Sp[(long)i * d + j];", "u[j] += qi * (double)S[(long)i * d + j];"),
+    ("o scale 1/d", "1.0 / sqrt((double)d)", "1.0 / (double)d"),
+    ("row stride", "r.row_stride = (long)cs->H * d;", "r.row_stride = d;"),
+    ("beta stride", "fetch(beta, (long)t * beta_stride, in_bf16)", "fetch(beta, (long)t, in_bf16)"),
+    ("bf16 widen shift", "((uint32_t)bits) << 16", "((uint32_t)bits) << 15"),
+    ("o row stride", "o[(long)t * o_stride + j]", "o[(long)t * d + j]"),
+]
+
+PIN_TESTS = [
+    lambda: pins.test_identity_beta0_g0_leaves_state_and_reads_it(),
+    lambda: pins.test_decay_closed_form(),
+    lambda: pins.test_clamp_bounds_are_exactly_minus5_and_0(),
+    lambda: pins.test_one_hot_key_writes_value_into_that_key_row(),
+    lambda: pins.test_associative_memory_with_orthonormal_keys(),
+    lambda: [pins.test_exact_rational_d4(s) for s in range(3)],
+    lambda: [pins.test_matrix_form_with_decay(*a) for a in [(4, 6, 0), (8, 9, 2)]],
+    lambda: pins.test_chains_are_independent_and_layout_strides_are_right(),
+    lambda: pins.test_bf16_widening_matches_ieee_table(),
+]
+
+
+def _build_mutant(tmp_path, name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for '{name}' not found"
+    mutated = src.replace(old, new, 1)
+    c = tmp_path / "mutant.c"
+    so = tmp_path / "libmutant.so"
+    c.write_text(mutated)
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
+                    str(c), "-o", str(so), "-lm", "-lpthread"], check=True)
+    return str(so)
+
+
+def _swap_in(path):
+    lib = ctypes.CDLL(path)
+    real = oracle.load()
+    for fn in ("kda_oracle_scan_rows", "kda_oracle_batched", "kda_oracle_version",
+               "kda_oracle_max_threads"):
+        getattr(lib, fn).argtypes = getattr(real, fn).argtypes
+        getattr(lib, fn).restype = getattr(real, fn).restype
+    return lib
+
+
+def test_unmutated_oracle_passes_every_pin():
+    for pin in PIN_TESTS:
+        pin()
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, monkeypatch, name, old, new):
+    lib = _swap_in(_build_mutant(tmp_path, name, old, new))
+    monkeypatch.setattr(oracle, "_lib", lib)
+    caught = 0
+    for pin in PIN_TESTS:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin catches the mutant '{name}'"

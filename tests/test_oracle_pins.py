@@ -1,0 +1,336 @@
+"""Pins for the CPU oracle: closed forms, invariants, exact and brute-force cases.
+
+Each test ties the oracle to something other than itself: exact rational
+arithmetic, an independent matrix form of the update, an IEEE closed form, a
+numpy routine, or a property the delta rule must have.  Together they are
+meant to fail for a dropped term, a wrong sign, a transposed operand, the
+wrong clamp bound, the wrong output scale, o read before the update, or a
+wrong layout stride.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+F32_EPS = 2.0 ** -23  # f32 ulp at 1.0
+
+
+def _rand_rows(rng, L, T, H, d, gmin=-5.0, gmax=0.0):
+    q = rng.standard_normal((L, T, H, d))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k = rng.standard_normal((L, T, H, d))
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((L, T, H, d))
+    g = rng.uniform(gmin, gmax, (L, T, H, d))
+    beta = rng.uniform(0.0, 1.0, (L, T, H))
+    f = lambda a: a.astype(np.float32)
+    return f(q), f(k), f(v), f(g), f(beta)
+
+
+# ---------------------------------------------------------------- identity / decay / clamp
+
+def test_identity_beta0_g0_leaves_state_and_reads_it():
+    rng = np.random.default_rng(10)
+    d, T = 128, 5
+    S0 = rng.standard_normal((1, 1, d, d)).astype(np.float32)
+    q, k, v, _, _ = _rand_rows(rng, 1, T, 1, d)
+    g = np.zeros_like(q)
+    beta = np.zeros((1, T, 1), np.float32)
+    S, o = oracle.scan_rows(S0, q, k, v, g, beta)
+    assert np.array_equal(S.view(np.uint32), S0.view(np.uint32))
+    for t in range(T):
+        ref = S0[0, 0].astype(np.float64).T @ q[0, t, 0].astype(np.float64) / np.sqrt(d)
+        np.testing.assert_allclose(o[0, t, 0], ref, rtol=0, atol=4 * F32_EPS * np.abs(ref).max())
+
+
+def test_decay_closed_form():
+    # beta = 0: S_T[i][j] = exp(sum_t clamp(g_t[i])) * S_0[i][j]
+    rng = np.random.default_rng(11)
+    d, T = 128, 15
+    S0 = rng.standard_normal((1, 1, d, d)).astype(np.float32)
+    q, k, v, g, _ = _rand_rows(rng, 1, T, 1, d, gmin=-7.0, gmax=1.0)  # some out of range
+    beta = np.zeros((1, T, 1), np.float32)
+    S, _ = oracle.scan_rows(S0, q, k, v, g, beta, want_o=False)
+    gc = np.clip(g[0, :, 0].astype(np.float64), -5.0, 0.0).sum(axis=0)
+    ref = np.exp(gc)[:, None] * S0[0, 0].astype(np.float64)
+    rel = np.abs(S[0, 0] - ref) / np.maximum(np.abs(ref), 1e-30)
+    # one f32 rounding per row plus the f64 exps: well inside (T+1) half-ulps
+    assert rel.max() <= (T + 1) * 0.5 * F32_EPS * 1.01
+
+
+def test_clamp_bounds_are_exactly_minus5_and_0():
+    rng = np.random.default_rng(12)
+    d, T = 128, 6
+    S0 = rng.standard_normal((1, 1, d, d)).astype(np.float32)
+    q, k, v, _, beta = _rand_rows(rng, 1, T, 1, d)
+    def run(gval):
+        g = np.full_like(q, gval)
+        return oracle.scan_rows(S0, q, k, v, g, beta)
+    for a, b in ((0.7, 0.0), (-9.0, -5.0), (3.0e30, 0.0), (-1.0e30, -5.0)):
+        Sa, oa = run(a)
+        Sb, ob = run(b)
+        assert np.array_equal(Sa.view(np.uint32), Sb.view(np.uint32))
+        assert np.array_equal(oa.view(np.uint32), ob.view(np.uint32))
+    # and inside the range the gate does act
+    S1, _ = run(-1.0)
+    S0_, _ = run(0.0)
+    assert not np.array_equal(S1, S0_)
+
+
+# ---------------------------------------------------------------- writes
+
+def test_one_hot_key_writes_value_into_that_key_row():
+    rng = np.random.default_rng(13)
+    d = 128
+    for m in (0, 37, 127):
+        S0 = np.zeros((1, 1, d, d), np.float32)
+        k = np.zeros((1, 1, 1, d), np.float32); k[..., m] = 1.0
+        q = k.copy()
+        v = rng.standard_normal((1, 1, 1, d)).astype(np.float32)
+        g = np.zeros_like(k)
+        beta = np.ones((1, 1, 1), np.float32)
+        S, o = oracle.scan_rows(S0, q, k, v, g, beta)
+        assert np.array_equal(S[0, 0, m], v[0, 0, 0])          # key row m == v, bit-exact
+        others = np.delete(S[0, 0], m, axis=0)
+        assert not others.any()                               # every other key row stays 0
+        ref = v[0, 0, 0].astype(np.float64) / np.sqrt(d)
+        ulp = np.spacing(np.abs(ref).astype(np.float32))
+        assert (np.abs(o[0, 0, 0] - ref) <= ulp).all()
+
+
+def test_all_one_hot_keys_write_matrix_exactly():
+    rng = np.random.default_rng(14)
+    d = 128
+    T = d
+    S0 = np.zeros((1, 1, d, d), np.float32)
+    k = np.zeros((1, T, 1, d), np.float32)
+    perm = rng.permutation(d)
+    for t in range(T):
+        k[0, t, 0, perm[t]] = 1.0
+    v = rng.standard_normal((1, T, 1, d)).astype(np.float32)
+    S, _ = oracle.scan_rows(S0, k, k, v, np.zeros_like(k), np.ones((1, T, 1), np.float32),
+                            want_o=False)
+    V = np.empty((d, d), np.float32)
+    V[perm] = v[0, :, 0]
+    assert np.array_equal(S[0, 0], V)
+
+
+def test_associative_memory_with_orthonormal_keys():
+    # beta = 1, g = 0, orthonormal keys: after writing (k_m, v_m), S^T k_m = v_m.
+    rng = np.random.default_rng(15)
+    d, M = 128, 64
+    Q, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    keys = Q[:M].astype(np.float32)
+    vals = rng.standard_normal((M, d)).astype(np.float32)
+    S0 = np.zeros((1, 1, d, d), np.float32)
+    k = keys[None, :, None, :]
+    v = vals[None, :, None, :]
+    S, _ = oracle.scan_rows(S0, k, k, v, np.zeros_like(k), np.ones((1, M, 1), np.float32),
+                            want_o=False)
+    recall = keys.astype(np.float64) @ S[0, 0].astype(np.float64)   # row m = S^T k_m
+    # keys are orthonormal only to f32 rounding (~1e-7 per entry); the residual
+    # cross-talk over 64 writes stays below 1e-5
+    assert np.abs(recall - vals).max() < 1e-5
+
+
+def test_norm_bound_every_row():
+    # ||k|| = 1, 0 <= beta <= 1, g <= 0  =>  ||S_t||_F <= ||S_{t-1}||_F + beta_t ||v_t||
+    rng = np.random.default_rng(16)
+    d, T = 128, 15
+    S = rng.standard_normal((1, 1, d, d)).astype(np.float32)
+    q, k, v, g, beta = _rand_rows(rng, 1, T, 1, d)
+    for t in range(T):
+        sl = slice(t, t + 1)
+        Sn, _ = oracle.scan_rows(S, q[:, sl], k[:, sl], v[:, sl], g[:, sl], beta[:, sl],
+                                 want_o=False)
+        lhs = np.linalg.norm(Sn.astype(np.float64))
+        rhs = np.linalg.norm(S.astype(np.float64)) + beta[0, t, 0] * np.linalg.norm(v[0, t, 0])
+        assert lhs <= rhs * (1 + 1e-6)
+        S = Sn
+
+
+# ---------------------------------------------------------------- exact and brute force
+
+def _frac_scan(S, qs, ks, vs, betas):
+    """Exact rational recurrence with g = 0 (no decay) and d = len(S)."""
+    d = len(S)
+    S = [row[:] for row in S]
+    outs = []
+    for q, k, v, b in zip(qs, ks, vs, betas):
+        u = [sum(k[i] * S[i][j] for i in range(d)) for j in range(d)]
+        e = [b * (v[j] - u[j]) for j in range(d)]
+        S = [[S[i][j] + k[i] * e[j] for j in range(d)] for i in range(d)]
+        # 1/sqrt(4) = 1/2 exactly
+        outs.append([sum(q[i] * S[i][j] for i in range(d)) / 2 for j in range(d)])
+    return S, outs
+
+
+def _f32_exact(x: Fraction) -> bool:
+    f = np.float32(float(x))
+    return Fraction(float(f)) == x
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4, 5])
+def test_exact_rational_d4(seed):
+    """d = 4 with dyadic inputs: every intermediate is exact in f64 and every
+    result exact in f32, so the oracle must reproduce the rational answer bit for bit."""
+    rng = np.random.default_rng(100 + seed)
+    d, T = 4, 3
+    halves = [Fraction(x, 2) for x in (-2, -1, 0, 1, 2)]
+    quarters = [Fraction(x, 4) for x in range(-4, 5)]
+    S0 = [[quarters[rng.integers(len(quarters))] for _ in range(d)] for _ in range(d)]
+    qs = [[halves[rng.integers(5)] for _ in range(d)] for _ in range(T)]
+    ks = [[halves[rng.integers(5)] for _ in range(d)] for _ in range(T)]
+    vs = [[halves[rng.integers(5)] for _ in range(d)] for _ in range(T)]
+    bs = [Fraction(int(rng.integers(1, 5)), 4) for _ in range(T)]
+    S_ex, o_ex = _frac_scan(S0, qs, ks, vs, bs)
+    assert all(_f32_exact(x) for row in S_ex for x in row)
+    assert all(_f32_exact(x) for row in o_ex for x in row)
+    A = lambda rows: np.array([[float(x) for x in r] for r in rows], np.float32)
+    S, o = oracle.scan_rows(A(S0)[None, None], A(qs)[None, :, None], A(ks)[None, :, None],
+                            A(vs)[None, :, None], np.zeros((1, T, 1, d), np.float32),
+                            np.array([float(b) for b in bs], np.float32)[None, :, None])
+    assert np.array_equal(S[0, 0], A(S_ex))
+    assert np.array_equal(o[0, :, 0], A(o_ex))
+    # non-vacuity: the case really moves the state
+    assert not np.array_equal(A(S_ex), A(S0))
+
+
+def _matrix_form(S0, q, k, v, g, beta):
+    """S_t = (I - beta k k^T) D_t S_{t-1} + beta k v^T, f64 per row, f32 state."""
+    d = S0.shape[0]
+    S = S0.astype(np.float32)
+    outs = []
+    for t in range(q.shape[0]):
+        kk = k[t].astype(np.float64)
+        Dt = np.diag(np.exp(np.clip(g[t].astype(np.float64), -5.0, 0.0)))
+        P = np.eye(d) - float(beta[t]) * np.outer(kk, kk)
+        Sn = P @ Dt @ S.astype(np.float64) + float(beta[t]) * np.outer(kk, v[t].astype(np.float64))
+        outs.append((Sn.T @ q[t].astype(np.float64)) / np.sqrt(d))
+        S = Sn.astype(np.float32)
+    return S, np.array(outs)
+
+
+@pytest.mark.parametrize("d,T,seed", [(4, 6, 0), (4, 15, 1), (8, 9, 2), (16, 4, 3)])
+def test_matrix_form_with_decay(d, T, seed):
+    rng = np.random.default_rng(200 + seed)
+    S0 = rng.standard_normal((d, d)).astype(np.float32)
+    q = rng.standard_normal((T, d)).astype(np.float32)
+    k = rng.standard_normal((T, d)).astype(np.float32)   # not normalised on purpose
+    v = rng.standard_normal((T, d)).astype(np.float32)
+    g = rng.uniform(-7.0, 1.0, (T, d)).astype(np.float32)
+    beta = rng.uniform(0.0, 1.0, T).astype(np.float32)
+    S_ref, o_ref = _matrix_form(S0, q, k, v, g, beta)
+    S, o = oracle.scan_rows(S0[None, None], q[None, :, None], k[None, :, None], v[None, :, None],
+                            g[None, :, None], beta[None, :, None])
+    # both sides compute each row in f64 and round the state to f32: they can part
+    # only by a last-place rounding flip, which then propagates through the chain
+    scale = max(1.0, np.abs(S_ref).max())
+    assert np.abs(S[0, 0] - S_ref).max() <= 64 * F32_EPS * scale
+    assert np.abs(o[0, :, 0] - o_ref).max() <= 64 * F32_EPS * max(1.0, np.abs(o_ref).max())
+
+
+# ---------------------------------------------------------------- replay, batched, layout
+
+def test_replay_is_the_scan_prefix():
+    rng = np.random.default_rng(17)
+    L, T, H, d = 2, 8, 3, 128
+    S0 = rng.standard_normal((L, H, d, d)).astype(np.float32)
+    rows = _rand_rows(rng, L, T, H, d)
+    S_full, o_full = oracle.scan_rows(S0, *rows)
+    for keep in (1, 3, T):
+        Sr = oracle.replay(S0, *rows, keep=keep)
+        sl = [x[:, :keep] for x in rows]
+        Sk, ok = oracle.scan_rows(S0, *sl)
+        assert np.array_equal(Sr, Sk)
+        assert np.array_equal(ok, o_full[:, :keep])
+    assert np.array_equal(oracle.replay(S0, *rows, keep=T), S_full)
+
+
+def test_batched_equals_isolated_single_rows():
+    rng = np.random.default_rng(18)
+    L, B, H, d = 2, 5, 3, 128
+    states = rng.standard_normal((L, B, H, d, d)).astype(np.float32)
+    q, k, v, g, beta = _rand_rows(rng, L, B, H, d)   # [L][B][H][d]: B in the row slot
+    Sb, ob = oracle.batched(states, q, k, v, g, beta)
+    for l in range(L):
+        for b in range(B):
+            sl = lambda x: x[l:l + 1, b:b + 1]
+            S1, o1 = oracle.scan_rows(states[l:l + 1, b], sl(q), sl(k), sl(v), sl(g), sl(beta))
+            assert np.array_equal(S1[0], Sb[l, b])
+            assert np.array_equal(o1[0, 0], ob[l, b])
+
+
+def test_chains_are_independent_and_layout_strides_are_right():
+    rng = np.random.default_rng(19)
+    L, T, H, d = 3, 4, 5, 128
+    S0 = rng.standard_normal((L, H, d, d)).astype(np.float32)
+    q, k, v, g, beta = _rand_rows(rng, L, T, H, d)
+    S, o = oracle.scan_rows(S0, q, k, v, g, beta)
+    # every chain run alone, through a 1x1 layout, gives the same bits
+    for l in range(L):
+        for h in range(H):
+            sl = lambda x: x[l:l + 1, :, h:h + 1]
+            S1, o1 = oracle.scan_rows(S0[l:l + 1, h:h + 1], sl(q), sl(k), sl(v), sl(g), sl(beta))
+            assert np.array_equal(S1[0, 0], S[l, h])
+            assert np.array_equal(o1[0, :, 0], o[l, :, h])
+    # permuting heads and layers permutes the results
+    ph, pl = rng.permutation(H), rng.permutation(L)
+    P = lambda x: x[pl][:, :, ph]
+    Sp, op = oracle.scan_rows(S0[pl][:, ph], P(q), P(k), P(v), P(g), beta[pl][:, :, ph])
+    assert np.array_equal(Sp, S[pl][:, ph])
+    assert np.array_equal(op, o[pl][:, :, ph])
+
+
+def test_threads_do_not_change_bits():
+    rng = np.random.default_rng(20)
+    L, T, H, d = 2, 3, 4, 128
+    S0 = rng.standard_normal((L, H, d, d)).astype(np.float32)
+    rows = _rand_rows(rng, L, T, H, d)
+    a = oracle.scan_rows(S0, *rows, threads=1)
+    b = oracle.scan_rows(S0, *rows, threads=4)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- bf16 inputs
+
+# (bf16 bits, exact value) from the IEEE binary16-brain layout: 1 sign, 8 exponent
+# (bias 127), 7 mantissa bits.
+BF16_TABLE = [
+    (0x3F80, 1.0), (0xBF80, -1.0), (0x4000, 2.0), (0xC040, -3.0), (0x3F00, 0.5),
+    (0x3FC0, 1.5), (0x4120, 10.0), (0x3E80, 0.25), (0x0000, 0.0), (0x3F81, 1.0 + 2.0 ** -7),
+    (0x0080, 2.0 ** -126), (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127), (0xC2C8, -100.0),
+]
+
+
+def test_bf16_widening_matches_ieee_table():
+    # write the bf16 values with a one-hot key from zero state: key row m == widened v
+    d = 128
+    bits = np.zeros(d, np.uint16)
+    vals = np.zeros(d, np.float64)
+    for n, (b, x) in enumerate(BF16_TABLE):
+        bits[n], vals[n] = b, x
+    one = 0x3F80
+    k = np.zeros((1, 1, 1, d), np.uint16); k[..., 5] = one
+    v = bits[None, None, None, :]
+    g = np.zeros_like(k)
+    beta = np.full((1, 1, 1), one, np.uint16)
+    S, _ = oracle.scan_rows(np.zeros((1, 1, d, d), np.float32), k, k, v, g, beta, want_o=False)
+    assert np.array_equal(S[0, 0, 5].astype(np.float64), vals)
+
+
+def test_bf16_scan_equals_f32_scan_of_torch_widened_values():
+    torch = pytest.importorskip("torch")
+    from gated_delta_rule_rows_amd import synth
+    rng = np.random.default_rng(21)
+    L, T, H, d = 1, 5, 2, 128
+    S0 = rng.standard_normal((L, H, d, d)).astype(np.float32)
+    rows = _rand_rows(rng, L, T, H, d)
+    bits = [synth.to_bf16_bits(x) for x in rows]
+    widened = [torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).float().numpy()
+               for b in bits]
+    a = oracle.scan_rows(S0, *bits)
+    b = oracle.scan_rows(S0, *widened)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
