@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Throughput of the KDA speculative-verify scan on one MI355X.
+
+One step = one verify round of the 34-layer x 64-head KDA stack at T = 15
+(K = 14 drafts): the T-row scan of every (layer, head) state out of place (the
+untouched input state is the round's snapshot), then, unless all 14 drafts
+were accepted, the accept-j replay of rows 0..j from that snapshot.  The
+accept counts j ~ U{0..14} and the row inputs are seeded and synthetic.
+
+Prints ONE JSON line.  `value` is verify rows x heads x layers per second
+(T rows counted per round), with every input resident in HBM before the timed
+region.  `roofline` covers the dominant kernel (the T = 15 scan): algorithmic
+bytes per launch / its mean launch time from HIP events on the launch stream.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same rounds.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+D = 128
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
+STATE_BYTES = 4 * D * D         # one head's f32 state
+KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_rows_amd", "csrc", "kda_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def scan_bytes_per_head(T: int, es: int = 4) -> int:
+    """State in + out, T rows of q,k,v,g,beta in, T rows of o out."""
+    return 2 * STATE_BYTES + T * (4 * D * es + es) + T * D * 4
+
+
+def replay_bytes_per_head(keep: int, es: int = 4) -> int:
+    """Snapshot in + state out, keep rows of k,v,g,beta in (q and o are not needed)."""
+    return 2 * STATE_BYTES + keep * (3 * D * es + es)
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the kernel source as it is now; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def pctl(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs), q))
+
+
+def cpu_baseline(host_rounds, js, T, seconds: float):
+    """The oracle on the same rounds (all chains, scan + replay), until `seconds` pass."""
+    import numpy as np
+    import oracle
+
+    threads = min(16, os.cpu_count() or 1)
+    L, _, H, _ = host_rounds[0]["q"].shape
+    s = np.zeros((L, H, D, D), np.float32)
+    rows = 0
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        r = host_rounds[n % len(host_rounds)]
+        args = [r[k] for k in ("q", "k", "v", "g", "beta")]
+        s_full, _ = oracle.scan_rows(s, *args, threads=threads)
+        keep = int(js[n % len(js)]) + 1
+        s = oracle.replay(s, *args, keep=keep, threads=threads) if keep < T else s_full
+        rows += T * H * L
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= len(js):
+            break
+    return {
+        "value": rows / el, "unit": "rows*heads/s", "cores": threads, "kind": "oracle",
+        "sample": f"{n} verify_k14 round(s): all {L}x{H} chains, T={T} scan + accept-j replay, "
+                  f"f64 oracle on {threads} host threads, {el:.1f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--sessions", type=int, default=1,
+                    help="independent state sets visited round-robin (1 = the single-session workload)")
+    ap.add_argument("--cold-launches", type=int, default=8,
+                    help="extra scan launches timed after a 512 MiB write, for the MALL-cold figure")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the scan shards by head, layer or "
+              "session with no exchange inside the path (see DESIGN.md), but no multi-GPU run "
+              "is part of it. Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_rows_amd as kda
+    from gated_delta_rule_rows_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS["verify_k14"]
+    L, H, T = w.L, w.H, w.T
+    K = T - 1
+    js = synth.accepts(w.seed, w.rounds, K)
+
+    # inputs: one buffer set per round, generated on the host, resident in HBM
+    n_pool = max(1, min(args.steps + args.warmup, w.rounds))
+    t0 = time.perf_counter()
+    host_rounds = [synth.rows(w.seed, r, L, T, H) for r in range(n_pool)]
+    names = ("q", "k", "v", "g", "beta")
+    dev_rounds = [[torch.from_numpy(r[n]).cuda() for n in names] for r in host_rounds]
+    gen_s = time.perf_counter() - t0
+
+    S = max(1, args.sessions)
+    bufs = [[torch.zeros(L, H, D, D, device="cuda"), torch.zeros(L, H, D, D, device="cuda")]
+            for _ in range(S)]
+    o = torch.empty(L, T, H, D, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def round_(i, ev=None):
+        r = i % w.rounds
+        rows = dev_rounds[r % n_pool]
+        pair = bufs[i % S]
+        snap, live = pair
+        keep = int(js[r]) + 1
+        if ev is not None:
+            ev[0].record(stream)
+        kda.kda_scan_rows(snap, live, *rows, o=o)
+        if ev is not None:
+            ev[1].record(stream)
+        replayed = keep < T
+        if replayed:
+            kda.kda_replay(snap, live, *rows, keep=keep)
+            if ev is not None:
+                ev[2].record(stream)
+        pair[0], pair[1] = live, snap
+        return keep, replayed
+
+    for i in range(args.warmup):
+        round_(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    info = []
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        info.append(round_(args.warmup + s, evs[s]))
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+
+    scan_us = [evs[s][0].elapsed_time(evs[s][1]) * 1e3 for s in range(args.steps)]
+    rep_us = [evs[s][1].elapsed_time(evs[s][2]) * 1e3 for s in range(args.steps) if info[s][1]]
+    rep_keep = [info[s][0] for s in range(args.steps) if info[s][1]]
+
+    chains = L * H
+    scan_bytes = chains * scan_bytes_per_head(T)
+    mean_scan_us = float(np.mean(scan_us))
+    achieved = scan_bytes / (mean_scan_us * 1e-6) / 1e9
+    rep_bytes = [chains * replay_bytes_per_head(k) for k in rep_keep]
+    rep_gbps = (sum(rep_bytes) / (sum(rep_us) * 1e-6) / 1e9) if rep_us else None
+    round_bytes = args.steps * scan_bytes + sum(rep_bytes)
+    ms_per_step = total_ms / args.steps
+    value = args.steps * T * H * L / (total_ms * 1e-3)
+    committed = sum(k for k, _ in info) * H * L / (total_ms * 1e-3)
+
+    # MALL-cold scan launches: write 512 MiB between launches, time the launch alone
+    cold_us = []
+    if args.cold_launches > 0:
+        flush = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
+        snap, live = bufs[0]
+        rows = dev_rounds[0]
+        for _ in range(args.cold_launches):
+            flush.zero_()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            kda.kda_scan_rows(snap, live, *rows, o=o)
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold_us.append(a.elapsed_time(b) * 1e3)
+        del flush
+
+    traffic = measured_traffic("scan_f32_o")
+    line = {
+        "metric": "verify-scan rows*heads/s and achieved HBM GB/s (% peak), K=14, 64 heads",
+        "value": value,
+        "unit": "rows*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "verify_k14", "layers": L, "heads": H, "T": T, "K": K,
+            "rounds": w.rounds, "accept": "j~U{0..14}, replay keep=j+1 when j<14",
+            "state": "f32 [34][64][128][128], out-of-place scan (input state = snapshot)",
+            "inputs": "f32 q,k,v,g [34][15][64][128], beta [34][15][64]", "sessions": S,
+            "seed": w.seed,
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+            "kernel": "kda_scan_kernel<f32, o> (T=15, 2176 workgroups)",
+            "bytes_per_launch": scan_bytes,
+            "mean_launch_us": mean_scan_us,
+        },
+        "scan_us": {"mean": mean_scan_us, "p10": pctl(scan_us, 10), "p50": pctl(scan_us, 50),
+                    "p90": pctl(scan_us, 90)},
+        "scan_us_mall_cold": ({"mean": float(np.mean(cold_us)), "p50": pctl(cold_us, 50),
+                               "gbps": scan_bytes / (float(np.mean(cold_us)) * 1e-6) / 1e9}
+                              if cold_us else None),
+        "replay": ({"launches": len(rep_us), "mean_us": float(np.mean(rep_us)),
+                    "mean_keep": float(np.mean(rep_keep)), "gbps": rep_gbps} if rep_us else None),
+        "round_gbps": round_bytes / (total_ms * 1e-3) / 1e9,
+        "round_frac_of_peak": round_bytes / (total_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "committed_rows_heads_per_s": committed,
+        "wall_s_timed": wall,
+        "input_gen_s": gen_s,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(host_rounds, js, T, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,339 @@
+// gfx950 kernels of the KDA verify-row scan.
+//
+// One workgroup owns one (layer, head) chain -- or, in the batched arm, one
+// (layer, session, head) chain -- and keeps that head's 128 x 128 f32 state in
+// VGPRs for the whole row loop: the state is read from HBM once and written
+// once per launch, whatever the row count T.  This is what the source page
+// (memra-engine 0.123.0 glm_spec.rs, module doc VERIFY-ROW BATCHING) means by
+// the in-kernel T-loop over register state being the chained t=1 program.
+//
+// Per row of one head (i = key channel, j = value channel):
+//   d_i = exp(clamp(g_i, -5, 0))                 (once per row, into LDS)
+//   S'  = d_i * S_ij                              (VGPR, in place)
+//   u_j = sum_i k_i S'_ij,  w_j = sum_i q_i S'_ij (in-lane FMA chains, then a
+//                                                 fixed DPP butterfly)
+//   e_j = beta (v_j - u_j)
+//   S   = S' + k_i e_j                            (VGPR, in place)
+//   o_j = (w_j + e_j * (q.k)) / sqrt(128)
+// The last line is o = S^T q read from the updated state, expanded as
+// q^T S' + (q.k) e so that both reductions of a row run in one phase.
+//
+// Tiling.  The recurrence reduces over i only; value columns never interact.
+// A lane owns R consecutive key rows x C consecutive value columns; the NI =
+// 128/R lanes that share a column group sit next to each other inside one
+// 16-lane DPP row, so the reduction over i is an in-lane chain followed by a
+// log2(NI)-step butterfly with no LDS traffic and no barrier.  A wave covers
+// (64/NI)*C columns and a head takes 128 / that many waves.
+//
+// Bit identity.  Every entry point (T-row scan, replay, batched t=1) runs the
+// same row code with the same tiling, explicit fmaf, -ffp-contract=off, one
+// expf, and a reduction tree that does not depend on T, B, L, H or the entry
+// point.  The state crosses HBM as exact f32 words, so a T-row launch equals
+// T chained one-row launches bit for bit.
+//
+// No MFMA: each row is two matrix-vector products and a rank-1 update with a
+// sequential dependency from row to row -- there is no dense contraction to
+// feed the matrix cores.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+constexpr int kDD = kD * kD;
+constexpr float kGateLo = -5.0f;   // gate_lower_bound of the glm5_next fixture
+constexpr float kGateHi = 0.0f;    // a log-decay never grows the state
+// 1/sqrt(128) rounded to f32
+constexpr float kInvSqrtD = 0.0883883476483184405501055452631f;
+
+template <int R, int C>
+struct Tile {
+    static constexpr int NI = kD / R;         // lanes reducing one column group
+    static constexpr int NJG = 64 / NI;       // column groups per wave
+    static constexpr int WCOLS = NJG * C;     // value columns per wave
+    static constexpr int WAVES = kD / WCOLS;  // waves per head
+    static constexpr int THREADS = 64 * WAVES;
+    static_assert(NI == 4 || NI == 8 || NI == 16, "the reduction must stay in one DPP row");
+    static_assert(kD % WCOLS == 0, "waves must tile the head");
+    static_assert(C == 2 || C == 4, "column vector width");
+};
+
+// The library's one tiling.  Changing it changes the canonical rounding of
+// every entry point together, so identity between them is kept.
+using TileT = Tile<16, 4>;
+
+// ------------------------------------------------------------------ lane ops
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over NI adjacent lanes, every lane ending with the same bits: each step
+// adds a value to its partner's, and partners compute a+b and b+a.
+template <int NI>
+__device__ __forceinline__ float group_sum(float x) {
+    x = x + dpp<0xB1>(x);                          // quad_perm [1,0,3,2]
+    x = x + dpp<0x4E>(x);                          // quad_perm [2,3,0,1]
+    if constexpr (NI >= 8) x = x + dpp<0x141>(x);  // row_half_mirror
+    if constexpr (NI >= 16) x = x + dpp<0x140>(x); // row_mirror
+    return x;
+}
+
+// ------------------------------------------------------------------ input loads
+
+template <bool BF16>
+__device__ __forceinline__ float4 load4(const void* base, size_t off) {
+    if constexpr (BF16) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + off);
+        float4 r;
+        r.x = __builtin_bit_cast(float, raw.x << 16);
+        r.y = __builtin_bit_cast(float, raw.x & 0xFFFF0000u);
+        r.z = __builtin_bit_cast(float, raw.y << 16);
+        r.w = __builtin_bit_cast(float, raw.y & 0xFFFF0000u);
+        return r;
+    } else {
+        return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* base, size_t off) {
+    if constexpr (BF16) {
+        return __builtin_bit_cast(float,
+                                  static_cast<uint32_t>(static_cast<const uint16_t*>(base)[off]) << 16);
+    } else {
+        return static_cast<const float*>(base)[off];
+    }
+}
+
+__device__ __forceinline__ float decay_of(float g) {
+    return expf(fminf(fmaxf(g, kGateLo), kGateHi));
+}
+
+template <int C>
+__device__ __forceinline__ void load_cols(const float* p, float (&x)[C]) {
+    if constexpr (C == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(p);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    } else {
+        const float2 v = *reinterpret_cast<const float2*>(p);
+        x[0] = v.x; x[1] = v.y;
+    }
+}
+
+template <int C>
+__device__ __forceinline__ void store_cols(float* p, const float (&x)[C]) {
+    if constexpr (C == 4) {
+        *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    } else {
+        *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+    }
+}
+
+// ------------------------------------------------------------------ the scan
+
+template <int R, int C, bool BF16, bool WRITE_O, bool TABLE>
+__global__ void __launch_bounds__((Tile<R, C>::THREADS))
+kda_scan_kernel(ScanArgs a) {
+    using TL = Tile<R, C>;
+    __shared__ float4 sd4[kTMax * kD / 4];   // decay exp(clamp(g)), [t][i]
+    __shared__ float4 sk4[kTMax * kD / 4];   // k, [t][i]
+    __shared__ float4 sq4[kTMax * kD / 4];   // q, [t][i]
+    __shared__ float4 sv4[kTMax * kD / 4];   // v, [t][j]
+    __shared__ float sb[kTMax];              // beta
+    __shared__ float sqk[kTMax];             // q.k
+    float* sk = reinterpret_cast<float*>(sk4);
+    float* sq = reinterpret_cast<float*>(sq4);
+    float* sv = reinterpret_cast<float*>(sv4);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int ig = lane % TL::NI;
+    const int jg = lane / TL::NI;
+    const int i0 = ig * R;
+    const int j0 = wave * TL::WCOLS + jg * C;
+
+    // --- where this chain lives
+    const size_t chain = blockIdx.x;
+    const float* st_in;
+    float* st_out;
+    size_t row0, rstride, b0, bstride, o0, ostride;
+    int T;
+    if constexpr (TABLE) {
+        const size_t lb = chain / a.H, h = chain % a.H;
+        float* p = a.s_ptrs[lb] + h * kDD;
+        st_in = p;
+        st_out = p;
+        row0 = chain * kD; rstride = 0;
+        b0 = chain; bstride = 0;
+        o0 = chain * kD; ostride = 0;
+        T = 1;
+    } else {
+        const size_t l = chain / a.H, h = chain % a.H;
+        st_in = a.s_in + chain * kDD;
+        st_out = a.s_out + chain * kDD;
+        row0 = (l * a.T_stride * a.H + h) * kD; rstride = static_cast<size_t>(a.H) * kD;
+        b0 = l * a.T_stride * a.H + h;           bstride = a.H;
+        o0 = (l * a.T * a.H + h) * kD;            ostride = static_cast<size_t>(a.H) * kD;
+        T = a.T;
+    }
+
+    // --- state slab into VGPRs (read once per launch)
+    float s[R][C];
+#pragma unroll
+    for (int r = 0; r < R; ++r) load_cols<C>(st_in + static_cast<size_t>(i0 + r) * kD + j0, s[r]);
+
+    // --- all T rows' inputs into LDS; exp(clamp(g)) once per (row, key)
+    for (int idx = tid; idx < T * (kD / 4); idx += TL::THREADS) {
+        const int t = idx >> 5;
+        const int c4 = idx & 31;
+        const size_t off = row0 + t * rstride + c4 * 4;
+        const float4 gk = load4<BF16>(a.k, off);
+        const float4 gv = load4<BF16>(a.v, off);
+        const float4 gg = load4<BF16>(a.g, off);
+        sk4[t * 32 + c4] = gk;
+        sv4[t * 32 + c4] = gv;
+        sd4[t * 32 + c4] = make_float4(decay_of(gg.x), decay_of(gg.y), decay_of(gg.z), decay_of(gg.w));
+        if constexpr (WRITE_O) sq4[t * 32 + c4] = load4<BF16>(a.q, off);
+    }
+    if (tid < T) sb[tid] = load1<BF16>(a.beta, b0 + tid * bstride);
+    __syncthreads();
+
+    // --- q.k per row: one 16-lane DPP row per verify row, 8 keys per lane in
+    //     ascending order, then the same butterfly as the main reduction
+    if constexpr (WRITE_O) {
+        const int l16 = lane & 15;
+        for (int t = wave * 4 + (lane >> 4); t < T; t += TL::WAVES * 4) {
+            float p = 0.0f;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) p = fmaf(sq[t * kD + l16 * 8 + m], sk[t * kD + l16 * 8 + m], p);
+            p = group_sum<16>(p);
+            if (l16 == 0) sqk[t] = p;
+        }
+        __syncthreads();
+    }
+
+    // --- the sequential row loop over register state
+#pragma unroll 1
+    for (int t = 0; t < T; ++t) {
+        float kk[R], dk[R], qq[R];
+#pragma unroll
+        for (int r4 = 0; r4 < R / 4; ++r4) {
+            const float4 x = sk4[(t * kD + i0) / 4 + r4];
+            const float4 y = sd4[(t * kD + i0) / 4 + r4];
+            kk[4 * r4 + 0] = x.x; kk[4 * r4 + 1] = x.y; kk[4 * r4 + 2] = x.z; kk[4 * r4 + 3] = x.w;
+            dk[4 * r4 + 0] = y.x; dk[4 * r4 + 1] = y.y; dk[4 * r4 + 2] = y.z; dk[4 * r4 + 3] = y.w;
+            if constexpr (WRITE_O) {
+                const float4 z = sq4[(t * kD + i0) / 4 + r4];
+                qq[4 * r4 + 0] = z.x; qq[4 * r4 + 1] = z.y; qq[4 * r4 + 2] = z.z; qq[4 * r4 + 3] = z.w;
+            }
+        }
+
+        // decay, then the two in-lane partial reductions over this lane's keys
+        float u[C], w[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) { u[c] = 0.0f; w[c] = 0.0f; }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                s[r][c] = s[r][c] * dk[r];
+                u[c] = fmaf(kk[r], s[r][c], u[c]);
+                if constexpr (WRITE_O) w[c] = fmaf(qq[r], s[r][c], w[c]);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            u[c] = group_sum<TL::NI>(u[c]);
+            if constexpr (WRITE_O) w[c] = group_sum<TL::NI>(w[c]);
+        }
+
+        // delta-rule write
+        const float bt = sb[t];
+        float vv[C];
+        load_cols<C>(sv + t * kD + j0, vv);
+        float e[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) e[c] = bt * (vv[c] - u[c]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) s[r][c] = fmaf(kk[r], e[c], s[r][c]);
+        }
+
+        if constexpr (WRITE_O) {
+            const float qk = sqk[t];
+            float ov[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) ov[c] = fmaf(e[c], qk, w[c]) * kInvSqrtD;
+            if (ig == 0) store_cols<C>(a.o + o0 + t * ostride + j0, ov);
+        }
+    }
+
+    // --- state slab back to HBM (written once per launch)
+#pragma unroll
+    for (int r = 0; r < R; ++r) store_cols<C>(st_out + static_cast<size_t>(i0 + r) * kD + j0, s[r]);
+}
+
+// ------------------------------------------------------------------ copy
+
+// Plain vector copy: 4 float4 per thread per iteration, grid-stride.
+__global__ void __launch_bounds__(256) kda_copy_kernel(const float4* __restrict__ src,
+                                                       float4* __restrict__ dst, size_t n4) {
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n4; i += 4 * stride) {
+        const float4 a0 = src[i];
+        const float4 a1 = src[i + stride];
+        const float4 a2 = src[i + 2 * stride];
+        const float4 a3 = src[i + 3 * stride];
+        dst[i] = a0;
+        dst[i + stride] = a1;
+        dst[i + 2 * stride] = a2;
+        dst[i + 3 * stride] = a3;
+    }
+    for (; i < n4; i += stride) dst[i] = src[i];
+}
+
+template <bool BF16, bool WRITE_O, bool TABLE>
+hipError_t launch_one(const ScanArgs& a, long long n_chains, hipStream_t stream) {
+    using TL = TileT;
+    kda_scan_kernel<16, 4, BF16, WRITE_O, TABLE>
+        <<<dim3(static_cast<unsigned>(n_chains)), dim3(TL::THREADS), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_scan(const ScanArgs& a, long long n_chains, bool bf16, bool write_o, bool table,
+                       hipStream_t stream) {
+    if (table) {
+        if (bf16) return write_o ? launch_one<true, true, true>(a, n_chains, stream)
+                                 : launch_one<true, false, true>(a, n_chains, stream);
+        return write_o ? launch_one<false, true, true>(a, n_chains, stream)
+                       : launch_one<false, false, true>(a, n_chains, stream);
+    }
+    if (bf16) return write_o ? launch_one<true, true, false>(a, n_chains, stream)
+                             : launch_one<true, false, false>(a, n_chains, stream);
+    return write_o ? launch_one<false, true, false>(a, n_chains, stream)
+                   : launch_one<false, false, false>(a, n_chains, stream);
+}
+
+hipError_t launch_copy(const float* src, float* dst, size_t n_floats, hipStream_t stream) {
+    const size_t n4 = n_floats / 4;   // n_floats is a multiple of 128*128
+    size_t blocks = (n4 + 4 * 256 - 1) / (4 * 256);
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    kda_copy_kernel<<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(
+        reinterpret_cast<const float4*>(src), reinterpret_cast<float4*>(dst), n4);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,142 @@
+/*
+ * kda.h -- C ABI of libkda.so, the MI355X (gfx950) KDA verify-row scan.
+ *
+ * The library runs the hot path of speculative verification on the KDA
+ * (Kimi delta attention) layers of a hybrid model: per head a 128 x 128 f32
+ * recurrent state S[i][j] (i = key channel, j = value channel) advanced by
+ * verify rows, plus the rollback seam (snapshot before row 0, retained row
+ * inputs, accept-j replay) and the batched-decode arm.
+ *
+ * One row t of one head, inputs q_t, k_t, v_t, g_t (128-vectors), beta_t:
+ *     gc   = min(max(g_t, -5), 0)            per key channel, in f32
+ *     S'   = diag(exp(gc)) S
+ *     u    = S'^T k_t
+ *     S    = S' + beta_t k_t (v_t - u)^T
+ *     o_t  = S^T q_t / sqrt(128)             (from the updated state)
+ * memra-engine 0.123.0 glm_spec.rs, module doc VERIFY-ROW BATCHING: the
+ * t = K+1 recurrence is sequential inside one scan launch and equals the
+ * chained t = 1 program; glm5_spec_ppn_gate.rs mini fixture: head_dim 128,
+ * gate_lower_bound -5.0.  The update rule itself is the delta-rule reading
+ * (the pages name the scan but do not print it).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers, 16-byte aligned, row-major and
+ *     contiguous.  The caller owns every buffer; the library never allocates,
+ *     frees or synchronizes.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL means
+ *     the null stream).
+ *   - Arguments are validated on the host before anything is enqueued.  On a
+ *     refusal nothing is enqueued, a nonzero KDA_ERR_* status is returned and
+ *     kda_last_error() describes it.  A failed launch returns KDA_ERR_HIP.
+ *     Faults inside a kernel surface at the caller's next synchronization.
+ *   - Row inputs (q, k, v, g, beta) are all f32 (KDA_IN_F32) or all bf16
+ *     (KDA_IN_BF16, widened exactly by bits << 16 as dflash.rs, memra-engine
+ *     0.98.0, fn bf16_to_f32, does).  State and outputs are always f32.
+ *   - Inputs must be finite; NaN/Inf are not checked on the hot path.
+ *   - Results are deterministic: for a given input every entry point gives
+ *     the same bits on every call, and a T-row scan gives the same bits as T
+ *     chained one-row scans, a replay of keep rows the same bits as a
+ *     keep-row scan, and the batched arm the same bits per row as isolated
+ *     one-row scans.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_HEAD_DIM 128   /* d_k = d_v; glm5_spec_ppn_gate.rs fixture head_dim */
+#define KDA_T_MAX 15       /* verify rows per round: K + 1 <= 15 (glm_spec.rs, WALK-REUSE) */
+#define KDA_B_MAX 15       /* batched-decode sessions per step (same knee) */
+#define KDA_ABI_VERSION 1
+
+enum { KDA_IN_F32 = 0, KDA_IN_BF16 = 1 };
+
+enum {
+    KDA_OK = 0,
+    KDA_ERR_ARG = 1,   /* null pointer or unknown dtype */
+    KDA_ERR_RANGE = 2, /* a count outside its range (T, keep, B, L, H) */
+    KDA_ERR_ALIGN = 3, /* a pointer not 16-byte aligned */
+    KDA_ERR_ALIAS = 4, /* an output overlaps an input (or another output) */
+    KDA_ERR_HIP = 5    /* the HIP runtime refused a launch */
+};
+
+/*
+ * Scan T verify rows of L independent layer-states x H heads.
+ *   glm_spec.rs (0.123.0), VERIFY-ROW BATCHING: one t = K+1 scan per layer,
+ *   rows chained sequentially; ROLLBACK: the state before row 0 is the
+ *   snapshot.
+ *   s_in, s_out : [L][H][128][128] f32.  s_out == s_in scans in place;
+ *                 disjoint buffers leave s_in untouched, so s_in then IS the
+ *                 pre-round snapshot at no cost.  Partial overlap is refused.
+ *   q, k, v, g  : [L][T][H][128] in in_dtype.
+ *   beta        : [L][T][H] in in_dtype.
+ *   o           : [L][T][H][128] f32, or NULL to skip the outputs.
+ *   L, H >= 1;  1 <= T <= KDA_T_MAX.
+ * The caller keeps q, k, v, g, beta alive until it has either replayed or
+ * accepted every row: they are the round's stash (glm_spec.rs, ROLLBACK:
+ * the row inputs are retained with zero copies).
+ */
+int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k,
+                  const void* v, const void* g, const void* beta, float* o, int L, int T, int H,
+                  int in_dtype, void* stream);
+
+/*
+ * snap = s, a device copy of L x H states [L][H][128][128] f32.
+ *   glm_spec.rs (0.123.0), walk per KDA layer: the state is cloned once per
+ *   layer per round before row 0.  Only callers that scan in place need it.
+ *   s and snap must not overlap.  L, H >= 1.
+ */
+int kda_snapshot(const float* s, float* snap, int L, int H, void* stream);
+
+/*
+ * Accept-j rollback: s_out = the state after rows 0..keep-1 of the round,
+ * rebuilt from the pre-round snapshot `snap` by re-running those rows on the
+ * round's retained inputs.  keep = j + 1 (the anchor row plus j accepted
+ * drafts), 1 <= keep <= T_round <= KDA_T_MAX.
+ *   glm_spec.rs (0.123.0), fn glm5_verify_rollback / glm5_rollback_layer and
+ *   the Glm5VerifyCkpt doc: keep outside 1..=rows is an error; the replay is
+ *   the same scan over the same inputs, so the rebuilt state is identical to
+ *   the one the scan held after row keep-1.  In serving keep == T_round needs
+ *   no replay (the resident state already is it); the call stays legal and
+ *   then returns the scan's final state bits.
+ *   snap, s_out : [L][H][128][128] f32; they must not overlap.
+ *   q..beta     : the very buffers passed to the round's kda_scan_rows, with
+ *                 that call's row count T_round (rows keep..T_round-1 unread).
+ *   No outputs are written.
+ */
+int kda_replay(const float* snap, float* s_out, const void* q, const void* k, const void* v,
+               const void* g, const void* beta, int L, int T_round, int keep, int H,
+               int in_dtype, void* stream);
+
+/*
+ * Batched-decode arm: B independent sessions, one row each (t = 1), each
+ * against its own state, updated in place.
+ *   glm_spec.rs (0.123.0), WALK-REUSE: B sessions, each row to its own cache
+ *   at its own position, each row bit-identical to the isolated t = 1 step,
+ *   for B <= 15.
+ *   s_ptrs      : DEVICE array of L*B pointers; s_ptrs[l*B + b] points at
+ *                 session b's layer-l state [H][128][128] f32 (16-byte
+ *                 aligned).  Entries must be distinct and must not overlap
+ *                 each other or any input/output; the library cannot check
+ *                 them (they live on the device).
+ *   q, k, v, g  : [L][B][H][128] in in_dtype.    beta: [L][B][H].
+ *   o           : [L][B][H][128] f32, or NULL.
+ *   L, H >= 1;  1 <= B <= KDA_B_MAX.
+ */
+int kda_scan_batched(float* const* s_ptrs, const void* q, const void* k, const void* v,
+                     const void* g, const void* beta, float* o, int L, int B, int H,
+                     int in_dtype, void* stream);
+
+/* Message for the last nonzero status returned on the calling thread. */
+const char* kda_last_error(void);
+
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

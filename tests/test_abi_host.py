@@ -1,0 +1,196 @@
+"""The C-ABI library loads, exports what include/kda.h declares, and refuses
+bad arguments on the host before anything is enqueued.
+
+No compute happens here: every call below is one that validation must refuse.
+Without a GPU the pointers are plain aligned integers (validation never
+dereferences them); with a GPU they are real device buffers large enough for
+every shape used, so even a validation bug could not read out of bounds.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_rows_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, ERR_ARG, ERR_RANGE, ERR_ALIGN, ERR_ALIAS, ERR_HIP = range(6)
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+(kda_\w+)\s*\(", text, re.M)))
+
+
+def _header_constant(name):
+    m = re.search(rf"#define\s+{name}\s+(\d+)", open(HEADER).read())
+    return int(m.group(1))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.lib_path()):
+        from gated_delta_rule_rows_amd import build
+        build.build()
+    return kda.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert set(names) >= {"kda_scan_rows", "kda_snapshot", "kda_replay", "kda_scan_batched",
+                          "kda_last_error", "kda_abi_version"}
+    for n in names:
+        assert hasattr(lib, n), f"libkda.so does not export {n}"
+
+
+def test_abi_version_matches_header(lib):
+    assert lib.kda_abi_version() == _header_constant("KDA_ABI_VERSION")
+    assert _header_constant("KDA_HEAD_DIM") == kda.D == 128
+    assert _header_constant("KDA_T_MAX") == kda.T_MAX == 15
+    assert _header_constant("KDA_B_MAX") == kda.B_MAX == 15
+
+
+class Bufs:
+    """Named buffers: real device memory when a GPU is visible, else fake aligned addresses."""
+
+    SIZE = 64 << 20   # bytes per buffer, enough for every shape below
+
+    def __init__(self):
+        self.keep = []
+        try:
+            import torch
+            self.gpu = torch.cuda.is_available()
+        except Exception:
+            self.gpu = False
+        self.addr = {}
+        for i, n in enumerate(["s_in", "s_out", "q", "k", "v", "g", "beta", "o", "snap", "ptrs"]):
+            if self.gpu:
+                import torch
+                t = torch.zeros(self.SIZE // 4, dtype=torch.float32, device="cuda")
+                self.keep.append(t)
+                self.addr[n] = t.data_ptr()
+            else:
+                self.addr[n] = 0x7F0000000000 + i * (1 << 32)
+
+    def __getitem__(self, n):
+        return ctypes.c_void_p(self.addr[n])
+
+
+@pytest.fixture(scope="module")
+def b():
+    return Bufs()
+
+
+def _scan(lib, b, **kw):
+    a = dict(s_in=b["s_in"], s_out=b["s_out"], q=b["q"], k=b["k"], v=b["v"], g=b["g"],
+             beta=b["beta"], o=b["o"], L=2, T=8, H=2, dt=0)
+    a.update(kw)
+    return lib.kda_scan_rows(a["s_in"], a["s_out"], a["q"], a["k"], a["v"], a["g"], a["beta"],
+                             a["o"], a["L"], a["T"], a["H"], a["dt"], None)
+
+
+def _replay(lib, b, **kw):
+    a = dict(snap=b["snap"], s_out=b["s_out"], q=b["q"], k=b["k"], v=b["v"], g=b["g"],
+             beta=b["beta"], L=2, T=8, keep=3, H=2, dt=0)
+    a.update(kw)
+    return lib.kda_replay(a["snap"], a["s_out"], a["q"], a["k"], a["v"], a["g"], a["beta"],
+                          a["L"], a["T"], a["keep"], a["H"], a["dt"], None)
+
+
+def _batched(lib, b, **kw):
+    a = dict(ptrs=b["ptrs"], q=b["q"], k=b["k"], v=b["v"], g=b["g"], beta=b["beta"], o=b["o"],
+             L=2, B=4, H=2, dt=0)
+    a.update(kw)
+    return lib.kda_scan_batched(a["ptrs"], a["q"], a["k"], a["v"], a["g"], a["beta"], a["o"],
+                                a["L"], a["B"], a["H"], a["dt"], None)
+
+
+def _msg(lib):
+    return lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(T=0), ERR_RANGE, "T=0"),
+    (dict(T=16), ERR_RANGE, "T=16"),
+    (dict(L=0), ERR_RANGE, "L=0"),
+    (dict(H=0), ERR_RANGE, "H=0"),
+    (dict(H=-3), ERR_RANGE, "H=-3"),
+    (dict(dt=2), ERR_ARG, "in_dtype"),
+    (dict(q=None), ERR_ARG, "q is NULL"),
+    (dict(beta=None), ERR_ARG, "beta is NULL"),
+    (dict(s_in=None), ERR_ARG, "s_in is NULL"),
+    (dict(s_out=None), ERR_ARG, "s_out is NULL"),
+])
+def test_scan_rows_refusals(lib, b, kw, code, needle):
+    assert _scan(lib, b, **kw) == code
+    assert needle in _msg(lib)
+
+
+def test_scan_rows_alignment_and_alias(lib, b):
+    off = lambda n, k: ctypes.c_void_p(b.addr[n] + k)
+    assert _scan(lib, b, k=off("k", 4)) == ERR_ALIGN and "k is not 16-byte aligned" in _msg(lib)
+    assert _scan(lib, b, o=off("o", 8)) == ERR_ALIGN
+    # s_out partially over s_in
+    assert _scan(lib, b, s_out=off("s_in", 4096)) == ERR_ALIAS and "partially" in _msg(lib)
+    # s_out over a row input, o over the state
+    assert _scan(lib, b, s_out=b["v"]) == ERR_ALIAS and "s_out overlaps v" in _msg(lib)
+    assert _scan(lib, b, o=b["s_in"]) == ERR_ALIAS and "o overlaps s_in" in _msg(lib)
+    assert _scan(lib, b, o=off("q", 1024)) == ERR_ALIAS
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(keep=0), ERR_RANGE, "keep=0"),
+    (dict(keep=9), ERR_RANGE, "keep=9"),
+    (dict(T=0, keep=1), ERR_RANGE, "T_round=0"),
+    (dict(T=16, keep=1), ERR_RANGE, "T_round=16"),
+    (dict(snap=None), ERR_ARG, "snap is NULL"),
+    (dict(dt=-1), ERR_ARG, "in_dtype"),
+])
+def test_replay_refusals(lib, b, kw, code, needle):
+    assert _replay(lib, b, **kw) == code
+    assert needle in _msg(lib)
+
+
+def test_replay_alias(lib, b):
+    assert _replay(lib, b, s_out=b["snap"]) == ERR_ALIAS and "s_out overlaps snap" in _msg(lib)
+    assert _replay(lib, b, s_out=b["g"]) == ERR_ALIAS
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(B=0), ERR_RANGE, "B=0"),
+    (dict(B=16), ERR_RANGE, "B=16"),
+    (dict(L=0), ERR_RANGE, "L=0"),
+    (dict(ptrs=None), ERR_ARG, "s_ptrs is NULL"),
+    (dict(dt=7), ERR_ARG, "in_dtype"),
+])
+def test_batched_refusals(lib, b, kw, code, needle):
+    assert _batched(lib, b, **kw) == code
+    assert needle in _msg(lib)
+
+
+def test_batched_alias(lib, b):
+    assert _batched(lib, b, o=b["q"]) == ERR_ALIAS and "o overlaps q" in _msg(lib)
+
+
+def test_snapshot_refusals(lib, b):
+    assert lib.kda_snapshot(b["s_in"], b["s_in"], 2, 2, None) == ERR_ALIAS
+    assert lib.kda_snapshot(b["s_in"], None, 2, 2, None) == ERR_ARG
+    assert lib.kda_snapshot(b["s_in"], b["snap"], 0, 2, None) == ERR_RANGE
+    assert lib.kda_snapshot(ctypes.c_void_p(b.addr["s_in"] + 8), b["snap"], 1, 1, None) == ERR_ALIGN
+
+
+def test_binding_rejects_bad_shapes_before_the_library():
+    torch = pytest.importorskip("torch")
+    # host tensors are refused by the marshalling layer (no CPU path exists)
+    q = torch.zeros(1, 2, 1, 128)
+    s = torch.zeros(1, 1, 128, 128)
+    beta = torch.zeros(1, 2, 1)
+    with pytest.raises(ValueError, match="device tensor"):
+        kda.kda_scan_rows(s, s.clone(), q, q, q, q, beta)
+    with pytest.raises(ValueError, match="shape"):
+        kda.kda_scan_rows(s, s.clone(), q, q, q, q, torch.zeros(1, 3, 1))
+    with pytest.raises(TypeError, match="dtype"):
+        kda.kda_scan_rows(s, s.clone(), q, q, q, q, beta.double())

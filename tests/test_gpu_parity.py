@@ -1,0 +1,356 @@
+"""GPU parity: the HIP path against the CPU oracle (1e-4) and against itself (bit for bit).
+
+Every call goes through libkda.so's C ABI via the Python binding.  Inputs come
+from the seeded generator; expected values come only from the oracle.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import gated_delta_rule_rows_amd as kda  # noqa: E402
+from gated_delta_rule_rows_amd import synth  # noqa: E402
+import oracle  # noqa: E402
+
+TOL = 1e-4          # max abs error on outputs and states, GPU vs oracle
+D = 128
+SAMPLE_HEADS = [0, 21, 42, 63]
+
+
+def dev(a):
+    """numpy -> device tensor (float32, or bf16 from uint16 bit patterns)."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def rows_dev(r):
+    return [dev(r[n]) for n in ("q", "k", "v", "g", "beta")]
+
+
+def rows_np(r):
+    return [r[n] for n in ("q", "k", "v", "g", "beta")]
+
+
+def maxerr(a, b):
+    return float(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)).max())
+
+
+def bits_equal(a, b):
+    a = host(a) if isinstance(a, torch.Tensor) else a
+    b = host(b) if isinstance(b, torch.Tensor) else b
+    return np.array_equal(np.ascontiguousarray(a).view(np.uint32),
+                          np.ascontiguousarray(b).view(np.uint32))
+
+
+def scan(s_in, rows, want_o=True, inplace=False):
+    L, T, H = rows[0].shape[:3]
+    s_out = s_in if inplace else torch.empty_like(s_in)
+    o = torch.empty(L, T, H, D, device="cuda") if want_o else None
+    kda.kda_scan_rows(s_in, s_out, *rows, o=o)
+    return s_out, o
+
+
+def slice_rows(rows, t0, t1):
+    return [x[:, t0:t1].contiguous() for x in rows]
+
+
+def rand_rows(seed, L, T, H, bf16=False):
+    r = synth.rows(seed, 0, L, T, H)
+    if bf16:
+        r = {n: synth.to_bf16_bits(a) for n, a in r.items()}
+    return r
+
+
+def rand_state(seed, L, H, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return (scale * rng.standard_normal((L, H, D, D))).astype(np.float32)
+
+
+# ----------------------------------------------------------------- oracle parity
+
+def test_tiny_workload_rounds_with_replay():
+    w = synth.WORKLOADS["tiny"]
+    js = synth.accepts(w.seed, w.rounds, w.T - 1)
+    s_gpu = torch.zeros(w.L, w.H, D, D, device="cuda")
+    s_ref = np.zeros((w.L, w.H, D, D), np.float32)
+    for r in range(w.rounds):
+        rw = synth.rows(w.seed, r, w.L, w.T, w.H)
+        rd = rows_dev(rw)
+        s_full, o = scan(s_gpu, rd)
+        S_ref, o_ref = oracle.scan_rows(s_ref, *rows_np(rw))
+        assert maxerr(host(o), o_ref) <= TOL
+        assert maxerr(host(s_full), S_ref) <= TOL
+        keep = int(js[r]) + 1
+        s_rep = torch.empty_like(s_gpu)
+        kda.kda_replay(s_gpu, s_rep, *rd, keep=keep)     # s_gpu is the snapshot
+        S_rep = oracle.replay(s_ref, *rows_np(rw), keep=keep)
+        assert maxerr(host(s_rep), S_rep) <= TOL
+        s_gpu, s_ref = s_rep, S_rep
+    assert np.abs(s_ref).max() > 0.1   # non-vacuous: the state is populated
+
+
+def test_one_layer_workload_replay_sweep():
+    w = synth.WORKLOADS["one_layer"]
+    warm = synth.warmup_rows(w.seed, w.warmup_rows, w.L, w.H)
+    s0, _ = oracle.scan_rows(np.zeros((w.L, w.H, D, D), np.float32), *rows_np(warm),
+                             want_o=False, threads=oracle.max_threads())
+    rw = synth.rows(w.seed, 0, w.L, w.T, w.H)
+    rd = rows_dev(rw)
+    s_in = dev(s0)
+    s_full, o = scan(s_in, rd)
+    S_ref, o_ref = oracle.scan_rows(s0, *rows_np(rw), threads=oracle.max_threads())
+    assert maxerr(host(o), o_ref) <= TOL
+    assert maxerr(host(s_full), S_ref) <= TOL
+    for j in range(w.T):
+        keep = j + 1
+        s_rep = torch.empty_like(s_in)
+        kda.kda_replay(s_in, s_rep, *rd, keep=keep)
+        S_rep = oracle.replay(s0, *rows_np(rw), keep=keep, threads=oracle.max_threads())
+        assert maxerr(host(s_rep), S_rep) <= TOL, f"keep={keep}"
+    assert bits_equal(s_in, dev(s0))   # the scan was out of place: the snapshot is intact
+
+
+@pytest.mark.parametrize("L,T,H,bf16", [(1, 1, 1, False), (2, 15, 3, False), (3, 5, 7, True),
+                                        (1, 15, 64, True)])
+def test_ragged_shapes_vs_oracle(L, T, H, bf16):
+    rw = rand_rows(7, L, T, H, bf16)
+    s0 = rand_state(8, L, H, scale=0.5)
+    s_out, o = scan(dev(s0), rows_dev(rw))
+    S_ref, o_ref = oracle.scan_rows(s0, *rows_np(rw), threads=oracle.max_threads())
+    assert maxerr(host(o), o_ref) <= TOL
+    assert maxerr(host(s_out), S_ref) <= TOL
+
+
+def test_verify_k14_full_size_sampled_chains():
+    w = synth.WORKLOADS["verify_k14"]
+    js = synth.accepts(w.seed, w.rounds, w.T - 1)
+    s_gpu = torch.zeros(w.L, w.H, D, D, device="cuda")
+    s_ref = np.zeros((w.L, len(SAMPLE_HEADS), D, D), np.float32)
+    for r in range(3):
+        rw = synth.rows(w.seed, r, w.L, w.T, w.H)
+        rd = rows_dev(rw)
+        s_full, o = scan(s_gpu, rd)
+        sub = [x[:, :, SAMPLE_HEADS] for x in rows_np(rw)]
+        S_ref, o_ref = oracle.scan_rows(s_ref, *sub, threads=oracle.max_threads())
+        assert maxerr(host(o)[:, :, SAMPLE_HEADS], o_ref) <= TOL
+        assert maxerr(host(s_full)[:, SAMPLE_HEADS], S_ref) <= TOL
+        keep = int(js[r]) + 1
+        if keep < w.T:
+            s_rep = torch.empty_like(s_gpu)
+            kda.kda_replay(s_gpu, s_rep, *rd, keep=keep)
+            S_ref = oracle.replay(s_ref, *sub, keep=keep, threads=oracle.max_threads())
+            assert maxerr(host(s_rep)[:, SAMPLE_HEADS], S_ref) <= TOL
+            s_gpu = s_rep
+        else:
+            s_gpu = s_full
+        s_ref = S_ref
+
+
+def test_batched_b15_full_size_sampled_chains():
+    w = synth.WORKLOADS["batched_b15"]
+    sess = [0, 7, 14]
+    states = torch.zeros(w.L, w.B, w.H, D, D, device="cuda")
+    table = kda.state_table(states)
+    s_ref = np.zeros((w.L, len(sess), len(SAMPLE_HEADS), D, D), np.float32)
+    for step in range(2):
+        rw = synth.rows(w.seed, step, w.L, w.B, w.H)      # [L][B][H][D]
+        o = torch.empty(w.L, w.B, w.H, D, device="cuda")
+        kda.kda_scan_batched(table, *rows_dev(rw), o=o)
+        sub = [x[:, sess][:, :, SAMPLE_HEADS] for x in rows_np(rw)]
+        s_ref, o_ref = oracle.batched(s_ref, *sub, threads=oracle.max_threads())
+        got_s = host(states)[:, sess][:, :, SAMPLE_HEADS]
+        got_o = host(o)[:, sess][:, :, SAMPLE_HEADS]
+        assert maxerr(got_o, o_ref) <= TOL
+        assert maxerr(got_s, s_ref) <= TOL
+
+
+@pytest.mark.parametrize("K", [1, 14])
+def test_serving_mix_bf16_sampled_chains(K):
+    w = synth.WORKLOADS["serving_mix_bf16"]
+    T = K + 1
+    heads = SAMPLE_HEADS
+    s_gpu = torch.zeros(w.L, w.H, D, D, device="cuda")
+    s_ref = np.zeros((w.L, len(heads), D, D), np.float32)
+    for r, j in enumerate([K, 0]):          # full accept, then worst-case j = 0
+        rw = synth.rows_bf16(w.seed, r, w.L, T, w.H)
+        rd = rows_dev(rw)
+        s_full, o = scan(s_gpu, rd)
+        sub = [x[:, :, heads] for x in rows_np(rw)]
+        S_ref, o_ref = oracle.scan_rows(s_ref, *sub, threads=oracle.max_threads())
+        assert maxerr(host(o)[:, :, heads], o_ref) <= TOL
+        if j == K:
+            s_gpu, s_ref = s_full, S_ref
+        else:
+            s_rep = torch.empty_like(s_gpu)
+            kda.kda_replay(s_gpu, s_rep, *rd, keep=j + 1)
+            s_ref = oracle.replay(s_ref, *sub, keep=j + 1, threads=oracle.max_threads())
+            s_gpu = s_rep
+        assert maxerr(host(s_gpu)[:, heads], s_ref) <= TOL
+
+
+# ----------------------------------------------------------------- closed forms on the GPU
+
+def test_gpu_identity_and_clamp_and_one_hot():
+    L, T, H = 1, 6, 2
+    rw = rand_rows(3, L, T, H)
+    s0 = dev(rand_state(4, L, H))
+    # beta = 0, g = 0: the state does not move (bit for bit)
+    r0 = dict(rw, g=np.zeros_like(rw["g"]), beta=np.zeros_like(rw["beta"]))
+    s1, _ = scan(s0, rows_dev(r0))
+    assert bits_equal(s1, s0)
+    # clamp: g = 0.7 acts as 0, g = -9 as -5
+    for a, b in ((0.7, 0.0), (-9.0, -5.0)):
+        ra = dict(rw, g=np.full_like(rw["g"], a))
+        rb = dict(rw, g=np.full_like(rw["g"], b))
+        sa, oa = scan(s0, rows_dev(ra))
+        sb, ob = scan(s0, rows_dev(rb))
+        assert bits_equal(sa, sb) and bits_equal(oa, ob)
+    # one-hot key from zero state writes v into key row m exactly
+    m = 77
+    k = np.zeros((1, 1, 1, D), np.float32); k[..., m] = 1
+    v = np.random.default_rng(5).standard_normal((1, 1, 1, D)).astype(np.float32)
+    r1 = [dev(k), dev(k), dev(v), dev(np.zeros_like(k)), dev(np.ones((1, 1, 1), np.float32))]
+    sz, _ = scan(torch.zeros(1, 1, D, D, device="cuda"), r1)
+    sz = host(sz)
+    assert np.array_equal(sz[0, 0, m], v[0, 0, 0])
+    assert not np.delete(sz[0, 0], m, axis=0).any()
+
+
+def test_snapshot_is_a_bit_copy():
+    s = dev(rand_state(6, 3, 5))
+    snap = torch.full_like(s, float("nan"))
+    kda.kda_snapshot(s, snap)
+    assert bits_equal(snap, s)
+
+
+# ----------------------------------------------------------------- GPU bit-identity gates
+
+@pytest.mark.parametrize("T,bf16", [(2, False), (8, False), (15, False), (15, True)])
+def test_t_row_launch_equals_chained_single_rows(T, bf16):
+    L, H = 3, 5
+    rd = rows_dev(rand_rows(11, L, T, H, bf16))
+    s0 = dev(rand_state(12, L, H))
+    s_T, o_T = scan(s0, rd)
+    s = s0
+    for t in range(T):
+        s, o1 = scan(s, slice_rows(rd, t, t + 1))
+        assert bits_equal(o1[:, 0], o_T[:, t]), f"row {t}"
+    assert bits_equal(s, s_T)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_replay_equals_state_after_keep_rows(bf16):
+    L, T, H = 2, 15, 4
+    rd = rows_dev(rand_rows(13, L, T, H, bf16))
+    snap = dev(rand_state(14, L, H))
+    s_full, _ = scan(snap, rd)
+    chained = snap
+    for keep in range(1, T + 1):
+        chained, _ = scan(chained, slice_rows(rd, keep - 1, keep))
+        s_rep = torch.empty_like(snap)
+        kda.kda_replay(snap, s_rep, *rd, keep=keep)
+        assert bits_equal(s_rep, chained), f"keep={keep}"
+        s_k, _ = scan(snap, slice_rows(rd, 0, keep), want_o=False)
+        assert bits_equal(s_rep, s_k)
+    s_rep = torch.empty_like(snap)
+    kda.kda_replay(snap, s_rep, *rd, keep=T)
+    assert bits_equal(s_rep, s_full)     # keep == T returns the resident bits
+
+
+@pytest.mark.parametrize("B,bf16", [(1, False), (7, True), (15, False)])
+def test_batched_equals_isolated_single_rows(B, bf16):
+    L, H = 2, 3
+    rw = rand_rows(15, L, B, H, bf16)        # [L][B][H][D]
+    rd = rows_dev(rw)
+    init = rand_state(16, L * B, H).reshape(L, B, H, D, D)
+    states = dev(init)
+    o = torch.empty(L, B, H, D, device="cuda")
+    kda.kda_scan_batched(kda.state_table(states), *rd, o=o)
+    for l in range(L):
+        for b in range(B):
+            one = [x[l:l + 1, b:b + 1].contiguous() for x in rd]
+            s1, o1 = scan(dev(init[l:l + 1, b]), one)
+            assert bits_equal(s1[0], states[l, b])
+            assert bits_equal(o1[0, 0], o[l, b])
+
+
+def test_batched_with_scattered_session_buffers():
+    L, B, H = 3, 4, 2
+    rd = rows_dev(rand_rows(17, L, B, H))
+    init = rand_state(18, L * B, H).reshape(L, B, H, D, D)
+    bufs = [[dev(init[l, b]) for b in range(B)] for l in range(L)]
+    kda.kda_scan_batched(kda.state_table(bufs), *rd)
+    ref = dev(init)
+    kda.kda_scan_batched(kda.state_table(ref), *rd)
+    for l in range(L):
+        for b in range(B):
+            assert bits_equal(bufs[l][b], ref[l, b])
+
+
+def test_in_place_equals_out_of_place_and_runs_repeat():
+    L, T, H = 2, 9, 6
+    rd = rows_dev(rand_rows(19, L, T, H))
+    s0 = dev(rand_state(20, L, H))
+    a, oa = scan(s0, rd)
+    b, ob = scan(s0, rd)
+    c = s0.clone()
+    _, oc = scan(c, rd, inplace=True)
+    assert bits_equal(a, b) and bits_equal(oa, ob)
+    assert bits_equal(a, c) and bits_equal(oa, oc)
+
+
+def test_no_outputs_leaves_state_bits_unchanged():
+    L, T, H = 2, 7, 3
+    rd = rows_dev(rand_rows(21, L, T, H))
+    s0 = dev(rand_state(22, L, H))
+    a, _ = scan(s0, rd, want_o=True)
+    b, _ = scan(s0, rd, want_o=False)
+    assert bits_equal(a, b)
+
+
+def test_chains_do_not_interact_on_gpu():
+    L, T, H = 3, 4, 5
+    rw = rand_rows(23, L, T, H)
+    s0 = rand_state(24, L, H)
+    a, oa = scan(dev(s0), rows_dev(rw))
+    ph = [4, 2, 0, 3, 1]
+    rp = {n: np.ascontiguousarray(x[:, :, ph]) for n, x in rw.items()}
+    b, ob = scan(dev(np.ascontiguousarray(s0[:, ph])), rows_dev(rp))
+    assert bits_equal(host(a)[:, ph], b)
+    assert bits_equal(host(oa)[:, :, ph], ob)
+
+
+# ----------------------------------------------------------------- red arms
+
+def test_red_arms_diverge():
+    """A wrong rollback must be visible: skipping the replay after a partial
+    accept, or replaying from the post-scan state, changes the state bits."""
+    L, T, H = 1, 8, 4
+    rd = rows_dev(rand_rows(25, L, T, H))
+    snap = dev(rand_state(26, L, H))
+    s_full, _ = scan(snap, rd)
+    keep = 3
+    good = torch.empty_like(snap)
+    kda.kda_replay(snap, good, *rd, keep=keep)
+    # red 1: no replay -- the resident post-row-K state stands in for the rollback
+    n1 = int((host(s_full).view(np.uint32) != host(good).view(np.uint32)).sum())
+    # red 2: replay from the wrong snapshot (the post-scan state)
+    bad = torch.empty_like(snap)
+    kda.kda_replay(s_full, bad, *rd, keep=keep)
+    n2 = int((host(bad).view(np.uint32) != host(good).view(np.uint32)).sum())
+    assert n1 > 0 and n2 > 0, (n1, n2)
+    # non-vacuity: the scan really moved the state away from the snapshot
+    assert not bits_equal(s_full, snap)
+    # and continuing one more row from each keeps them apart
+    nxt = slice_rows(rows_dev(rand_rows(27, L, 1, H)), 0, 1)
+    c_good, _ = scan(good, nxt)
+    c_bad, _ = scan(s_full, nxt)
+    assert not bits_equal(c_good, c_bad)
