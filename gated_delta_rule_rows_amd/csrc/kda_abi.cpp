@@ -41,11 +41,15 @@ bool overlap(const Span& a, const Span& b) {
     return a.p < b.p + b.n && b.p < a.p + a.n;
 }
 
-int check_ptrs(const char* fn, const Span* s, int n) {
+// Every pointer must be non-null and 16-byte aligned, except beta (the last
+// span when `beta_elem` is nonzero), which is read one element at a time and
+// only needs element alignment.
+int check_ptrs(const char* fn, const Span* s, int n, unsigned beta_elem = 0) {
     for (int i = 0; i < n; ++i) {
         if (s[i].p == 0) return refuse(KDA_ERR_ARG, "%s: %s is NULL", fn, s[i].name);
-        if (s[i].p % 16 != 0)
-            return refuse(KDA_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, s[i].name);
+        const unsigned align = (beta_elem && i == n - 1) ? beta_elem : 16;
+        if (s[i].p % align != 0)
+            return refuse(KDA_ERR_ALIGN, "%s: %s is not %u-byte aligned", fn, s[i].name, align);
     }
     return KDA_OK;
 }
@@ -102,7 +106,7 @@ int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k,
         {"g", reinterpret_cast<uintptr_t>(g), rows * kda::kD * es},
         {"beta", reinterpret_cast<uintptr_t>(beta), rows * es},
     };
-    if ((rc = check_ptrs(fn, sp, 7))) return rc;
+    if ((rc = check_ptrs(fn, sp, 7, static_cast<unsigned>(es)))) return rc;
     const Span so = {"o", reinterpret_cast<uintptr_t>(o), rows * kda::kD * 4};
     if (o && so.p % 16 != 0) return refuse(KDA_ERR_ALIGN, "%s: o is not 16-byte aligned", fn);
     // s_out: identical to s_in (in place) or disjoint from it; never over a row input
@@ -121,8 +125,8 @@ int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k,
     kda::ScanArgs a{};
     a.s_in = s_in; a.s_out = s_out; a.s_ptrs = nullptr;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
-    a.H = H; a.T = T; a.T_stride = T;
-    return launched(fn, kda::launch_scan(a, chains, in_dtype == KDA_IN_BF16, o != nullptr, false,
+    a.n_chains = chains; a.H = H; a.T = T; a.T_stride = T;
+    return launched(fn, kda::launch_scan(a, in_dtype == KDA_IN_BF16, o != nullptr, false,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -168,7 +172,7 @@ int kda_replay(const float* snap, float* s_out, const void* q, const void* k, co
         {"g", reinterpret_cast<uintptr_t>(g), rows * kda::kD * es},
         {"beta", reinterpret_cast<uintptr_t>(beta), rows * es},
     };
-    if ((rc = check_ptrs(fn, sp, 7))) return rc;
+    if ((rc = check_ptrs(fn, sp, 7, static_cast<unsigned>(es)))) return rc;
     for (int i = 0; i < 7; ++i) {
         if (i != 1 && overlap(sp[1], sp[i]))
             return refuse(KDA_ERR_ALIAS, "%s: s_out overlaps %s", fn, sp[i].name);
@@ -176,8 +180,8 @@ int kda_replay(const float* snap, float* s_out, const void* q, const void* k, co
     kda::ScanArgs a{};
     a.s_in = snap; a.s_out = s_out; a.s_ptrs = nullptr;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = nullptr;
-    a.H = H; a.T = keep; a.T_stride = T_round;
-    return launched(fn, kda::launch_scan(a, chains, in_dtype == KDA_IN_BF16, false, false,
+    a.n_chains = chains; a.H = H; a.T = keep; a.T_stride = T_round;
+    return launched(fn, kda::launch_scan(a, in_dtype == KDA_IN_BF16, false, false,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -203,7 +207,7 @@ int kda_scan_batched(float* const* s_ptrs, const void* q, const void* k, const v
         {"g", reinterpret_cast<uintptr_t>(g), rows * kda::kD * es},
         {"beta", reinterpret_cast<uintptr_t>(beta), rows * es},
     };
-    if ((rc = check_ptrs(fn, sp, 6))) return rc;
+    if ((rc = check_ptrs(fn, sp, 6, static_cast<unsigned>(es)))) return rc;
     const Span so = {"o", reinterpret_cast<uintptr_t>(o), rows * kda::kD * 4};
     if (o) {
         if (so.p % 16 != 0) return refuse(KDA_ERR_ALIGN, "%s: o is not 16-byte aligned", fn);
@@ -215,8 +219,8 @@ int kda_scan_batched(float* const* s_ptrs, const void* q, const void* k, const v
     kda::ScanArgs a{};
     a.s_in = nullptr; a.s_out = nullptr; a.s_ptrs = s_ptrs;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
-    a.H = H; a.T = 1; a.T_stride = 1;
-    return launched(fn, kda::launch_scan(a, chains, in_dtype == KDA_IN_BF16, o != nullptr, true,
+    a.n_chains = chains; a.H = H; a.T = 1; a.T_stride = 1;
+    return launched(fn, kda::launch_scan(a, in_dtype == KDA_IN_BF16, o != nullptr, true,
                                          static_cast<hipStream_t>(stream)));
 }
 

@@ -112,6 +112,12 @@ __device__ __forceinline__ float load1(const void* base, size_t off) {
     }
 }
 
+// An empty asm the compiler must assume rewrites x: arithmetic on x cannot
+// move above this point.
+__device__ __forceinline__ void opaque(float4& x) {
+    asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w)::"memory");
+}
+
 __device__ __forceinline__ float decay_of(float g) {
     return expf(fminf(fmaxf(g, kGateLo), kGateHi));
 }
@@ -138,19 +144,32 @@ __device__ __forceinline__ void store_cols(float* p, const float (&x)[C]) {
 
 // ------------------------------------------------------------------ the scan
 
+// LDS row layout for the per-key vectors (decay, k, scaled q).  A lane reads
+// the R consecutive keys of its group; group ig starts at ig*(R+4) floats so
+// the NI groups of a wave land on distinct bank quads (a plain ig*R stride
+// maps groups ig and ig+2 onto the same banks).
+template <int R>
+struct KeyRow {
+    static constexpr int kPad = 4;
+    static constexpr int kStride = (kD / R) * (R + kPad);   // floats per row
+    __device__ static constexpr int at(int i) { return (i / R) * (R + kPad) + i % R; }
+};
+
 template <int R, int C, bool BF16, bool WRITE_O, bool TABLE>
-__global__ void __launch_bounds__((Tile<R, C>::THREADS))
+__global__ void __launch_bounds__((Tile<R, C>::THREADS)) __attribute__((amdgpu_waves_per_eu(4)))
 kda_scan_kernel(ScanArgs a) {
     using TL = Tile<R, C>;
-    __shared__ float4 sd4[kTMax * kD / 4];   // decay exp(clamp(g)), [t][i]
-    __shared__ float4 sk4[kTMax * kD / 4];   // k, [t][i]
-    __shared__ float4 sq4[kTMax * kD / 4];   // q, [t][i]
-    __shared__ float4 sv4[kTMax * kD / 4];   // v, [t][j]
-    __shared__ float sb[kTMax];              // beta
-    __shared__ float sqk[kTMax];             // q.k
+    using KR = KeyRow<R>;
+    __shared__ float4 sd4[kTMax * KR::kStride / 4];   // exp(clamp(g)), [t][key layout]
+    __shared__ float4 sk4[kTMax * KR::kStride / 4];   // k
+    __shared__ float4 sq4[kTMax * KR::kStride / 4];   // q / sqrt(128)
+    __shared__ float4 sbv4[kTMax * kD / 4];           // beta * v, [t][j]
+    __shared__ float sb[kTMax];                       // beta
+    __shared__ float sqk[kTMax];                      // (q / sqrt(128)) . k
+    float* sd = reinterpret_cast<float*>(sd4);
     float* sk = reinterpret_cast<float*>(sk4);
     float* sq = reinterpret_cast<float*>(sq4);
-    float* sv = reinterpret_cast<float*>(sv4);
+    float* sbv = reinterpret_cast<float*>(sbv4);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -185,35 +204,77 @@ kda_scan_kernel(ScanArgs a) {
         T = a.T;
     }
 
-    // --- state slab into VGPRs (read once per launch)
+    // --- loads: this chain's row inputs first (staged first), then its state
+    //     slab (read once per launch); the counters drain in issue order, so
+    //     staging can start while the state is still in flight
+    constexpr int kPer = (kTMax * (kD / 4) + TL::THREADS - 1) / TL::THREADS;
+    float4 in_k[kPer], in_v[kPer], in_g[kPer], in_q[kPer];
+    float in_b[kPer];
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+        // unconditional (row clamped into range, surplus values unused): a
+        // branch here would make the merge copies wait on the loads
+        const int idx = tid + p * TL::THREADS;
+        const int t = min(idx >> 5, T - 1);
+        const size_t off = row0 + t * rstride + (idx & 31) * 4;
+        in_k[p] = load4<BF16>(a.k, off);
+        in_v[p] = load4<BF16>(a.v, off);
+        in_g[p] = load4<BF16>(a.g, off);
+        if constexpr (WRITE_O) in_q[p] = load4<BF16>(a.q, off);
+        in_b[p] = load1<BF16>(a.beta, b0 + t * bstride);
+    }
     float s[R][C];
 #pragma unroll
     for (int r = 0; r < R; ++r) load_cols<C>(st_in + static_cast<size_t>(i0 + r) * kD + j0, s[r]);
-
-    // --- all T rows' inputs into LDS; exp(clamp(g)) once per (row, key)
-    for (int idx = tid; idx < T * (kD / 4); idx += TL::THREADS) {
-        const int t = idx >> 5;
-        const int c4 = idx & 31;
-        const size_t off = row0 + t * rstride + c4 * 4;
-        const float4 gk = load4<BF16>(a.k, off);
-        const float4 gv = load4<BF16>(a.v, off);
-        const float4 gg = load4<BF16>(a.g, off);
-        sk4[t * 32 + c4] = gk;
-        sv4[t * 32 + c4] = gv;
-        sd4[t * 32 + c4] = make_float4(decay_of(gg.x), decay_of(gg.y), decay_of(gg.z), decay_of(gg.w));
-        if constexpr (WRITE_O) sq4[t * 32 + c4] = load4<BF16>(a.q, off);
+    // keep the staging arithmetic below from being hoisted between the loads
+    // (it would wait on the first input load before the state loads are
+    // issued): the staged values pass through an empty asm placed here
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+        opaque(in_k[p]);
+        opaque(in_v[p]);
+        opaque(in_g[p]);
+        if constexpr (WRITE_O) opaque(in_q[p]);
+        asm volatile("" : "+v"(in_b[p])::"memory");
     }
-    if (tid < T) sb[tid] = load1<BF16>(a.beta, b0 + tid * bstride);
+
+    // --- stage all T rows in LDS: exp(clamp(g)) once per (row, key), q
+    //     pre-scaled by 1/sqrt(128), beta * v
+#pragma unroll
+    for (int p = 0; p < kPer; ++p) {
+        const int idx = tid + p * TL::THREADS;
+        if (idx < T * (kD / 4)) {
+            const int t = idx >> 5;
+            const int c4 = idx & 31;
+            const int kp = t * KR::kStride + KR::at(c4 * 4);   // 4 keys never straddle a group
+            const float bt = in_b[p];
+            const float4 gg = in_g[p];
+            const float4 gv = in_v[p];
+            *reinterpret_cast<float4*>(sk + kp) = in_k[p];
+            *reinterpret_cast<float4*>(sd + kp) =
+                make_float4(decay_of(gg.x), decay_of(gg.y), decay_of(gg.z), decay_of(gg.w));
+            sbv4[t * 32 + c4] = make_float4(bt * gv.x, bt * gv.y, bt * gv.z, bt * gv.w);
+            if constexpr (WRITE_O) {
+                const float4 gq = in_q[p];
+                *reinterpret_cast<float4*>(sq + kp) = make_float4(
+                    gq.x * kInvSqrtD, gq.y * kInvSqrtD, gq.z * kInvSqrtD, gq.w * kInvSqrtD);
+            }
+            if (c4 == 0) sb[t] = bt;
+        }
+    }
     __syncthreads();
 
-    // --- q.k per row: one 16-lane DPP row per verify row, 8 keys per lane in
-    //     ascending order, then the same butterfly as the main reduction
+    // --- (q/sqrt(128)).k per row: one 16-lane DPP row per verify row, 8 keys per
+    //     lane in ascending order, then a fixed butterfly
     if constexpr (WRITE_O) {
         const int l16 = lane & 15;
         for (int t = wave * 4 + (lane >> 4); t < T; t += TL::WAVES * 4) {
             float p = 0.0f;
 #pragma unroll
-            for (int m = 0; m < 8; ++m) p = fmaf(sq[t * kD + l16 * 8 + m], sk[t * kD + l16 * 8 + m], p);
+            for (int m = 0; m < 8; ++m) {
+                const int kp = t * KR::kStride + KR::at(l16 * 8 + m);
+                p = fmaf(sq[kp], sk[kp], p);
+            }
             p = group_sum<16>(p);
             if (l16 == 0) sqk[t] = p;
         }
@@ -223,18 +284,22 @@ kda_scan_kernel(ScanArgs a) {
     // --- the sequential row loop over register state
 #pragma unroll 1
     for (int t = 0; t < T; ++t) {
+        const int kb = t * KR::kStride + KR::at(i0);
         float kk[R], dk[R], qq[R];
 #pragma unroll
         for (int r4 = 0; r4 < R / 4; ++r4) {
-            const float4 x = sk4[(t * kD + i0) / 4 + r4];
-            const float4 y = sd4[(t * kD + i0) / 4 + r4];
+            const float4 x = sk4[kb / 4 + r4];
+            const float4 y = sd4[kb / 4 + r4];
             kk[4 * r4 + 0] = x.x; kk[4 * r4 + 1] = x.y; kk[4 * r4 + 2] = x.z; kk[4 * r4 + 3] = x.w;
             dk[4 * r4 + 0] = y.x; dk[4 * r4 + 1] = y.y; dk[4 * r4 + 2] = y.z; dk[4 * r4 + 3] = y.w;
             if constexpr (WRITE_O) {
-                const float4 z = sq4[(t * kD + i0) / 4 + r4];
+                const float4 z = sq4[kb / 4 + r4];
                 qq[4 * r4 + 0] = z.x; qq[4 * r4 + 1] = z.y; qq[4 * r4 + 2] = z.z; qq[4 * r4 + 3] = z.w;
             }
         }
+        const float nbt = -sb[t];
+        float bv[C];
+        load_cols<C>(sbv + t * kD + j0, bv);
 
         // decay, then the two in-lane partial reductions over this lane's keys
         float u[C], w[C];
@@ -255,13 +320,10 @@ kda_scan_kernel(ScanArgs a) {
             if constexpr (WRITE_O) w[c] = group_sum<TL::NI>(w[c]);
         }
 
-        // delta-rule write
-        const float bt = sb[t];
-        float vv[C];
-        load_cols<C>(sv + t * kD + j0, vv);
+        // delta-rule write: e = beta v - beta u, S = S' + k e^T
         float e[C];
 #pragma unroll
-        for (int c = 0; c < C; ++c) e[c] = bt * (vv[c] - u[c]);
+        for (int c = 0; c < C; ++c) e[c] = fmaf(nbt, u[c], bv[c]);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
 #pragma unroll
@@ -272,7 +334,7 @@ kda_scan_kernel(ScanArgs a) {
             const float qk = sqk[t];
             float ov[C];
 #pragma unroll
-            for (int c = 0; c < C; ++c) ov[c] = fmaf(e[c], qk, w[c]) * kInvSqrtD;
+            for (int c = 0; c < C; ++c) ov[c] = fmaf(e[c], qk, w[c]);
             if (ig == 0) store_cols<C>(a.o + o0 + t * ostride + j0, ov);
         }
     }
@@ -303,27 +365,26 @@ __global__ void __launch_bounds__(256) kda_copy_kernel(const float4* __restrict_
 }
 
 template <bool BF16, bool WRITE_O, bool TABLE>
-hipError_t launch_one(const ScanArgs& a, long long n_chains, hipStream_t stream) {
+hipError_t launch_one(const ScanArgs& a, hipStream_t stream) {
     using TL = TileT;
     kda_scan_kernel<16, 4, BF16, WRITE_O, TABLE>
-        <<<dim3(static_cast<unsigned>(n_chains)), dim3(TL::THREADS), 0, stream>>>(a);
+        <<<dim3(static_cast<unsigned>(a.n_chains)), dim3(TL::THREADS), 0, stream>>>(a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_scan(const ScanArgs& a, long long n_chains, bool bf16, bool write_o, bool table,
-                       hipStream_t stream) {
+hipError_t launch_scan(const ScanArgs& a, bool bf16, bool write_o, bool table, hipStream_t stream) {
     if (table) {
-        if (bf16) return write_o ? launch_one<true, true, true>(a, n_chains, stream)
-                                 : launch_one<true, false, true>(a, n_chains, stream);
-        return write_o ? launch_one<false, true, true>(a, n_chains, stream)
-                       : launch_one<false, false, true>(a, n_chains, stream);
+        if (bf16) return write_o ? launch_one<true, true, true>(a, stream)
+                                 : launch_one<true, false, true>(a, stream);
+        return write_o ? launch_one<false, true, true>(a, stream)
+                       : launch_one<false, false, true>(a, stream);
     }
-    if (bf16) return write_o ? launch_one<true, true, false>(a, n_chains, stream)
-                             : launch_one<true, false, false>(a, n_chains, stream);
-    return write_o ? launch_one<false, true, false>(a, n_chains, stream)
-                   : launch_one<false, false, false>(a, n_chains, stream);
+    if (bf16) return write_o ? launch_one<true, true, false>(a, stream)
+                             : launch_one<true, false, false>(a, stream);
+    return write_o ? launch_one<false, true, false>(a, stream)
+                   : launch_one<false, false, false>(a, stream);
 }
 
 hipError_t launch_copy(const float* src, float* dst, size_t n_floats, hipStream_t stream) {

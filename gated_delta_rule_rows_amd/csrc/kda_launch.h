@@ -26,13 +26,13 @@ struct ScanArgs {
     const void* g;
     const void* beta;
     float* o;        // written only when write_o
+    long long n_chains;  // (layer, head) or (layer, session, head) chains
     int H;
     int T;           // rows scanned by this launch
     int T_stride;    // rows per layer in the input layout (contiguous mode)
 };
 
-hipError_t launch_scan(const ScanArgs& a, long long n_chains, bool bf16, bool write_o, bool table,
-                       hipStream_t stream);
+hipError_t launch_scan(const ScanArgs& a, bool bf16, bool write_o, bool table, hipStream_t stream);
 
 hipError_t launch_copy(const float* src, float* dst, size_t n_floats, hipStream_t stream);
 

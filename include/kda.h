@@ -20,8 +20,9 @@
  * (the pages name the scan but do not print it).
  *
  * Conventions for every entry point:
- *   - Tensor pointers are DEVICE pointers, 16-byte aligned, row-major and
- *     contiguous.  The caller owns every buffer; the library never allocates,
+ *   - Tensor pointers are DEVICE pointers, row-major and contiguous, 16-byte
+ *     aligned -- except beta, which needs only its element alignment (4 bytes
+ *     for f32, 2 for bf16).  The caller owns every buffer; the library never allocates,
  *     frees or synchronizes.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL means
  *     the null stream).

@@ -133,6 +133,10 @@ def test_scan_rows_alignment_and_alias(lib, b):
     off = lambda n, k: ctypes.c_void_p(b.addr[n] + k)
     assert _scan(lib, b, k=off("k", 4)) == ERR_ALIGN and "k is not 16-byte aligned" in _msg(lib)
     assert _scan(lib, b, o=off("o", 8)) == ERR_ALIGN
+    # beta is read per element: it needs element alignment only
+    assert _scan(lib, b, beta=off("beta", 2)) == ERR_ALIGN and "4-byte" in _msg(lib)
+    assert _scan(lib, b, beta=off("beta", 1), dt=1) == ERR_ALIGN and "2-byte" in _msg(lib)
+    assert _batched(lib, b, beta=off("beta", 2)) == ERR_ALIGN
     # s_out partially over s_in
     assert _scan(lib, b, s_out=off("s_in", 4096)) == ERR_ALIAS and "partially" in _msg(lib)
     # s_out over a row input, o over the state
