@@ -88,12 +88,13 @@ def cpu_baseline(host_rounds, js, T, seconds: float):
         rows += T * H * L
         n += 1
         el = time.perf_counter() - t0
-        if el >= seconds or n >= len(js):
+        if el >= seconds:
             break
     return {
         "value": rows / el, "unit": "rows*heads/s", "cores": threads, "kind": "oracle",
-        "sample": f"{n} verify_k14 round(s): all {L}x{H} chains, T={T} scan + accept-j replay, "
-                  f"f64 oracle on {threads} host threads, {el:.1f} s",
+        "sample": f"{n} verify_k14 round(s) (inputs of rounds 0..{len(host_rounds) - 1} "
+                  f"cycled): all {L}x{H} chains, T={T} scan + accept-j replay, f64 oracle on "
+                  f"{threads} host threads, {el:.1f} s",
     }
 
 
@@ -106,13 +107,15 @@ def main() -> int:
                     help="independent state sets visited round-robin (1 = the single-session workload)")
     ap.add_argument("--cold-launches", type=int, default=8,
                     help="extra scan launches timed after a 512 MiB write, for the MALL-cold figure")
+    ap.add_argument("--copy-launches", type=int, default=8,
+                    help="kda_snapshot launches of the full state, timed for the copy ceiling")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; the scan shards by head, layer or "
-              "session with no exchange inside the path (see DESIGN.md), but no multi-GPU run "
+              "session with no exchange inside the path, but no multi-GPU run "
               "is part of it. Run with --gpus 1.", file=sys.stderr)
         return 2
 
@@ -214,7 +217,23 @@ def main() -> int:
             cold_us.append(a.elapsed_time(b) * 1e3)
         del flush
 
-    traffic = measured_traffic("scan_f32_o")
+    # measured copy ceiling: kda_snapshot of the whole 34x64-head state
+    copy_gbps = None
+    if args.copy_launches > 0:
+        src, dst = bufs[0][0], torch.empty_like(bufs[0][0])
+        cu = []
+        for _ in range(args.copy_launches):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            kda.kda_snapshot(src, dst)
+            b.record(stream)
+            torch.cuda.synchronize()
+            cu.append(a.elapsed_time(b) * 1e3)
+        copy_gbps = 2 * src.numel() * 4 / (float(np.median(cu)) * 1e-6) / 1e9
+        del dst
+
+    traffic = measured_traffic("scan")
     line = {
         "metric": "verify-scan rows*heads/s and achieved HBM GB/s (% peak), K=14, 64 heads",
         "value": value,
@@ -250,6 +269,8 @@ def main() -> int:
                               if cold_us else None),
         "replay": ({"launches": len(rep_us), "mean_us": float(np.mean(rep_us)),
                     "mean_keep": float(np.mean(rep_keep)), "gbps": rep_gbps} if rep_us else None),
+        "copy_ceiling_gbps": copy_gbps,
+        "scan_frac_of_copy_ceiling": (achieved / copy_gbps) if copy_gbps else None,
         "round_gbps": round_bytes / (total_ms * 1e-3) / 1e9,
         "round_frac_of_peak": round_bytes / (total_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "committed_rows_heads_per_s": committed,
