@@ -1,17 +1,26 @@
 #!/usr/bin/env python3
 """Throughput of the KDA speculative-verify scan on one MI355X.
 
-One step = one verify round of the 34-layer x 64-head KDA stack at T = 15
-(K = 14 drafts): the T-row scan of every (layer, head) state out of place (the
-untouched input state is the round's snapshot), then, unless all 14 drafts
-were accepted, the accept-j replay of rows 0..j from that snapshot.  The
-accept counts j ~ U{0..14} and the row inputs are seeded and synthetic.
+One step is one verify round of the 34-layer x 64-head KDA stack at T = 15
+(K = 14 drafts) with accept counts j ~ U{0..14}: the round's rows are scanned
+for their outputs, and the state is rolled back to the j + 1 kept rows.  The
+row inputs are seeded and synthetic, and every input is resident in HBM
+before the timed region.
 
-Prints ONE JSON line.  `value` is verify rows x heads x layers per second
-(T rows counted per round), with every input resident in HBM before the timed
-region.  `roofline` covers the dominant kernel (the T = 15 scan): algorithmic
-bytes per launch / its mean launch time from HIP events on the launch stream.
-`cpu_baseline` times the CPU oracle on a bounded sample of the same rounds.
+Two pipelines of the same round are timed in one run:
+
+  fused (the headline): one kda_verify_round launch per round -- replay of
+      the previous round's kept rows from its snapshot (from the stash plane
+      e), store of the committed state (this round's snapshot), scan of this
+      round's rows for o and e.  The state crosses HBM once per round.
+  split: kda_scan_rows out of place (the untouched input is the snapshot),
+      then kda_replay of the kept rows when j < 14.
+
+Prints ONE JSON line.  `value` is verify rows x heads x layers per second of
+the fused pipeline (T rows counted per round).  `roofline` covers its
+dominant kernel (the fused round kernel): algorithmic bytes per launch / mean
+launch time from HIP events on the launch stream.  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same rounds.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
@@ -30,18 +39,26 @@ sys.path.insert(0, ROOT)
 D = 128
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E, AMD published peak
 STATE_BYTES = 4 * D * D         # one head's f32 state
+ROW_BYTES = D * 4               # one f32 128-vector
 KERNEL_SRC = os.path.join(ROOT, "gated_delta_rule_rows_amd", "csrc", "kda_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def scan_bytes_per_head(T: int, es: int = 4) -> int:
-    """State in + out, T rows of q,k,v,g,beta in, T rows of o out."""
-    return 2 * STATE_BYTES + T * (4 * D * es + es) + T * D * 4
+def scan_bytes_per_head(T: int, es: int = 4, stash: bool = False) -> int:
+    """State in + out, T rows of q,k,v,g,beta in, T rows of o (and e) out."""
+    return 2 * STATE_BYTES + T * (4 * D * es + es) + T * ROW_BYTES * (2 if stash else 1)
 
 
 def replay_bytes_per_head(keep: int, es: int = 4) -> int:
     """Snapshot in + state out, keep rows of k,v,g,beta in (q and o are not needed)."""
     return 2 * STATE_BYTES + keep * (3 * D * es + es)
+
+
+def round_bytes_per_head(keep_prev: int, T: int, es: int = 4) -> int:
+    """Fused round: snapshot in + committed state out, keep_prev rows of k, g and
+    the stash e in, T rows of q,k,v,g,beta in, T rows of o and e out."""
+    return (2 * STATE_BYTES + keep_prev * (2 * D * es + ROW_BYTES)
+            + T * (4 * D * es + es) + 2 * T * ROW_BYTES)
 
 
 def kernel_hash() -> str:
@@ -66,6 +83,12 @@ def measured_traffic(kernel: str):
 def pctl(xs, q):
     import numpy as np
     return float(np.percentile(np.asarray(xs), q))
+
+
+def stats_us(xs):
+    import numpy as np
+    return {"mean": float(np.mean(xs)), "p10": pctl(xs, 10), "p50": pctl(xs, 50),
+            "p90": pctl(xs, 90)}
 
 
 def cpu_baseline(host_rounds, js, T, seconds: float):
@@ -106,9 +129,10 @@ def main() -> int:
     ap.add_argument("--sessions", type=int, default=1,
                     help="independent state sets visited round-robin (1 = the single-session workload)")
     ap.add_argument("--cold-launches", type=int, default=8,
-                    help="extra scan launches timed after a 512 MiB write, for the MALL-cold figure")
+                    help="extra round launches timed after a 512 MiB write, for the MALL-cold figure")
     ap.add_argument("--copy-launches", type=int, default=8,
                     help="kda_snapshot launches of the full state, timed for the copy ceiling")
+    ap.add_argument("--no-split", action="store_true", help="skip the split scan + replay pipeline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -133,6 +157,7 @@ def main() -> int:
     L, H, T = w.L, w.H, w.T
     K = T - 1
     js = synth.accepts(w.seed, w.rounds, K)
+    chains = L * H
 
     # inputs: one buffer set per round, generated on the host, resident in HBM
     n_pool = max(1, min(args.steps + args.warmup, w.rounds))
@@ -146,72 +171,113 @@ def main() -> int:
     bufs = [[torch.zeros(L, H, D, D, device="cuda"), torch.zeros(L, H, D, D, device="cuda")]
             for _ in range(S)]
     o = torch.empty(L, T, H, D, device="cuda")
+    # stash planes: the current round's and the previous round's, per session
+    stash = [[torch.zeros(L, T, H, D, device="cuda") for _ in range(2)] for _ in range(S)]
     stream = torch.cuda.current_stream()
 
-    def round_(i, ev=None):
+    def ev():
+        return torch.cuda.Event(enable_timing=True)
+
+    def timed(step_fn, n_warm, n_steps, n_marks):
+        for i in range(n_warm):
+            step_fn(i, None)
+        torch.cuda.synchronize()
+        marks = [[ev() for _ in range(n_marks)] for _ in range(n_steps)]
+        start, end = ev(), ev()
+        info = []
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        start.record(stream)
+        for s in range(n_steps):
+            info.append(step_fn(n_warm + s, marks[s]))
+        end.record(stream)
+        torch.cuda.synchronize()
+        return marks, info, start.elapsed_time(end), time.perf_counter() - wall0
+
+    # ---------------- fused pipeline: one kda_verify_round per round
+    sess_prev = [None] * S   # per session: (rows, stash e, keep) of its previous round
+
+    def fused_round(i, m):
         r = i % w.rounds
         rows = dev_rounds[r % n_pool]
-        pair = bufs[i % S]
-        snap, live = pair
-        keep = int(js[r]) + 1
-        if ev is not None:
-            ev[0].record(stream)
-        kda.kda_scan_rows(snap, live, *rows, o=o)
-        if ev is not None:
-            ev[1].record(stream)
-        replayed = keep < T
-        if replayed:
-            kda.kda_replay(snap, live, *rows, keep=keep)
-            if ev is not None:
-                ev[2].record(stream)
-        pair[0], pair[1] = live, snap
-        return keep, replayed
+        sid = i % S
+        pair = bufs[sid]
+        snap, nxt = pair
+        prev = sess_prev[sid]
+        e_cur = stash[sid][(i // S) % 2]
+        keep_prev = prev[2] if prev else 0
+        if m is not None:
+            m[0].record(stream)
+        if prev:
+            p_rows, p_e, _ = prev
+            kda.kda_verify_round(snap, nxt, (p_rows[1], None, p_rows[3], None, p_e), keep_prev,
+                                 *rows, o, e=e_cur)
+        else:
+            kda.kda_verify_round(snap, nxt, None, 0, *rows, o, e=e_cur)
+        if m is not None:
+            m[1].record(stream)
+        sess_prev[sid] = (rows, e_cur, int(js[r]) + 1)
+        pair[0], pair[1] = nxt, snap
+        return keep_prev
 
-    for i in range(args.warmup):
-        round_(i)
-    torch.cuda.synchronize()
+    fm, finfo, f_ms, f_wall = timed(fused_round, args.warmup, args.steps, 2)
+    f_us = [fm[s][0].elapsed_time(fm[s][1]) * 1e3 for s in range(args.steps)]
+    f_bytes = [chains * round_bytes_per_head(kp, T) for kp in finfo]
+    achieved = sum(f_bytes) / (sum(f_us) * 1e-6) / 1e9
+    value = args.steps * T * H * L / (f_ms * 1e-3)
+    ms_per_step = f_ms / args.steps
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    info = []
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for s in range(args.steps):
-        info.append(round_(args.warmup + s, evs[s]))
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(end)
+    # ---------------- split pipeline: scan, then replay when j < 14
+    split = None
+    if not args.no_split:
+        def split_round(i, m):
+            r = i % w.rounds
+            rows = dev_rounds[r % n_pool]
+            pair = bufs[i % S]
+            snap, live = pair
+            keep = int(js[r]) + 1
+            if m is not None:
+                m[0].record(stream)
+            kda.kda_scan_rows(snap, live, *rows, o=o)
+            if m is not None:
+                m[1].record(stream)
+            replayed = keep < T
+            if replayed:
+                kda.kda_replay(snap, live, *rows[1:], keep=keep)
+                if m is not None:
+                    m[2].record(stream)
+            pair[0], pair[1] = live, snap
+            return keep, replayed
 
-    scan_us = [evs[s][0].elapsed_time(evs[s][1]) * 1e3 for s in range(args.steps)]
-    rep_us = [evs[s][1].elapsed_time(evs[s][2]) * 1e3 for s in range(args.steps) if info[s][1]]
-    rep_keep = [info[s][0] for s in range(args.steps) if info[s][1]]
+        sm, sinfo, s_ms, _ = timed(split_round, args.warmup, args.steps, 3)
+        scan_us = [sm[s][0].elapsed_time(sm[s][1]) * 1e3 for s in range(args.steps)]
+        rep_us = [sm[s][1].elapsed_time(sm[s][2]) * 1e3 for s in range(args.steps) if sinfo[s][1]]
+        rep_keep = [sinfo[s][0] for s in range(args.steps) if sinfo[s][1]]
+        scan_bytes = chains * scan_bytes_per_head(T)
+        rep_bytes = [chains * replay_bytes_per_head(k) for k in rep_keep]
+        split = {
+            "value": args.steps * T * H * L / (s_ms * 1e-3),
+            "ms_per_step": s_ms / args.steps,
+            "scan_us": stats_us(scan_us),
+            "scan_gbps": scan_bytes / (float(np.mean(scan_us)) * 1e-6) / 1e9,
+            "replay": ({"launches": len(rep_us), "mean_us": float(np.mean(rep_us)),
+                        "mean_keep": float(np.mean(rep_keep)),
+                        "gbps": sum(rep_bytes) / (sum(rep_us) * 1e-6) / 1e9} if rep_us else None),
+            "round_gbps": (args.steps * scan_bytes + sum(rep_bytes)) / (s_ms * 1e-3) / 1e9,
+        }
 
-    chains = L * H
-    scan_bytes = chains * scan_bytes_per_head(T)
-    mean_scan_us = float(np.mean(scan_us))
-    achieved = scan_bytes / (mean_scan_us * 1e-6) / 1e9
-    rep_bytes = [chains * replay_bytes_per_head(k) for k in rep_keep]
-    rep_gbps = (sum(rep_bytes) / (sum(rep_us) * 1e-6) / 1e9) if rep_us else None
-    round_bytes = args.steps * scan_bytes + sum(rep_bytes)
-    ms_per_step = total_ms / args.steps
-    value = args.steps * T * H * L / (total_ms * 1e-3)
-    committed = sum(k for k, _ in info) * H * L / (total_ms * 1e-3)
-
-    # MALL-cold scan launches: write 512 MiB between launches, time the launch alone
+    # MALL-cold round launches: write 512 MiB between launches, time the launch alone
     cold_us = []
     if args.cold_launches > 0:
         flush = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
-        snap, live = bufs[0]
+        snap, nxt = bufs[0]
         rows = dev_rounds[0]
         for _ in range(args.cold_launches):
             flush.zero_()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
+            a, b = ev(), ev()
             a.record(stream)
-            kda.kda_scan_rows(snap, live, *rows, o=o)
+            kda.kda_verify_round(snap, nxt, (rows[1], None, rows[3], None, stash[0][0]), 8,
+                                 *rows, o, e=stash[0][1])
             b.record(stream)
             torch.cuda.synchronize()
             cold_us.append(a.elapsed_time(b) * 1e3)
@@ -223,8 +289,7 @@ def main() -> int:
         src, dst = bufs[0][0], torch.empty_like(bufs[0][0])
         cu = []
         for _ in range(args.copy_launches):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
+            a, b = ev(), ev()
             a.record(stream)
             kda.kda_snapshot(src, dst)
             b.record(stream)
@@ -233,7 +298,6 @@ def main() -> int:
         copy_gbps = 2 * src.numel() * 4 / (float(np.median(cu)) * 1e-6) / 1e9
         del dst
 
-    traffic = measured_traffic("scan")
     line = {
         "metric": "verify-scan rows*heads/s and achieved HBM GB/s (% peak), K=14, 64 heads",
         "value": value,
@@ -249,32 +313,31 @@ def main() -> int:
         "data": "synthetic",
         "config": {
             "workload": "verify_k14", "layers": L, "heads": H, "T": T, "K": K,
-            "rounds": w.rounds, "accept": "j~U{0..14}, replay keep=j+1 when j<14",
-            "state": "f32 [34][64][128][128], out-of-place scan (input state = snapshot)",
-            "inputs": "f32 q,k,v,g [34][15][64][128], beta [34][15][64]", "sessions": S,
-            "seed": w.seed,
+            "rounds": w.rounds, "accept": "j~U{0..14}, keep=j+1 rows committed",
+            "pipeline": "fused kda_verify_round (replay of the previous round's kept rows + "
+                        "this round's scan; the state crosses HBM once per round)",
+            "state": "f32 [34][64][128][128]",
+            "inputs": "f32 q,k,v,g [34][15][64][128], beta [34][15][64]; stash e f32",
+            "sessions": S, "seed": w.seed,
         },
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS,
-            "traffic": traffic,
-            "kernel": "kda_scan_kernel<f32, o> (T=15, 2176 workgroups)",
-            "bytes_per_launch": scan_bytes,
-            "mean_launch_us": mean_scan_us,
+            "traffic": measured_traffic("round"),
+            "kernel": "kda_verify_round kernel (replay from the stash + full-row scan, "
+                      "2176 workgroups)",
+            "bytes_per_launch": sum(f_bytes) / len(f_bytes),
+            "mean_launch_us": float(np.mean(f_us)),
         },
-        "scan_us": {"mean": mean_scan_us, "p10": pctl(scan_us, 10), "p50": pctl(scan_us, 50),
-                    "p90": pctl(scan_us, 90)},
-        "scan_us_mall_cold": ({"mean": float(np.mean(cold_us)), "p50": pctl(cold_us, 50),
-                               "gbps": scan_bytes / (float(np.mean(cold_us)) * 1e-6) / 1e9}
-                              if cold_us else None),
-        "replay": ({"launches": len(rep_us), "mean_us": float(np.mean(rep_us)),
-                    "mean_keep": float(np.mean(rep_keep)), "gbps": rep_gbps} if rep_us else None),
+        "round_us": stats_us(f_us),
+        "round_us_mall_cold": ({"mean": float(np.mean(cold_us)), "p50": pctl(cold_us, 50)}
+                               if cold_us else None),
+        "committed_rows_heads_per_s": sum(int(js[(args.warmup + s) % w.rounds]) + 1
+                                          for s in range(args.steps)) * H * L / (f_ms * 1e-3),
+        "split": split,
         "copy_ceiling_gbps": copy_gbps,
-        "scan_frac_of_copy_ceiling": (achieved / copy_gbps) if copy_gbps else None,
-        "round_gbps": round_bytes / (total_ms * 1e-3) / 1e9,
-        "round_frac_of_peak": round_bytes / (total_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "committed_rows_heads_per_s": committed,
-        "wall_s_timed": wall,
+        "frac_of_copy_ceiling": (achieved / copy_gbps) if copy_gbps else None,
+        "wall_s_timed": f_wall,
         "input_gen_s": gen_s,
     }
     if not args.no_cpu_baseline:

@@ -12,6 +12,8 @@ Shapes (D = 128):
   q, k, v, g       [L][T][H][D] float32 or bfloat16 (all five the same dtype)
   beta             [L][T][H]
   o                [L][T][H][D] float32 or None
+  e (stash plane)  [L][T][H][D] float32 or None: per-row delta vectors a scan
+                   writes and a replay (or the next fused round) reads
   batched arm      rows [L][B][H][D], beta [L][B][H], o [L][B][H][D];
                    s_ptrs = state_table(...) -> int64 device tensor [L*B]
 """
@@ -54,12 +56,14 @@ def load():
             f"{_LIB_PATH} is not built; run `python -m gated_delta_rule_rows_amd.build`")
     lib = ctypes.CDLL(_LIB_PATH)
     p, i = ctypes.c_void_p, ctypes.c_int
-    lib.kda_scan_rows.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, p]
+    lib.kda_scan_rows.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, p]
     lib.kda_snapshot.argtypes = [p, p, i, i, p]
     lib.kda_replay.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, p]
     lib.kda_scan_batched.argtypes = [p, p, p, p, p, p, p, i, i, i, i, p]
+    lib.kda_verify_round.argtypes = [p, p, p, p, p, p, p, i, i, p, p, p, p, p, p, p,
+                                     i, i, i, i, p]
     for fn in (lib.kda_scan_rows, lib.kda_snapshot, lib.kda_replay, lib.kda_scan_batched,
-               lib.kda_abi_version):
+               lib.kda_verify_round, lib.kda_abi_version):
         fn.restype = i
     lib.kda_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -120,23 +124,34 @@ def _rows_shape(q, k, v, g, beta):
     return L, T, H
 
 
-def kda_scan_rows(s_in, s_out, q, k, v, g, beta, o=None, stream=None) -> None:
+def _state(t, shape, name):
+    _shape(t, shape, name)
+    _f32(t, name)
+
+
+def _plane(t, shape, name):
+    """An optional f32 [.., D] plane (o or the stash e)."""
+    if t is not None:
+        _shape(t, shape, name)
+        _f32(t, name)
+
+
+def kda_scan_rows(s_in, s_out, q, k, v, g, beta, o=None, e=None, stream=None) -> None:
     """Scan the T rows of q/k/v/g/beta over every (layer, head) state.
 
     s_out may be s_in (in place); a distinct s_out leaves s_in as the snapshot.
+    o receives the outputs, e (optional) the stash plane for a cheaper replay.
     """
     lib = load()
     L, T, H = _rows_shape(q, k, v, g, beta)
-    for st, n in ((s_in, "s_in"), (s_out, "s_out")):
-        _shape(st, (L, H, D, D), n)
-        _f32(st, n)
-    if o is not None:
-        _shape(o, (L, T, H, D), "o")
-        _f32(o, "o")
+    _state(s_in, (L, H, D, D), "s_in")
+    _state(s_out, (L, H, D, D), "s_out")
+    _plane(o, (L, T, H, D), "o")
+    _plane(e, (L, T, H, D), "e")
     dt = _in_dtype((q, k, v, g, beta))
     _check(lib.kda_scan_rows(_dev(s_in, "s_in"), _dev(s_out, "s_out"), _dev(q, "q"), _dev(k, "k"),
                              _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"),
-                             L, T, H, dt, _stream(stream)))
+                             _dev(e, "e"), L, T, H, dt, _stream(stream)))
 
 
 def kda_snapshot(s, snap, stream=None) -> None:
@@ -151,20 +166,69 @@ def kda_snapshot(s, snap, stream=None) -> None:
     _check(lib.kda_snapshot(_dev(s, "s"), _dev(snap, "snap"), L, H, _stream(stream)))
 
 
-def kda_replay(snap, s_out, q, k, v, g, beta, keep: int, stream=None) -> None:
+def _kept_rows(k, v, g, beta, e, what):
+    """Shape check of a round's retained rows; v and beta may be None when e is given."""
+    if k.dim() != 4 or k.shape[-1] != D:
+        raise ValueError(f"{what} k must be [L][T][H][{D}], got {tuple(k.shape)}")
+    L, T, H, _ = k.shape
+    _shape(g, k.shape, f"{what} g")
+    present = [k, g]
+    if e is None or v is not None:
+        if v is None or beta is None:
+            raise ValueError(f"{what}: v and beta are needed without the stash plane e")
+        _shape(v, k.shape, f"{what} v")
+        _shape(beta, (L, T, H), f"{what} beta")
+        present += [v, beta]
+    _plane(e, (L, T, H, D), f"{what} e")
+    return L, T, H, _in_dtype(present)
+
+
+def kda_replay(snap, s_out, k, v, g, beta, keep: int, e=None, stream=None) -> None:
     """s_out = state after rows 0..keep-1 of the round, rebuilt from snap.
 
-    q..beta are the round's retained inputs ([L][T_round][H]...); keep = j + 1.
+    k, v, g [L][T_round][H][D] and beta [L][T_round][H] are the round's retained
+    inputs; keep = j + 1.  With the round's stash plane e, v and beta may be None.
     """
     lib = load()
-    L, T_round, H = _rows_shape(q, k, v, g, beta)
-    for st, n in ((snap, "snap"), (s_out, "s_out")):
-        _shape(st, (L, H, D, D), n)
-        _f32(st, n)
+    L, T_round, H, dt = _kept_rows(k, v, g, beta, e, "replay")
+    _state(snap, (L, H, D, D), "snap")
+    _state(s_out, (L, H, D, D), "s_out")
+    _check(lib.kda_replay(_dev(snap, "snap"), _dev(s_out, "s_out"), _dev(k, "k"), _dev(v, "v"),
+                          _dev(g, "g"), _dev(beta, "beta"), _dev(e, "e"), L, T_round, int(keep),
+                          H, dt, _stream(stream)))
+
+
+def kda_verify_round(snap_prev, snap_out, prev, keep: int, q, k, v, g, beta, o, e=None,
+                     stream=None) -> None:
+    """One fused verify round.
+
+    prev = (k, v, g, beta, e) of the previous round (v/beta may be None when its
+    stash e is given; prev may be None when keep == 0).  snap_out receives
+    snap_prev advanced by the previous round's first `keep` rows (this round's
+    snapshot); o receives this round's outputs, e (optional) its stash plane.
+    """
+    lib = load()
+    L, T, H = _rows_shape(q, k, v, g, beta)
     dt = _in_dtype((q, k, v, g, beta))
-    _check(lib.kda_replay(_dev(snap, "snap"), _dev(s_out, "s_out"), _dev(q, "q"), _dev(k, "k"),
-                          _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"), L, T_round, int(keep), H,
-                          dt, _stream(stream)))
+    _state(snap_prev, (L, H, D, D), "snap_prev")
+    _state(snap_out, (L, H, D, D), "snap_out")
+    _plane(o, (L, T, H, D), "o")
+    _plane(e, (L, T, H, D), "e")
+    if prev is None:
+        if keep != 0:
+            raise ValueError("keep > 0 needs the previous round's rows")
+        pk = pv = pg = pb = pe = None
+        T_prev = 0
+    else:
+        pk, pv, pg, pb, pe = prev
+        Lp, T_prev, Hp, pdt = _kept_rows(pk, pv, pg, pb, pe, "prev")
+        if (Lp, Hp) != (L, H) or pdt != dt:
+            raise ValueError("previous round's rows do not match this round's L, H, dtype")
+    _check(lib.kda_verify_round(
+        _dev(snap_prev, "snap_prev"), _dev(snap_out, "snap_out"), _dev(pk, "pk"), _dev(pv, "pv"),
+        _dev(pg, "pg"), _dev(pb, "pbeta"), _dev(pe, "pe"), int(T_prev), int(keep), _dev(q, "q"),
+        _dev(k, "k"), _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"),
+        _dev(e, "e"), L, T, H, dt, _stream(stream)))
 
 
 def state_table(states, device=None) -> torch.Tensor:
@@ -222,5 +286,6 @@ def kda_last_error() -> str:
 
 __all__ = [
     "D", "T_MAX", "B_MAX", "KdaError", "load", "lib_path", "kda_scan_rows", "kda_snapshot",
-    "kda_replay", "kda_scan_batched", "state_table", "kda_abi_version", "kda_last_error",
+    "kda_replay", "kda_scan_batched", "kda_verify_round", "state_table", "kda_abi_version",
+    "kda_last_error",
 ]

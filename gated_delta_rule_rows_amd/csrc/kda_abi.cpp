@@ -29,27 +29,54 @@ int refuse(int code, const char* fmt, ...) {
     return code;
 }
 
-// A byte range [p, p + n) of device memory.
+// A byte range [p, p + n) of device memory, with the alignment it needs.
 struct Span {
     const char* name;
-    uintptr_t p;
+    const void* ptr;
     unsigned long long n;
+    unsigned align;
+    bool optional;   // may be NULL
 };
 
+uintptr_t addr(const Span& s) { return reinterpret_cast<uintptr_t>(s.ptr); }
+
 bool overlap(const Span& a, const Span& b) {
-    if (a.p == 0 || b.p == 0 || a.n == 0 || b.n == 0) return false;
-    return a.p < b.p + b.n && b.p < a.p + a.n;
+    if (!a.ptr || !b.ptr || a.n == 0 || b.n == 0) return false;
+    return addr(a) < addr(b) + b.n && addr(b) < addr(a) + a.n;
 }
 
-// Every pointer must be non-null and 16-byte aligned, except beta (the last
-// span when `beta_elem` is nonzero), which is read one element at a time and
-// only needs element alignment.
-int check_ptrs(const char* fn, const Span* s, int n, unsigned beta_elem = 0) {
+int check_spans(const char* fn, const Span* s, int n) {
     for (int i = 0; i < n; ++i) {
-        if (s[i].p == 0) return refuse(KDA_ERR_ARG, "%s: %s is NULL", fn, s[i].name);
-        const unsigned align = (beta_elem && i == n - 1) ? beta_elem : 16;
-        if (s[i].p % align != 0)
-            return refuse(KDA_ERR_ALIGN, "%s: %s is not %u-byte aligned", fn, s[i].name, align);
+        if (!s[i].ptr) {
+            if (s[i].optional) continue;
+            return refuse(KDA_ERR_ARG, "%s: %s is NULL", fn, s[i].name);
+        }
+        if (addr(s[i]) % s[i].align != 0)
+            return refuse(KDA_ERR_ALIGN, "%s: %s is not %u-byte aligned", fn, s[i].name, s[i].align);
+    }
+    return KDA_OK;
+}
+
+// No output may overlap an input or another output.  `same_out`/`same_in`
+// name one (output, input) pair that may be the identical buffer (a state
+// updated in place); a partial overlap of that pair is still refused.
+int check_alias(const char* fn, const Span* out, int n_out, const Span* in, int n_in,
+                const Span* same_out = nullptr, const Span* same_in = nullptr) {
+    for (int i = 0; i < n_out; ++i) {
+        for (int j = 0; j < n_in; ++j) {
+            const bool pair = &out[i] == same_out && &in[j] == same_in;
+            if (pair && out[i].ptr == in[j].ptr) continue;
+            if (overlap(out[i], in[j])) {
+                if (pair)
+                    return refuse(KDA_ERR_ALIAS, "%s: %s partially overlaps %s", fn, out[i].name,
+                                  in[j].name);
+                return refuse(KDA_ERR_ALIAS, "%s: %s overlaps %s", fn, out[i].name, in[j].name);
+            }
+        }
+        for (int j = i + 1; j < n_out; ++j) {
+            if (overlap(out[i], out[j]))
+                return refuse(KDA_ERR_ALIAS, "%s: %s overlaps %s", fn, out[i].name, out[j].name);
+        }
     }
     return KDA_OK;
 }
@@ -57,6 +84,7 @@ int check_ptrs(const char* fn, const Span* s, int n, unsigned beta_elem = 0) {
 int check_counts(const char* fn, long long L, long long H) {
     if (L < 1) return refuse(KDA_ERR_RANGE, "%s: L=%lld, need L >= 1", fn, L);
     if (H < 1) return refuse(KDA_ERR_RANGE, "%s: H=%lld, need H >= 1", fn, H);
+    if (L * H > INT_MAX) return refuse(KDA_ERR_RANGE, "%s: L*H=%lld too large", fn, L * H);
     return KDA_OK;
 }
 
@@ -67,6 +95,13 @@ int check_dtype(const char* fn, int in_dtype) {
     return KDA_OK;
 }
 
+int check_rows(const char* fn, const char* what, int T) {
+    if (T < 1 || T > KDA_T_MAX)
+        return refuse(KDA_ERR_RANGE, "%s: %s=%d outside 1..%d (K+1 verify rows, K <= 14)", fn, what,
+                      T, KDA_T_MAX);
+    return KDA_OK;
+}
+
 int launched(const char* fn, hipError_t e) {
     if (e != hipSuccess) return refuse(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
     g_err[0] = '\0';
@@ -74,6 +109,7 @@ int launched(const char* fn, hipError_t e) {
 }
 
 constexpr unsigned long long kStateBytes = 4ull * kda::kD * kda::kD;
+constexpr unsigned long long kRowElems = kda::kD;
 
 }  // namespace
 
@@ -84,49 +120,38 @@ int kda_abi_version(void) { return KDA_ABI_VERSION; }
 const char* kda_last_error(void) { return g_err; }
 
 int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k, const void* v,
-                  const void* g, const void* beta, float* o, int L, int T, int H, int in_dtype,
-                  void* stream) {
+                  const void* g, const void* beta, float* o, float* e, int L, int T, int H,
+                  int in_dtype, void* stream) {
     const char* fn = "kda_scan_rows";
     int rc;
-    if ((rc = check_dtype(fn, in_dtype))) return rc;
-    if ((rc = check_counts(fn, L, H))) return rc;
-    if (T < 1 || T > KDA_T_MAX)
-        return refuse(KDA_ERR_RANGE, "%s: T=%d outside 1..%d (K+1 verify rows, K <= 14)", fn, T,
-                      KDA_T_MAX);
-    const long long chains = static_cast<long long>(L) * H;
-    if (chains > INT_MAX) return refuse(KDA_ERR_RANGE, "%s: L*H=%lld too large", fn, chains);
-    const unsigned long long es = in_dtype == KDA_IN_BF16 ? 2 : 4;
-    const unsigned long long rows = static_cast<unsigned long long>(chains) * T;
-    const Span sp[] = {
-        {"s_in", reinterpret_cast<uintptr_t>(s_in), chains * kStateBytes},
-        {"s_out", reinterpret_cast<uintptr_t>(s_out), chains * kStateBytes},
-        {"q", reinterpret_cast<uintptr_t>(q), rows * kda::kD * es},
-        {"k", reinterpret_cast<uintptr_t>(k), rows * kda::kD * es},
-        {"v", reinterpret_cast<uintptr_t>(v), rows * kda::kD * es},
-        {"g", reinterpret_cast<uintptr_t>(g), rows * kda::kD * es},
-        {"beta", reinterpret_cast<uintptr_t>(beta), rows * es},
+    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H)) ||
+        (rc = check_rows(fn, "T", T)))
+        return rc;
+    const unsigned long long chains = static_cast<unsigned long long>(L) * H;
+    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
+    const unsigned long long rows = chains * T;
+    const Span in[] = {
+        {"s_in", s_in, chains * kStateBytes, 16, false},
+        {"q", q, rows * kRowElems * es, 16, false},
+        {"k", k, rows * kRowElems * es, 16, false},
+        {"v", v, rows * kRowElems * es, 16, false},
+        {"g", g, rows * kRowElems * es, 16, false},
+        {"beta", beta, rows * es, es, false},
     };
-    if ((rc = check_ptrs(fn, sp, 7, static_cast<unsigned>(es)))) return rc;
-    const Span so = {"o", reinterpret_cast<uintptr_t>(o), rows * kda::kD * 4};
-    if (o && so.p % 16 != 0) return refuse(KDA_ERR_ALIGN, "%s: o is not 16-byte aligned", fn);
-    // s_out: identical to s_in (in place) or disjoint from it; never over a row input
-    if (sp[1].p != sp[0].p && overlap(sp[0], sp[1]))
-        return refuse(KDA_ERR_ALIAS, "%s: s_out partially overlaps s_in", fn);
-    for (int i = 2; i < 7; ++i) {
-        if (overlap(sp[1], sp[i]))
-            return refuse(KDA_ERR_ALIAS, "%s: s_out overlaps %s", fn, sp[i].name);
-    }
-    if (o) {
-        for (int i = 0; i < 7; ++i) {
-            if (overlap(so, sp[i]))
-                return refuse(KDA_ERR_ALIAS, "%s: o overlaps %s", fn, sp[i].name);
-        }
-    }
+    const Span out[] = {
+        {"s_out", s_out, chains * kStateBytes, 16, false},
+        {"o", o, rows * kRowElems * 4, 16, true},
+        {"e", e, rows * kRowElems * 4, 16, true},
+    };
+    if ((rc = check_spans(fn, in, 6)) || (rc = check_spans(fn, out, 3)) ||
+        (rc = check_alias(fn, out, 3, in, 6, &out[0], &in[0])))
+        return rc;
     kda::ScanArgs a{};
-    a.s_in = s_in; a.s_out = s_out; a.s_ptrs = nullptr;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
-    a.n_chains = chains; a.H = H; a.T = T; a.T_stride = T;
-    return launched(fn, kda::launch_scan(a, in_dtype == KDA_IN_BF16, o != nullptr, false,
+    a.s_in = s_in; a.s_out = s_out;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.e_out = e;
+    a.n_chains = static_cast<long long>(chains); a.H = H; a.T = T; a.T_stride = T;
+    const kda::Launch kind = o ? kda::Launch::kScanOut : kda::Launch::kScanState;
+    return launched(fn, kda::launch_scan(a, kind, in_dtype == KDA_IN_BF16,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -134,54 +159,51 @@ int kda_snapshot(const float* s, float* snap, int L, int H, void* stream) {
     const char* fn = "kda_snapshot";
     int rc;
     if ((rc = check_counts(fn, L, H))) return rc;
-    const long long chains = static_cast<long long>(L) * H;
-    const Span sp[] = {
-        {"s", reinterpret_cast<uintptr_t>(s), chains * kStateBytes},
-        {"snap", reinterpret_cast<uintptr_t>(snap), chains * kStateBytes},
-    };
-    if ((rc = check_ptrs(fn, sp, 2))) return rc;
-    if (overlap(sp[0], sp[1])) return refuse(KDA_ERR_ALIAS, "%s: snap overlaps s", fn);
+    const unsigned long long chains = static_cast<unsigned long long>(L) * H;
+    const Span in[] = {{"s", s, chains * kStateBytes, 16, false}};
+    const Span out[] = {{"snap", snap, chains * kStateBytes, 16, false}};
+    if ((rc = check_spans(fn, in, 1)) || (rc = check_spans(fn, out, 1)) ||
+        (rc = check_alias(fn, out, 1, in, 1)))
+        return rc;
     return launched(fn, kda::launch_copy(s, snap, static_cast<size_t>(chains) * kda::kD * kda::kD,
                                          static_cast<hipStream_t>(stream)));
 }
 
-int kda_replay(const float* snap, float* s_out, const void* q, const void* k, const void* v,
-               const void* g, const void* beta, int L, int T_round, int keep, int H, int in_dtype,
+int kda_replay(const float* snap, float* s_out, const void* k, const void* v, const void* g,
+               const void* beta, const float* e, int L, int T_round, int keep, int H, int in_dtype,
                void* stream) {
     const char* fn = "kda_replay";
     int rc;
-    if ((rc = check_dtype(fn, in_dtype))) return rc;
-    if ((rc = check_counts(fn, L, H))) return rc;
-    if (T_round < 1 || T_round > KDA_T_MAX)
-        return refuse(KDA_ERR_RANGE, "%s: T_round=%d outside 1..%d", fn, T_round, KDA_T_MAX);
+    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H)) ||
+        (rc = check_rows(fn, "T_round", T_round)))
+        return rc;
     if (keep < 1 || keep > T_round)
         return refuse(KDA_ERR_RANGE,
                       "%s: keep=%d outside 1..=%d (the anchor row is always committed; "
                       "keep = accepted drafts + 1)",
                       fn, keep, T_round);
-    const long long chains = static_cast<long long>(L) * H;
-    if (chains > INT_MAX) return refuse(KDA_ERR_RANGE, "%s: L*H=%lld too large", fn, chains);
-    const unsigned long long es = in_dtype == KDA_IN_BF16 ? 2 : 4;
-    const unsigned long long rows = static_cast<unsigned long long>(chains) * T_round;
-    const Span sp[] = {
-        {"snap", reinterpret_cast<uintptr_t>(snap), chains * kStateBytes},
-        {"s_out", reinterpret_cast<uintptr_t>(s_out), chains * kStateBytes},
-        {"q", reinterpret_cast<uintptr_t>(q), rows * kda::kD * es},
-        {"k", reinterpret_cast<uintptr_t>(k), rows * kda::kD * es},
-        {"v", reinterpret_cast<uintptr_t>(v), rows * kda::kD * es},
-        {"g", reinterpret_cast<uintptr_t>(g), rows * kda::kD * es},
-        {"beta", reinterpret_cast<uintptr_t>(beta), rows * es},
+    const unsigned long long chains = static_cast<unsigned long long>(L) * H;
+    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
+    const unsigned long long rows = chains * T_round;
+    const bool stash = e != nullptr;   // with the stash plane, v and beta are not read
+    const Span in[] = {
+        {"snap", snap, chains * kStateBytes, 16, false},
+        {"k", k, rows * kRowElems * es, 16, false},
+        {"g", g, rows * kRowElems * es, 16, false},
+        {"v", v, rows * kRowElems * es, 16, stash},
+        {"beta", beta, rows * es, es, stash},
+        {"e", e, rows * kRowElems * 4, 16, true},
     };
-    if ((rc = check_ptrs(fn, sp, 7, static_cast<unsigned>(es)))) return rc;
-    for (int i = 0; i < 7; ++i) {
-        if (i != 1 && overlap(sp[1], sp[i]))
-            return refuse(KDA_ERR_ALIAS, "%s: s_out overlaps %s", fn, sp[i].name);
-    }
+    const Span out[] = {{"s_out", s_out, chains * kStateBytes, 16, false}};
+    if ((rc = check_spans(fn, in, 6)) || (rc = check_spans(fn, out, 1)) ||
+        (rc = check_alias(fn, out, 1, in, 6)))
+        return rc;
     kda::ScanArgs a{};
-    a.s_in = snap; a.s_out = s_out; a.s_ptrs = nullptr;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = nullptr;
-    a.n_chains = chains; a.H = H; a.T = keep; a.T_stride = T_round;
-    return launched(fn, kda::launch_scan(a, in_dtype == KDA_IN_BF16, false, false,
+    a.s_in = snap; a.s_out = s_out;
+    a.k = k; a.v = v; a.g = g; a.beta = beta; a.e_in = e;
+    a.n_chains = static_cast<long long>(chains); a.H = H; a.T = keep; a.T_stride = T_round;
+    const kda::Launch kind = stash ? kda::Launch::kReplayStash : kda::Launch::kReplay;
+    return launched(fn, kda::launch_scan(a, kind, in_dtype == KDA_IN_BF16,
                                          static_cast<hipStream_t>(stream)));
 }
 
@@ -190,37 +212,83 @@ int kda_scan_batched(float* const* s_ptrs, const void* q, const void* k, const v
                      void* stream) {
     const char* fn = "kda_scan_batched";
     int rc;
-    if ((rc = check_dtype(fn, in_dtype))) return rc;
-    if ((rc = check_counts(fn, L, H))) return rc;
+    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H))) return rc;
     if (B < 1 || B > KDA_B_MAX)
         return refuse(KDA_ERR_RANGE, "%s: B=%d outside 1..%d (per-row exactness knee)", fn, B,
                       KDA_B_MAX);
-    const long long chains = static_cast<long long>(L) * B * H;
-    if (chains > INT_MAX) return refuse(KDA_ERR_RANGE, "%s: L*B*H=%lld too large", fn, chains);
-    const unsigned long long es = in_dtype == KDA_IN_BF16 ? 2 : 4;
-    const unsigned long long rows = static_cast<unsigned long long>(chains);
-    const Span sp[] = {
-        {"s_ptrs", reinterpret_cast<uintptr_t>(s_ptrs), static_cast<unsigned long long>(L) * B * 8},
-        {"q", reinterpret_cast<uintptr_t>(q), rows * kda::kD * es},
-        {"k", reinterpret_cast<uintptr_t>(k), rows * kda::kD * es},
-        {"v", reinterpret_cast<uintptr_t>(v), rows * kda::kD * es},
-        {"g", reinterpret_cast<uintptr_t>(g), rows * kda::kD * es},
-        {"beta", reinterpret_cast<uintptr_t>(beta), rows * es},
+    const unsigned long long chains = static_cast<unsigned long long>(L) * B * H;
+    if (chains > INT_MAX) return refuse(KDA_ERR_RANGE, "%s: L*B*H=%llu too large", fn, chains);
+    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
+    const Span in[] = {
+        {"s_ptrs", s_ptrs, static_cast<unsigned long long>(L) * B * 8, 8, false},
+        {"q", q, chains * kRowElems * es, 16, false},
+        {"k", k, chains * kRowElems * es, 16, false},
+        {"v", v, chains * kRowElems * es, 16, false},
+        {"g", g, chains * kRowElems * es, 16, false},
+        {"beta", beta, chains * es, es, false},
     };
-    if ((rc = check_ptrs(fn, sp, 6, static_cast<unsigned>(es)))) return rc;
-    const Span so = {"o", reinterpret_cast<uintptr_t>(o), rows * kda::kD * 4};
-    if (o) {
-        if (so.p % 16 != 0) return refuse(KDA_ERR_ALIGN, "%s: o is not 16-byte aligned", fn);
-        for (int i = 0; i < 6; ++i) {
-            if (overlap(so, sp[i]))
-                return refuse(KDA_ERR_ALIAS, "%s: o overlaps %s", fn, sp[i].name);
-        }
-    }
+    const Span out[] = {{"o", o, chains * kRowElems * 4, 16, true}};
+    if ((rc = check_spans(fn, in, 6)) || (rc = check_spans(fn, out, 1)) ||
+        (rc = check_alias(fn, out, 1, in, 6)))
+        return rc;
     kda::ScanArgs a{};
-    a.s_in = nullptr; a.s_out = nullptr; a.s_ptrs = s_ptrs;
+    a.s_ptrs = s_ptrs;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o;
-    a.n_chains = chains; a.H = H; a.T = 1; a.T_stride = 1;
-    return launched(fn, kda::launch_scan(a, in_dtype == KDA_IN_BF16, o != nullptr, true,
+    a.n_chains = static_cast<long long>(chains); a.H = H; a.T = 1; a.T_stride = 1;
+    const kda::Launch kind = o ? kda::Launch::kBatchedOut : kda::Launch::kBatchedState;
+    return launched(fn, kda::launch_scan(a, kind, in_dtype == KDA_IN_BF16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int kda_verify_round(const float* snap_prev, float* snap_out, const void* pk, const void* pv,
+                     const void* pg, const void* pbeta, const float* pe, int T_prev, int keep,
+                     const void* q, const void* k, const void* v, const void* g, const void* beta,
+                     float* o, float* e, int L, int T, int H, int in_dtype, void* stream) {
+    const char* fn = "kda_verify_round";
+    int rc;
+    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H)) ||
+        (rc = check_rows(fn, "T", T)))
+        return rc;
+    if (T_prev < 0 || T_prev > KDA_T_MAX)
+        return refuse(KDA_ERR_RANGE, "%s: T_prev=%d outside 0..%d", fn, T_prev, KDA_T_MAX);
+    if (keep < 0 || keep > T_prev)
+        return refuse(KDA_ERR_RANGE, "%s: keep=%d outside 0..=%d (previous-round rows to replay)",
+                      fn, keep, T_prev);
+    const unsigned long long chains = static_cast<unsigned long long>(L) * H;
+    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
+    const unsigned long long prow = chains * T_prev;
+    const unsigned long long rows = chains * T;
+    const bool replay = keep > 0;
+    const bool stash = replay && pe != nullptr;
+    const Span in[] = {
+        {"snap_prev", snap_prev, chains * kStateBytes, 16, false},
+        {"pk", replay ? pk : nullptr, prow * kRowElems * es, 16, !replay},
+        {"pg", replay ? pg : nullptr, prow * kRowElems * es, 16, !replay},
+        {"pv", replay && !stash ? pv : nullptr, prow * kRowElems * es, 16, !replay || stash},
+        {"pbeta", replay && !stash ? pbeta : nullptr, prow * es, es, !replay || stash},
+        {"pe", stash ? pe : nullptr, prow * kRowElems * 4, 16, true},
+        {"q", q, rows * kRowElems * es, 16, false},
+        {"k", k, rows * kRowElems * es, 16, false},
+        {"v", v, rows * kRowElems * es, 16, false},
+        {"g", g, rows * kRowElems * es, 16, false},
+        {"beta", beta, rows * es, es, false},
+    };
+    const Span out[] = {
+        {"snap_out", snap_out, chains * kStateBytes, 16, false},
+        {"o", o, rows * kRowElems * 4, 16, false},
+        {"e", e, rows * kRowElems * 4, 16, true},
+    };
+    if ((rc = check_spans(fn, in, 11)) || (rc = check_spans(fn, out, 3)) ||
+        (rc = check_alias(fn, out, 3, in, 11, &out[0], &in[0])))
+        return rc;
+    kda::ScanArgs a{};
+    a.s_in = snap_prev; a.s_out = snap_out;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.e_out = e;
+    a.pk = pk; a.pv = pv; a.pg = pg; a.pbeta = pbeta; a.pe = stash ? pe : nullptr;
+    a.T_prev = T_prev; a.keep = keep;
+    a.n_chains = static_cast<long long>(chains); a.H = H; a.T = T; a.T_stride = T;
+    const kda::Launch kind = stash ? kda::Launch::kRoundStash : kda::Launch::kRound;
+    return launched(fn, kda::launch_scan(a, kind, in_dtype == KDA_IN_BF16,
                                          static_cast<hipStream_t>(stream)));
 }
 

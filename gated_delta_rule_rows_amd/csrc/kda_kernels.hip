@@ -31,6 +31,14 @@
 // point.  The state crosses HBM as exact f32 words, so a T-row launch equals
 // T chained one-row launches bit for bit.
 //
+// Rollback.  A scan can also write each row's delta vector e (the "stash"
+// plane beside the row inputs).  A replay that reads e skips both reductions:
+// per element it is the decay multiply and the rank-1 FMA, with the very e
+// bits the scan used, so it rebuilds the same state bits.  The fused verify
+// round replays the previous round's kept rows from its snapshot, stores that
+// committed state (this round's snapshot) and then scans the new rows for o,
+// so the state crosses HBM once per round.
+//
 // No MFMA: each row is two matrix-vector products and a rank-1 update with a
 // sequential dependency from row to row -- there is no dense contraction to
 // feed the matrix cores.
@@ -122,6 +130,34 @@ __device__ __forceinline__ float decay_of(float g) {
     return expf(fminf(fmaxf(g, kGateLo), kGateHi));
 }
 
+// Pointers known to address global memory: loads and stores through them are
+// global (not flat) instructions even when the pointer was read from memory.
+using gfloat = __attribute__((address_space(1))) float;
+typedef float vf2 __attribute__((ext_vector_type(2)));
+typedef float vf4 __attribute__((ext_vector_type(4)));
+using gvf2 = __attribute__((address_space(1))) vf2;
+using gvf4 = __attribute__((address_space(1))) vf4;
+
+template <int C>
+__device__ __forceinline__ void load_gcols(const gfloat* p, float (&x)[C]) {
+    if constexpr (C == 4) {
+        const vf4 v = *(const gvf4*)p;
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    } else {
+        const vf2 v = *(const gvf2*)p;
+        x[0] = v.x; x[1] = v.y;
+    }
+}
+
+template <int C>
+__device__ __forceinline__ void store_gcols(gfloat* p, const float (&x)[C]) {
+    if constexpr (C == 4) {
+        *(gvf4*)p = vf4{x[0], x[1], x[2], x[3]};
+    } else {
+        *(gvf2*)p = vf2{x[0], x[1]};
+    }
+}
+
 template <int C>
 __device__ __forceinline__ void load_cols(const float* p, float (&x)[C]) {
     if constexpr (C == 4) {
@@ -155,59 +191,46 @@ struct KeyRow {
     __device__ static constexpr int at(int i) { return (i / R) * (R + kPad) + i % R; }
 };
 
-template <int R, int C, bool BF16, bool WRITE_O, bool TABLE>
-__global__ void __launch_bounds__((Tile<R, C>::THREADS)) __attribute__((amdgpu_waves_per_eu(4)))
-kda_scan_kernel(ScanArgs a) {
+// What a phase of rows computes.
+enum class Rows {
+    kNone,
+    kFull,    // u and w reductions: state, o and (optionally) e -- the verify scan
+    kState,   // u reduction only: state and (optionally) e
+    kStash,   // e read from the stash: decay and rank-1 update only
+};
+
+// All T rows of one phase, staged in LDS.
+template <int R>
+struct Stage {
+    float4 d[kTMax * KeyRow<R>::kStride / 4];   // exp(clamp(g)), key layout
+    float4 k[kTMax * KeyRow<R>::kStride / 4];   // k, key layout
+    float4 q[kTMax * KeyRow<R>::kStride / 4];   // q / sqrt(128), key layout (kFull)
+    float4 ve[kTMax * kD / 4];                  // beta * v, or e for kStash; [t][j]
+    float b[kTMax];                             // beta
+    float qk[kTMax];                            // (q / sqrt(128)) . k
+};
+
+// One phase's row inputs, located for one chain.
+struct Src {
+    const void *q, *k, *v, *g, *beta;
+    const float* e;              // the stash plane (kStash)
+    size_t row0, rstride;        // element offset of row 0, elements between rows
+    size_t b0, bstride;          // beta
+    int T;
+};
+
+// Load one phase's rows, run `between` (the state loads, when this is the
+// first phase), then stage everything in LDS.  All loads are in flight before
+// the first wait.  Ends with the staged rows visible to every wave.
+template <int R, int C, bool BF16, Rows M, typename F>
+__device__ __forceinline__ void stage(Stage<R>& L, const Src& src, int tid, F&& between) {
     using TL = Tile<R, C>;
     using KR = KeyRow<R>;
-    __shared__ float4 sd4[kTMax * KR::kStride / 4];   // exp(clamp(g)), [t][key layout]
-    __shared__ float4 sk4[kTMax * KR::kStride / 4];   // k
-    __shared__ float4 sq4[kTMax * KR::kStride / 4];   // q / sqrt(128)
-    __shared__ float4 sbv4[kTMax * kD / 4];           // beta * v, [t][j]
-    __shared__ float sb[kTMax];                       // beta
-    __shared__ float sqk[kTMax];                      // (q / sqrt(128)) . k
-    float* sd = reinterpret_cast<float*>(sd4);
-    float* sk = reinterpret_cast<float*>(sk4);
-    float* sq = reinterpret_cast<float*>(sq4);
-    float* sbv = reinterpret_cast<float*>(sbv4);
-
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    const int ig = lane % TL::NI;
-    const int jg = lane / TL::NI;
-    const int i0 = ig * R;
-    const int j0 = wave * TL::WCOLS + jg * C;
-
-    // --- where this chain lives
-    const size_t chain = blockIdx.x;
-    const float* st_in;
-    float* st_out;
-    size_t row0, rstride, b0, bstride, o0, ostride;
-    int T;
-    if constexpr (TABLE) {
-        const size_t lb = chain / a.H, h = chain % a.H;
-        float* p = a.s_ptrs[lb] + h * kDD;
-        st_in = p;
-        st_out = p;
-        row0 = chain * kD; rstride = 0;
-        b0 = chain; bstride = 0;
-        o0 = chain * kD; ostride = 0;
-        T = 1;
-    } else {
-        const size_t l = chain / a.H, h = chain % a.H;
-        st_in = a.s_in + chain * kDD;
-        st_out = a.s_out + chain * kDD;
-        row0 = (l * a.T_stride * a.H + h) * kD; rstride = static_cast<size_t>(a.H) * kD;
-        b0 = l * a.T_stride * a.H + h;           bstride = a.H;
-        o0 = (l * a.T * a.H + h) * kD;            ostride = static_cast<size_t>(a.H) * kD;
-        T = a.T;
-    }
-
-    // --- loads: this chain's row inputs first (staged first), then its state
-    //     slab (read once per launch); the counters drain in issue order, so
-    //     staging can start while the state is still in flight
+    float* sd = reinterpret_cast<float*>(L.d);
+    float* sk = reinterpret_cast<float*>(L.k);
+    float* sq = reinterpret_cast<float*>(L.q);
     constexpr int kPer = (kTMax * (kD / 4) + TL::THREADS - 1) / TL::THREADS;
+    const int T = src.T;
     float4 in_k[kPer], in_v[kPer], in_g[kPer], in_q[kPer];
     float in_b[kPer];
 #pragma unroll
@@ -216,16 +239,18 @@ kda_scan_kernel(ScanArgs a) {
         // branch here would make the merge copies wait on the loads
         const int idx = tid + p * TL::THREADS;
         const int t = min(idx >> 5, T - 1);
-        const size_t off = row0 + t * rstride + (idx & 31) * 4;
-        in_k[p] = load4<BF16>(a.k, off);
-        in_v[p] = load4<BF16>(a.v, off);
-        in_g[p] = load4<BF16>(a.g, off);
-        if constexpr (WRITE_O) in_q[p] = load4<BF16>(a.q, off);
-        in_b[p] = load1<BF16>(a.beta, b0 + t * bstride);
+        const size_t off = src.row0 + t * src.rstride + (idx & 31) * 4;
+        in_k[p] = load4<BF16>(src.k, off);
+        in_g[p] = load4<BF16>(src.g, off);
+        if constexpr (M == Rows::kStash) {
+            in_v[p] = *reinterpret_cast<const float4*>(src.e + off);
+        } else {
+            in_v[p] = load4<BF16>(src.v, off);
+            in_b[p] = load1<BF16>(src.beta, src.b0 + t * src.bstride);
+        }
+        if constexpr (M == Rows::kFull) in_q[p] = load4<BF16>(src.q, off);
     }
-    float s[R][C];
-#pragma unroll
-    for (int r = 0; r < R; ++r) load_cols<C>(st_in + static_cast<size_t>(i0 + r) * kD + j0, s[r]);
+    between();
     // keep the staging arithmetic below from being hoisted between the loads
     // (it would wait on the first input load before the state loads are
     // issued): the staged values pass through an empty asm placed here
@@ -234,12 +259,9 @@ kda_scan_kernel(ScanArgs a) {
         opaque(in_k[p]);
         opaque(in_v[p]);
         opaque(in_g[p]);
-        if constexpr (WRITE_O) opaque(in_q[p]);
-        asm volatile("" : "+v"(in_b[p])::"memory");
+        if constexpr (M == Rows::kFull) opaque(in_q[p]);
+        if constexpr (M != Rows::kStash) asm volatile("" : "+v"(in_b[p])::"memory");
     }
-
-    // --- stage all T rows in LDS: exp(clamp(g)) once per (row, key), q
-    //     pre-scaled by 1/sqrt(128), beta * v
 #pragma unroll
     for (int p = 0; p < kPer; ++p) {
         const int idx = tid + p * TL::THREADS;
@@ -247,28 +269,33 @@ kda_scan_kernel(ScanArgs a) {
             const int t = idx >> 5;
             const int c4 = idx & 31;
             const int kp = t * KR::kStride + KR::at(c4 * 4);   // 4 keys never straddle a group
-            const float bt = in_b[p];
             const float4 gg = in_g[p];
-            const float4 gv = in_v[p];
             *reinterpret_cast<float4*>(sk + kp) = in_k[p];
             *reinterpret_cast<float4*>(sd + kp) =
                 make_float4(decay_of(gg.x), decay_of(gg.y), decay_of(gg.z), decay_of(gg.w));
-            sbv4[t * 32 + c4] = make_float4(bt * gv.x, bt * gv.y, bt * gv.z, bt * gv.w);
-            if constexpr (WRITE_O) {
+            if constexpr (M == Rows::kStash) {
+                L.ve[t * 32 + c4] = in_v[p];
+            } else {
+                const float bt = in_b[p];
+                const float4 gv = in_v[p];
+                L.ve[t * 32 + c4] = make_float4(bt * gv.x, bt * gv.y, bt * gv.z, bt * gv.w);
+                if (c4 == 0) L.b[t] = bt;
+            }
+            if constexpr (M == Rows::kFull) {
                 const float4 gq = in_q[p];
                 *reinterpret_cast<float4*>(sq + kp) = make_float4(
                     gq.x * kInvSqrtD, gq.y * kInvSqrtD, gq.z * kInvSqrtD, gq.w * kInvSqrtD);
             }
-            if (c4 == 0) sb[t] = bt;
         }
     }
     __syncthreads();
 
-    // --- (q/sqrt(128)).k per row: one 16-lane DPP row per verify row, 8 keys per
-    //     lane in ascending order, then a fixed butterfly
-    if constexpr (WRITE_O) {
-        const int l16 = lane & 15;
-        for (int t = wave * 4 + (lane >> 4); t < T; t += TL::WAVES * 4) {
+    // (q/sqrt(128)).k per row: one 16-lane DPP row per verify row, 8 keys per
+    // lane in ascending order, then a fixed butterfly
+    if constexpr (M == Rows::kFull) {
+        const int wave = tid >> 6;
+        const int l16 = tid & 15;
+        for (int t = wave * 4 + ((tid & 63) >> 4); t < T; t += TL::WAVES * 4) {
             float p = 0.0f;
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
@@ -276,72 +303,173 @@ kda_scan_kernel(ScanArgs a) {
                 p = fmaf(sq[kp], sk[kp], p);
             }
             p = group_sum<16>(p);
-            if (l16 == 0) sqk[t] = p;
+            if (l16 == 0) L.qk[t] = p;
         }
         __syncthreads();
     }
+}
 
-    // --- the sequential row loop over register state
+// The sequential row loop over register state.  o_row(t) / e_row(t) give the
+// (wave-uniform) start of row t's output vectors; e rows are written only
+// when `e_out` is set.
+template <int R, int C, Rows M>
+__device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], int T,
+                                         float* o, float* e_out, size_t o0, size_t ostride,
+                                         int ig, int i0, int j0) {
+    using TL = Tile<R, C>;
+    using KR = KeyRow<R>;
+    const float* sve = reinterpret_cast<const float*>(L.ve);
 #pragma unroll 1
     for (int t = 0; t < T; ++t) {
         const int kb = t * KR::kStride + KR::at(i0);
         float kk[R], dk[R], qq[R];
 #pragma unroll
         for (int r4 = 0; r4 < R / 4; ++r4) {
-            const float4 x = sk4[kb / 4 + r4];
-            const float4 y = sd4[kb / 4 + r4];
+            const float4 x = L.k[kb / 4 + r4];
+            const float4 y = L.d[kb / 4 + r4];
             kk[4 * r4 + 0] = x.x; kk[4 * r4 + 1] = x.y; kk[4 * r4 + 2] = x.z; kk[4 * r4 + 3] = x.w;
             dk[4 * r4 + 0] = y.x; dk[4 * r4 + 1] = y.y; dk[4 * r4 + 2] = y.z; dk[4 * r4 + 3] = y.w;
-            if constexpr (WRITE_O) {
-                const float4 z = sq4[kb / 4 + r4];
+            if constexpr (M == Rows::kFull) {
+                const float4 z = L.q[kb / 4 + r4];
                 qq[4 * r4 + 0] = z.x; qq[4 * r4 + 1] = z.y; qq[4 * r4 + 2] = z.z; qq[4 * r4 + 3] = z.w;
             }
         }
-        const float nbt = -sb[t];
-        float bv[C];
-        load_cols<C>(sbv + t * kD + j0, bv);
+        float ve[C];   // beta * v, or e itself for kStash
+        load_cols<C>(sve + t * kD + j0, ve);
 
-        // decay, then the two in-lane partial reductions over this lane's keys
-        float u[C], w[C];
+        float e[C];
+        if constexpr (M == Rows::kStash) {
 #pragma unroll
-        for (int c = 0; c < C; ++c) { u[c] = 0.0f; w[c] = 0.0f; }
+            for (int r = 0; r < R; ++r) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
+                for (int c = 0; c < C; ++c) s[r][c] = s[r][c] * dk[r];
+            }
+#pragma unroll
+            for (int c = 0; c < C; ++c) e[c] = ve[c];
+        } else {
+            const float nbt = -L.b[t];
+            // decay, then the in-lane partial reductions over this lane's keys
+            float u[C], w[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) { u[c] = 0.0f; w[c] = 0.0f; }
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                    s[r][c] = s[r][c] * dk[r];
+                    u[c] = fmaf(kk[r], s[r][c], u[c]);
+                    if constexpr (M == Rows::kFull) w[c] = fmaf(qq[r], s[r][c], w[c]);
+                }
+            }
 #pragma unroll
             for (int c = 0; c < C; ++c) {
-                s[r][c] = s[r][c] * dk[r];
-                u[c] = fmaf(kk[r], s[r][c], u[c]);
-                if constexpr (WRITE_O) w[c] = fmaf(qq[r], s[r][c], w[c]);
+                u[c] = group_sum<TL::NI>(u[c]);
+                if constexpr (M == Rows::kFull) w[c] = group_sum<TL::NI>(w[c]);
             }
-        }
+            // e = beta v - beta u
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            u[c] = group_sum<TL::NI>(u[c]);
-            if constexpr (WRITE_O) w[c] = group_sum<TL::NI>(w[c]);
-        }
-
-        // delta-rule write: e = beta v - beta u, S = S' + k e^T
-        float e[C];
+            for (int c = 0; c < C; ++c) e[c] = fmaf(nbt, u[c], ve[c]);
+            if constexpr (M == Rows::kFull) {
+                const float qk = L.qk[t];
+                float ov[C];
 #pragma unroll
-        for (int c = 0; c < C; ++c) e[c] = fmaf(nbt, u[c], bv[c]);
+                for (int c = 0; c < C; ++c) ov[c] = fmaf(e[c], qk, w[c]);
+                if (ig == 0) store_cols<C>(o + (o0 + t * ostride) + j0, ov);
+            }
+            if (e_out != nullptr && ig == 0) store_cols<C>(e_out + (o0 + t * ostride) + j0, e);
+        }
+        // delta-rule write: S = S' + k e^T
 #pragma unroll
         for (int r = 0; r < R; ++r) {
 #pragma unroll
             for (int c = 0; c < C; ++c) s[r][c] = fmaf(kk[r], e[c], s[r][c]);
         }
+    }
+}
 
-        if constexpr (WRITE_O) {
-            const float qk = sqk[t];
-            float ov[C];
-#pragma unroll
-            for (int c = 0; c < C; ++c) ov[c] = fmaf(e[c], qk, w[c]);
-            if (ig == 0) store_cols<C>(a.o + o0 + t * ostride + j0, ov);
-        }
+// One launch: optionally a replay phase A (FUSED: rows 0..keep-1 of the
+// previous round from the snapshot, then that committed state is stored),
+// then phase B (this launch's rows).  Without FUSED the state after phase B
+// is stored.
+template <int R, int C, bool BF16, Rows MA, Rows MB, bool TABLE>
+__global__ void __launch_bounds__((Tile<R, C>::THREADS)) __attribute__((amdgpu_waves_per_eu(4)))
+kda_scan_kernel(ScanArgs a) {
+    using TL = Tile<R, C>;
+    constexpr bool FUSED = MA != Rows::kNone;
+    __shared__ Stage<R> L;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int ig = lane % TL::NI;
+    const int jg = lane / TL::NI;
+    const int i0 = ig * R;
+    const int j0 = wave * TL::WCOLS + jg * C;
+    // this lane's element offset inside a head's state; the per-head base
+    // pointers are wave-uniform, so addresses are SGPR base + 32-bit offset
+    const uint32_t lane_off = static_cast<uint32_t>(i0 * kD + j0);
+
+    // --- where this chain lives
+    const size_t chain = blockIdx.x;
+    const gfloat* st_in;
+    gfloat* st_out;
+    Src b;   // this launch's rows
+    size_t o0, ostride;
+    b.q = a.q; b.k = a.k; b.v = a.v; b.g = a.g; b.beta = a.beta; b.e = a.e_in;
+    if constexpr (TABLE) {
+        const size_t lb = chain / a.H, h = chain % a.H;
+        // the table entry is wave-uniform: keep it in scalar registers
+        const uint64_t raw = reinterpret_cast<const uint64_t*>(a.s_ptrs)[lb];
+        const uint64_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(raw)));
+        const uint64_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(raw >> 32)));
+        gfloat* p = reinterpret_cast<gfloat*>(lo | (hi << 32)) + h * kDD;
+        st_in = p;
+        st_out = p;
+        b.row0 = chain * kD; b.rstride = 0;
+        b.b0 = chain; b.bstride = 0;
+        b.T = 1;
+        o0 = chain * kD; ostride = 0;
+    } else {
+        const size_t l = chain / a.H, h = chain % a.H;
+        st_in = (const gfloat*)a.s_in + chain * kDD;
+        st_out = (gfloat*)a.s_out + chain * kDD;
+        b.row0 = (l * a.T_stride * a.H + h) * kD; b.rstride = static_cast<size_t>(a.H) * kD;
+        b.b0 = l * a.T_stride * a.H + h;           b.bstride = a.H;
+        b.T = a.T;
+        o0 = (l * a.T * a.H + h) * kD;              ostride = static_cast<size_t>(a.H) * kD;
     }
 
-    // --- state slab back to HBM (written once per launch)
+    float s[R][C];
+    auto load_state = [&] {
 #pragma unroll
-    for (int r = 0; r < R; ++r) store_cols<C>(st_out + static_cast<size_t>(i0 + r) * kD + j0, s[r]);
+        for (int r = 0; r < R; ++r) load_gcols<C>(st_in + (lane_off + r * kD), s[r]);
+    };
+    auto store_state = [&] {
+#pragma unroll
+        for (int r = 0; r < R; ++r) store_gcols<C>(st_out + (lane_off + r * kD), s[r]);
+    };
+
+    if constexpr (FUSED) {
+        if (a.keep > 0) {
+            const size_t l = chain / a.H, h = chain % a.H;
+            Src p;
+            p.q = nullptr; p.k = a.pk; p.v = a.pv; p.g = a.pg; p.beta = a.pbeta; p.e = a.pe;
+            p.row0 = (l * a.T_prev * a.H + h) * kD; p.rstride = static_cast<size_t>(a.H) * kD;
+            p.b0 = l * a.T_prev * a.H + h;           p.bstride = a.H;
+            p.T = a.keep;
+            stage<R, C, BF16, MA>(L, p, tid, load_state);
+            run_rows<R, C, MA>(L, s, a.keep, nullptr, nullptr, 0, 0, ig, i0, j0);
+            __syncthreads();   // every wave is done with phase A's staged rows
+        } else {
+            load_state();
+        }
+        store_state();         // the committed state: this round's snapshot
+        stage<R, C, BF16, MB>(L, b, tid, [] {});
+    } else {
+        stage<R, C, BF16, MB>(L, b, tid, load_state);
+    }
+    run_rows<R, C, MB>(L, s, b.T, a.o, TABLE ? nullptr : a.e_out, o0, ostride, ig, i0, j0);
+    if constexpr (!FUSED) store_state();
 }
 
 // ------------------------------------------------------------------ copy
@@ -364,27 +492,33 @@ __global__ void __launch_bounds__(256) kda_copy_kernel(const float4* __restrict_
     for (; i < n4; i += stride) dst[i] = src[i];
 }
 
-template <bool BF16, bool WRITE_O, bool TABLE>
+template <bool BF16, Rows MA, Rows MB, bool TABLE>
 hipError_t launch_one(const ScanArgs& a, hipStream_t stream) {
     using TL = TileT;
-    kda_scan_kernel<16, 4, BF16, WRITE_O, TABLE>
+    kda_scan_kernel<16, 4, BF16, MA, MB, TABLE>
         <<<dim3(static_cast<unsigned>(a.n_chains)), dim3(TL::THREADS), 0, stream>>>(a);
     return hipGetLastError();
 }
 
+template <bool BF16>
+hipError_t launch_dtype(const ScanArgs& a, Launch kind, hipStream_t stream) {
+    switch (kind) {
+        case Launch::kScanOut:      return launch_one<BF16, Rows::kNone, Rows::kFull, false>(a, stream);
+        case Launch::kScanState:    return launch_one<BF16, Rows::kNone, Rows::kState, false>(a, stream);
+        case Launch::kReplay:       return launch_one<BF16, Rows::kNone, Rows::kState, false>(a, stream);
+        case Launch::kReplayStash:  return launch_one<BF16, Rows::kNone, Rows::kStash, false>(a, stream);
+        case Launch::kBatchedOut:   return launch_one<BF16, Rows::kNone, Rows::kFull, true>(a, stream);
+        case Launch::kBatchedState: return launch_one<BF16, Rows::kNone, Rows::kState, true>(a, stream);
+        case Launch::kRound:        return launch_one<BF16, Rows::kState, Rows::kFull, false>(a, stream);
+        case Launch::kRoundStash:   return launch_one<BF16, Rows::kStash, Rows::kFull, false>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
-hipError_t launch_scan(const ScanArgs& a, bool bf16, bool write_o, bool table, hipStream_t stream) {
-    if (table) {
-        if (bf16) return write_o ? launch_one<true, true, true>(a, stream)
-                                 : launch_one<true, false, true>(a, stream);
-        return write_o ? launch_one<false, true, true>(a, stream)
-                       : launch_one<false, false, true>(a, stream);
-    }
-    if (bf16) return write_o ? launch_one<true, true, false>(a, stream)
-                             : launch_one<true, false, false>(a, stream);
-    return write_o ? launch_one<false, true, false>(a, stream)
-                   : launch_one<false, false, false>(a, stream);
+hipError_t launch_scan(const ScanArgs& a, Launch kind, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_dtype<true>(a, kind, stream) : launch_dtype<false>(a, kind, stream);
 }
 
 hipError_t launch_copy(const float* src, float* dst, size_t n_floats, hipStream_t stream) {

@@ -12,27 +12,49 @@ constexpr int kD = 128;        // head dim: d_k = d_v
 constexpr int kTMax = 15;      // verify rows per launch
 constexpr int kBMax = 15;      // batched-decode sessions
 
-// One launch of the row scan.  Either the contiguous layout
+// One launch of the row kernel.  Either the contiguous layout
 //   state [chain][128][128], chain = l*H + h, rows [L][T_stride][H][128]
-// or (table) the batched layout
+// or (batched) the table layout
 //   state s_ptrs[l*B + b] + h*128*128, chain = (l*B + b)*H + h, rows [L][B][H][128].
 struct ScanArgs {
     const float* s_in;
     float* s_out;
     float* const* s_ptrs;
+    // this launch's rows
     const void* q;
     const void* k;
     const void* v;
     const void* g;
     const void* beta;
-    float* o;        // written only when write_o
+    const float* e_in;   // stash plane read by a stash replay
+    float* o;            // per-row outputs (full rows)
+    float* e_out;        // stash plane written by a scan, or nullptr
+    // the previous round's rows (fused verify round only)
+    const void* pk;
+    const void* pv;
+    const void* pg;
+    const void* pbeta;
+    const float* pe;
+    int T_prev;          // rows per layer in the previous round's layout
+    int keep;            // previous-round rows to replay (0 = none)
     long long n_chains;  // (layer, head) or (layer, session, head) chains
     int H;
-    int T;           // rows scanned by this launch
-    int T_stride;    // rows per layer in the input layout (contiguous mode)
+    int T;               // rows this launch runs
+    int T_stride;        // rows per layer in this launch's input layout
 };
 
-hipError_t launch_scan(const ScanArgs& a, bool bf16, bool write_o, bool table, hipStream_t stream);
+enum class Launch {
+    kScanOut,       // T rows, outputs o (and e), state stored
+    kScanState,     // T rows, state (and e) only
+    kReplay,        // keep rows recomputed from the row inputs, state stored
+    kReplayStash,   // keep rows from the stash plane e, state stored
+    kBatchedOut,    // batched arm, one row per session, o
+    kBatchedState,  // batched arm, state only
+    kRound,         // fused verify round: replay (recomputed), store, scan for o
+    kRoundStash,    // fused verify round: replay from the stash, store, scan for o
+};
+
+hipError_t launch_scan(const ScanArgs& a, Launch kind, bool bf16, hipStream_t stream);
 
 hipError_t launch_copy(const float* src, float* dst, size_t n_floats, hipStream_t stream);
 

@@ -50,7 +50,7 @@ extern "C" {
 #define KDA_HEAD_DIM 128   /* d_k = d_v; glm5_spec_ppn_gate.rs fixture head_dim */
 #define KDA_T_MAX 15       /* verify rows per round: K + 1 <= 15 (glm_spec.rs, WALK-REUSE) */
 #define KDA_B_MAX 15       /* batched-decode sessions per step (same knee) */
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 enum { KDA_IN_F32 = 0, KDA_IN_BF16 = 1 };
 
@@ -74,14 +74,18 @@ enum {
  *   q, k, v, g  : [L][T][H][128] in in_dtype.
  *   beta        : [L][T][H] in in_dtype.
  *   o           : [L][T][H][128] f32, or NULL to skip the outputs.
+ *   e           : [L][T][H][128] f32, or NULL.  If given, row t's delta
+ *                 vector e_t = beta_t (v_t - S'^T k_t) is written: the stash
+ *                 plane that lets kda_replay / kda_verify_round rebuild the
+ *                 state without the two reductions, bit for bit.
  *   L, H >= 1;  1 <= T <= KDA_T_MAX.
- * The caller keeps q, k, v, g, beta alive until it has either replayed or
- * accepted every row: they are the round's stash (glm_spec.rs, ROLLBACK:
- * the row inputs are retained with zero copies).
+ * The caller keeps k, g (and v, beta, or e) alive until it has either
+ * replayed or accepted every row: they are the round's stash (glm_spec.rs,
+ * ROLLBACK: the row inputs are retained with zero copies).
  */
 int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k,
-                  const void* v, const void* g, const void* beta, float* o, int L, int T, int H,
-                  int in_dtype, void* stream);
+                  const void* v, const void* g, const void* beta, float* o, float* e, int L,
+                  int T, int H, int in_dtype, void* stream);
 
 /*
  * snap = s, a device copy of L x H states [L][H][128][128] f32.
@@ -98,17 +102,21 @@ int kda_snapshot(const float* s, float* snap, int L, int H, void* stream);
  * drafts), 1 <= keep <= T_round <= KDA_T_MAX.
  *   glm_spec.rs (0.123.0), fn glm5_verify_rollback / glm5_rollback_layer and
  *   the Glm5VerifyCkpt doc: keep outside 1..=rows is an error; the replay is
- *   the same scan over the same inputs, so the rebuilt state is identical to
- *   the one the scan held after row keep-1.  In serving keep == T_round needs
- *   no replay (the resident state already is it); the call stays legal and
- *   then returns the scan's final state bits.
+ *   the same row program over the same inputs, so the rebuilt state is
+ *   identical to the one the scan held after row keep-1.  In serving keep ==
+ *   T_round needs no replay (the resident state already is it); the call stays
+ *   legal and then returns the scan's final state bits.
  *   snap, s_out : [L][H][128][128] f32; they must not overlap.
- *   q..beta     : the very buffers passed to the round's kda_scan_rows, with
- *                 that call's row count T_round (rows keep..T_round-1 unread).
+ *   k, v, g     : the round's row buffers [L][T_round][H][128] (in_dtype),
+ *   beta        : [L][T_round][H], as passed to the round's kda_scan_rows;
+ *                 rows keep..T_round-1 are not read.
+ *   e           : the stash plane that scan wrote ([L][T_round][H][128] f32),
+ *                 or NULL.  With e, v and beta are not read (may be NULL) and
+ *                 each row is only the decay and the rank-1 update.
  *   No outputs are written.
  */
-int kda_replay(const float* snap, float* s_out, const void* q, const void* k, const void* v,
-               const void* g, const void* beta, int L, int T_round, int keep, int H,
+int kda_replay(const float* snap, float* s_out, const void* k, const void* v, const void* g,
+               const void* beta, const float* e, int L, int T_round, int keep, int H,
                int in_dtype, void* stream);
 
 /*
@@ -129,6 +137,39 @@ int kda_replay(const float* snap, float* s_out, const void* q, const void* k, co
 int kda_scan_batched(float* const* s_ptrs, const void* q, const void* k, const void* v,
                      const void* g, const void* beta, float* o, int L, int B, int H,
                      int in_dtype, void* stream);
+
+/*
+ * One fused verify round: roll the previous round back to its kept rows, store
+ * that committed state (this round's snapshot), then scan this round's rows
+ * for their outputs.  The state crosses HBM once per round.
+ *   glm_spec.rs (0.123.0), ROLLBACK: accept-j replays rows 0..j of the
+ *   previous round from its snapshot; VERIFY-ROW BATCHING: this round's rows
+ *   are scanned sequentially.  Here the replay of round r-1 and the scan of
+ *   round r share one launch and one pass over the state.
+ *   snap_prev   : [L][H][128][128] f32, the previous round's snapshot (its
+ *                 committed state before its rows).
+ *   snap_out    : [L][H][128][128] f32, receives snap_prev advanced by rows
+ *                 0..keep-1 of the previous round -- the committed state and
+ *                 this round's snapshot.  == snap_prev updates in place.
+ *                 The state after this round's rows is NOT stored: the next
+ *                 round (or kda_replay) rebuilds what the accept keeps.
+ *   pk, pv, pg, pbeta, pe : the previous round's retained rows and stash, as
+ *                 for kda_replay, in a [L][T_prev][H] layout.  With pe, pv and
+ *                 pbeta are not read.  All may be NULL when keep == 0.
+ *   T_prev      : the previous round's row count, 0..KDA_T_MAX.
+ *   keep        : previous-round rows to keep, 0..T_prev (0: snap_prev is
+ *                 already committed; then snap_out is a copy of it).
+ *   q..beta, o  : this round's rows and outputs, as for kda_scan_rows; o is
+ *                 required.  e (optional) receives this round's stash plane.
+ *   1 <= T <= KDA_T_MAX.
+ * Bit for bit, snap_out equals kda_replay(snap_prev, ..., keep) and o equals
+ * kda_scan_rows(snap_out, ...)'s outputs.
+ */
+int kda_verify_round(const float* snap_prev, float* snap_out, const void* pk, const void* pv,
+                     const void* pg, const void* pbeta, const float* pe, int T_prev, int keep,
+                     const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, float* o, float* e, int L, int T, int H, int in_dtype,
+                     void* stream);
 
 /* Message for the last nonzero status returned on the calling thread. */
 const char* kda_last_error(void);

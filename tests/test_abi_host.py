@@ -41,7 +41,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"kda_scan_rows", "kda_snapshot", "kda_replay", "kda_scan_batched",
-                          "kda_last_error", "kda_abi_version"}
+                          "kda_verify_round", "kda_last_error", "kda_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -86,18 +86,29 @@ def b():
 
 def _scan(lib, b, **kw):
     a = dict(s_in=b["s_in"], s_out=b["s_out"], q=b["q"], k=b["k"], v=b["v"], g=b["g"],
-             beta=b["beta"], o=b["o"], L=2, T=8, H=2, dt=0)
+             beta=b["beta"], o=b["o"], e=None, L=2, T=8, H=2, dt=0)
     a.update(kw)
     return lib.kda_scan_rows(a["s_in"], a["s_out"], a["q"], a["k"], a["v"], a["g"], a["beta"],
-                             a["o"], a["L"], a["T"], a["H"], a["dt"], None)
+                             a["o"], a["e"], a["L"], a["T"], a["H"], a["dt"], None)
 
 
 def _replay(lib, b, **kw):
-    a = dict(snap=b["snap"], s_out=b["s_out"], q=b["q"], k=b["k"], v=b["v"], g=b["g"],
-             beta=b["beta"], L=2, T=8, keep=3, H=2, dt=0)
+    a = dict(snap=b["snap"], s_out=b["s_out"], k=b["k"], v=b["v"], g=b["g"], beta=b["beta"],
+             e=None, L=2, T=8, keep=3, H=2, dt=0)
     a.update(kw)
-    return lib.kda_replay(a["snap"], a["s_out"], a["q"], a["k"], a["v"], a["g"], a["beta"],
+    return lib.kda_replay(a["snap"], a["s_out"], a["k"], a["v"], a["g"], a["beta"], a["e"],
                           a["L"], a["T"], a["keep"], a["H"], a["dt"], None)
+
+
+def _round(lib, b, **kw):
+    a = dict(snap_prev=b["snap"], snap_out=b["s_out"], pk=b["k"], pv=b["v"], pg=b["g"],
+             pbeta=b["beta"], pe=None, T_prev=8, keep=3, q=b["q"], k=b["k"], v=b["v"],
+             g=b["g"], beta=b["beta"], o=b["o"], e=None, L=2, T=8, H=2, dt=0)
+    a.update(kw)
+    return lib.kda_verify_round(a["snap_prev"], a["snap_out"], a["pk"], a["pv"], a["pg"],
+                                a["pbeta"], a["pe"], a["T_prev"], a["keep"], a["q"], a["k"],
+                                a["v"], a["g"], a["beta"], a["o"], a["e"], a["L"], a["T"],
+                                a["H"], a["dt"], None)
 
 
 def _batched(lib, b, **kw):
@@ -143,6 +154,8 @@ def test_scan_rows_alignment_and_alias(lib, b):
     assert _scan(lib, b, s_out=b["v"]) == ERR_ALIAS and "s_out overlaps v" in _msg(lib)
     assert _scan(lib, b, o=b["s_in"]) == ERR_ALIAS and "o overlaps s_in" in _msg(lib)
     assert _scan(lib, b, o=off("q", 1024)) == ERR_ALIAS
+    assert _scan(lib, b, e=b["o"]) == ERR_ALIAS and "o overlaps e" in _msg(lib)
+    assert _scan(lib, b, e=off("ptrs", 8)) == ERR_ALIGN
 
 
 @pytest.mark.parametrize("kw,code,needle", [
@@ -161,6 +174,44 @@ def test_replay_refusals(lib, b, kw, code, needle):
 def test_replay_alias(lib, b):
     assert _replay(lib, b, s_out=b["snap"]) == ERR_ALIAS and "s_out overlaps snap" in _msg(lib)
     assert _replay(lib, b, s_out=b["g"]) == ERR_ALIAS
+    assert _replay(lib, b, e=b["ptrs"], s_out=b["ptrs"]) == ERR_ALIAS and "overlaps e" in _msg(lib)
+
+
+def test_replay_stash_makes_v_and_beta_optional(lib, b):
+    # without the stash plane, v and beta are required
+    assert _replay(lib, b, v=None) == ERR_ARG and "v is NULL" in _msg(lib)
+    assert _replay(lib, b, beta=None) == ERR_ARG and "beta is NULL" in _msg(lib)
+    # with it they are optional; the refusal then comes from the (bad) keep only
+    assert _replay(lib, b, v=None, beta=None, e=b["ptrs"], keep=0) == ERR_RANGE
+    assert _replay(lib, b, e=ctypes.c_void_p(b.addr["ptrs"] + 4), keep=1) == ERR_ALIGN
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(T=0), ERR_RANGE, "T=0"),
+    (dict(T=16), ERR_RANGE, "T=16"),
+    (dict(T_prev=-1), ERR_RANGE, "T_prev=-1"),
+    (dict(T_prev=16), ERR_RANGE, "T_prev=16"),
+    (dict(keep=-1), ERR_RANGE, "keep=-1"),
+    (dict(keep=9), ERR_RANGE, "keep=9"),
+    (dict(o=None), ERR_ARG, "o is NULL"),
+    (dict(pk=None), ERR_ARG, "pk is NULL"),
+    (dict(pv=None), ERR_ARG, "pv is NULL"),
+    (dict(snap_prev=None), ERR_ARG, "snap_prev is NULL"),
+    (dict(dt=3), ERR_ARG, "in_dtype"),
+])
+def test_verify_round_refusals(lib, b, kw, code, needle):
+    assert _round(lib, b, **kw) == code
+    assert needle in _msg(lib)
+
+
+def test_verify_round_alias(lib, b):
+    off = lambda n, k: ctypes.c_void_p(b.addr[n] + k)
+    assert _round(lib, b, snap_out=off("snap", 64)) == ERR_ALIAS and "partially" in _msg(lib)
+    assert _round(lib, b, o=b["k"]) == ERR_ALIAS and "o overlaps" in _msg(lib)
+    assert _round(lib, b, e=b["o"]) == ERR_ALIAS and "o overlaps e" in _msg(lib)
+    assert _round(lib, b, snap_out=b["g"]) == ERR_ALIAS
+    # keep == 0 needs no previous rows: with those NULL the refusal is the o alias
+    assert _round(lib, b, keep=0, pk=None, pv=None, pg=None, pbeta=None, o=b["q"]) == ERR_ALIAS
 
 
 @pytest.mark.parametrize("kw,code,needle", [

@@ -90,7 +90,7 @@ def test_tiny_workload_rounds_with_replay():
         assert maxerr(host(s_full), S_ref) <= TOL
         keep = int(js[r]) + 1
         s_rep = torch.empty_like(s_gpu)
-        kda.kda_replay(s_gpu, s_rep, *rd, keep=keep)     # s_gpu is the snapshot
+        kda.kda_replay(s_gpu, s_rep, *rd[1:], keep=keep)     # s_gpu is the snapshot
         S_rep = oracle.replay(s_ref, *rows_np(rw), keep=keep)
         assert maxerr(host(s_rep), S_rep) <= TOL
         s_gpu, s_ref = s_rep, S_rep
@@ -112,7 +112,7 @@ def test_one_layer_workload_replay_sweep():
     for j in range(w.T):
         keep = j + 1
         s_rep = torch.empty_like(s_in)
-        kda.kda_replay(s_in, s_rep, *rd, keep=keep)
+        kda.kda_replay(s_in, s_rep, *rd[1:], keep=keep)
         S_rep = oracle.replay(s0, *rows_np(rw), keep=keep, threads=oracle.max_threads())
         assert maxerr(host(s_rep), S_rep) <= TOL, f"keep={keep}"
     assert bits_equal(s_in, dev(s0))   # the scan was out of place: the snapshot is intact
@@ -145,7 +145,7 @@ def test_verify_k14_full_size_sampled_chains():
         keep = int(js[r]) + 1
         if keep < w.T:
             s_rep = torch.empty_like(s_gpu)
-            kda.kda_replay(s_gpu, s_rep, *rd, keep=keep)
+            kda.kda_replay(s_gpu, s_rep, *rd[1:], keep=keep)
             S_ref = oracle.replay(s_ref, *sub, keep=keep, threads=oracle.max_threads())
             assert maxerr(host(s_rep)[:, SAMPLE_HEADS], S_ref) <= TOL
             s_gpu = s_rep
@@ -190,7 +190,7 @@ def test_serving_mix_bf16_sampled_chains(K):
             s_gpu, s_ref = s_full, S_ref
         else:
             s_rep = torch.empty_like(s_gpu)
-            kda.kda_replay(s_gpu, s_rep, *rd, keep=j + 1)
+            kda.kda_replay(s_gpu, s_rep, *rd[1:], keep=j + 1)
             s_ref = oracle.replay(s_ref, *sub, keep=j + 1, threads=oracle.max_threads())
             s_gpu = s_rep
         assert maxerr(host(s_gpu)[:, heads], s_ref) <= TOL
@@ -256,12 +256,12 @@ def test_replay_equals_state_after_keep_rows(bf16):
     for keep in range(1, T + 1):
         chained, _ = scan(chained, slice_rows(rd, keep - 1, keep))
         s_rep = torch.empty_like(snap)
-        kda.kda_replay(snap, s_rep, *rd, keep=keep)
+        kda.kda_replay(snap, s_rep, *rd[1:], keep=keep)
         assert bits_equal(s_rep, chained), f"keep={keep}"
         s_k, _ = scan(snap, slice_rows(rd, 0, keep), want_o=False)
         assert bits_equal(s_rep, s_k)
     s_rep = torch.empty_like(snap)
-    kda.kda_replay(snap, s_rep, *rd, keep=T)
+    kda.kda_replay(snap, s_rep, *rd[1:], keep=T)
     assert bits_equal(s_rep, s_full)     # keep == T returns the resident bits
 
 
@@ -339,12 +339,12 @@ def test_red_arms_diverge():
     s_full, _ = scan(snap, rd)
     keep = 3
     good = torch.empty_like(snap)
-    kda.kda_replay(snap, good, *rd, keep=keep)
+    kda.kda_replay(snap, good, *rd[1:], keep=keep)
     # red 1: no replay -- the resident post-row-K state stands in for the rollback
     n1 = int((host(s_full).view(np.uint32) != host(good).view(np.uint32)).sum())
     # red 2: replay from the wrong snapshot (the post-scan state)
     bad = torch.empty_like(snap)
-    kda.kda_replay(s_full, bad, *rd, keep=keep)
+    kda.kda_replay(s_full, bad, *rd[1:], keep=keep)
     n2 = int((host(bad).view(np.uint32) != host(good).view(np.uint32)).sum())
     assert n1 > 0 and n2 > 0, (n1, n2)
     # non-vacuity: the scan really moved the state away from the snapshot
@@ -354,3 +354,110 @@ def test_red_arms_diverge():
     c_good, _ = scan(good, nxt)
     c_bad, _ = scan(s_full, nxt)
     assert not bits_equal(c_good, c_bad)
+
+
+# ----------------------------------------------------------------- stash plane and fused round
+
+def scan_e(s_in, rows):
+    L, T, H = rows[0].shape[:3]
+    s_out = torch.empty_like(s_in)
+    o = torch.empty(L, T, H, D, device="cuda")
+    e = torch.empty(L, T, H, D, device="cuda")
+    kda.kda_scan_rows(s_in, s_out, *rows, o=o, e=e)
+    return s_out, o, e
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_stash_replay_equals_recomputed_replay(bf16):
+    L, T, H = 2, 15, 5
+    rd = rows_dev(rand_rows(31, L, T, H, bf16))
+    snap = dev(rand_state(32, L, H))
+    s_full, o, e = scan_e(snap, rd)
+    s2, o2 = scan(snap, rd)            # writing the stash plane changes nothing else
+    assert bits_equal(s_full, s2) and bits_equal(o, o2)
+    for keep in range(1, T + 1):
+        a = torch.empty_like(snap)
+        kda.kda_replay(snap, a, *rd[1:], keep=keep)
+        b = torch.empty_like(snap)
+        kda.kda_replay(snap, b, rd[1], None, rd[3], None, keep=keep, e=e)
+        assert bits_equal(a, b), f"keep={keep}"
+    assert bits_equal(b, s_full)       # keep == T: the resident bits
+
+
+def _prev(rows, e, stash):
+    k, v, g, beta = rows[1:]
+    return (k, None, g, None, e) if stash else (k, v, g, beta, None)
+
+
+@pytest.mark.parametrize("bf16,stash", [(False, False), (False, True), (True, True)])
+def test_verify_round_equals_replay_then_scan(bf16, stash):
+    L, H, T_prev, T = 2, 5, 15, 8
+    prev = rows_dev(rand_rows(33, L, T_prev, H, bf16))
+    cur = rows_dev(rand_rows(34, L, T, H, bf16))
+    snap_prev = dev(rand_state(35, L, H))
+    _, _, e_prev = scan_e(snap_prev, prev)
+    for keep in (0, 1, 7, T_prev):
+        if keep:
+            ref_snap = torch.empty_like(snap_prev)
+            kda.kda_replay(snap_prev, ref_snap, *prev[1:], keep=keep)
+        else:
+            ref_snap = snap_prev
+        _, ref_o, ref_e = scan_e(ref_snap, cur)
+        snap_out = torch.empty_like(snap_prev)
+        o = torch.empty(L, T, H, D, device="cuda")
+        e = torch.empty(L, T, H, D, device="cuda")
+        kda.kda_verify_round(snap_prev, snap_out, _prev(prev, e_prev, stash) if keep else None,
+                             keep, *cur, o, e=e)
+        assert bits_equal(snap_out, ref_snap), f"keep={keep}"
+        assert bits_equal(o, ref_o) and bits_equal(e, ref_e), f"keep={keep}"
+    # in place
+    x = snap_prev.clone()
+    o = torch.empty(L, T, H, D, device="cuda")
+    kda.kda_verify_round(x, x, _prev(prev, e_prev, stash), 7, *cur, o)
+    ref_snap = torch.empty_like(snap_prev)
+    kda.kda_replay(snap_prev, ref_snap, *prev[1:], keep=7)
+    assert bits_equal(x, ref_snap)
+
+
+def _fused_pipeline(w, rounds, heads, bf16=False, stash=True, Ts=None):
+    """Run `rounds` fused verify rounds of workload w on the GPU and the matching
+    scan/replay chain on the oracle (sampled heads); compare every round."""
+    js = synth.accepts(w.seed, max(rounds, 1), w.T - 1)
+    snap = torch.zeros(w.L, w.H, D, D, device="cuda")
+    ref = np.zeros((w.L, len(heads), D, D), np.float32)
+    prev = None
+    for r in range(rounds):
+        T = Ts[r] if Ts else w.T
+        rw = synth.rows_bf16(w.seed, r, w.L, T, w.H) if bf16 else synth.rows(w.seed, r, w.L, T, w.H)
+        cur = rows_dev(rw)
+        o = torch.empty(w.L, T, w.H, D, device="cuda")
+        e = torch.empty(w.L, T, w.H, D, device="cuda")
+        nxt = torch.empty_like(snap)
+        if prev is None:
+            kda.kda_verify_round(snap, nxt, None, 0, *cur, o, e=e)
+        else:
+            p_rows, p_e, keep = prev
+            kda.kda_verify_round(snap, nxt, _prev(p_rows, p_e, stash), keep, *cur, o, e=e)
+        snap = nxt
+        sub = [x[:, :, heads] for x in rows_np(rw)]
+        _, o_ref = oracle.scan_rows(ref, *sub, threads=oracle.max_threads())
+        assert maxerr(host(snap)[:, heads], ref) <= TOL, f"round {r} snapshot"
+        assert maxerr(host(o)[:, :, heads], o_ref) <= TOL, f"round {r} outputs"
+        keep = int(js[r] % T) + 1
+        ref = oracle.replay(ref, *sub, keep=keep, threads=oracle.max_threads())
+        prev = (cur, e, keep)
+    return ref
+
+
+def test_fused_pipeline_tiny_vs_oracle():
+    _fused_pipeline(synth.WORKLOADS["tiny"], 4, [0])
+
+
+def test_fused_pipeline_verify_k14_sampled_vs_oracle():
+    _fused_pipeline(synth.WORKLOADS["verify_k14"], 3, SAMPLE_HEADS)
+
+
+def test_fused_pipeline_serving_mix_bf16_sampled_vs_oracle():
+    w = synth.WORKLOADS["serving_mix_bf16"]
+    Ks = synth.serving_ks(w.seed, 3)
+    _fused_pipeline(w, 3, SAMPLE_HEADS, bf16=True, stash=False, Ts=[int(k) + 1 for k in Ks])
