@@ -61,6 +61,19 @@ def round_bytes_per_head(keep_prev: int, T: int, es: int = 4) -> int:
             + T * (4 * D * es + es) + 2 * T * ROW_BYTES)
 
 
+# One state element per row: a scan row is the decay multiply (1 flop) and three
+# FMAs (u, w, update: 6 flops); a replay row read from the stash plane is the
+# decay multiply and the update FMA (3 flops).
+SCAN_ROW_FLOPS = 7
+STASH_ROW_FLOPS = 3
+# fp32 vector FMA peak without packed math: 256 CU x 4 SIMD x 16 lanes x 2 flops x 2.4 GHz
+PEAK_VALU_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+
+
+def round_flops_per_head(keep_prev: int, T: int) -> int:
+    return D * D * (T * SCAN_ROW_FLOPS + keep_prev * STASH_ROW_FLOPS)
+
+
 def kernel_hash() -> str:
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -223,7 +236,9 @@ def main() -> int:
     fm, finfo, f_ms, f_wall = timed(fused_round, args.warmup, args.steps, 2)
     f_us = [fm[s][0].elapsed_time(fm[s][1]) * 1e3 for s in range(args.steps)]
     f_bytes = [chains * round_bytes_per_head(kp, T) for kp in finfo]
+    f_flops = [chains * round_flops_per_head(kp, T) for kp in finfo]
     achieved = sum(f_bytes) / (sum(f_us) * 1e-6) / 1e9
+    tflops = sum(f_flops) / (sum(f_us) * 1e-6) / 1e12
     value = args.steps * T * H * L / (f_ms * 1e-3)
     ms_per_step = f_ms / args.steps
 
@@ -321,13 +336,16 @@ def main() -> int:
             "sessions": S, "seed": w.seed,
         },
         "roofline": {
-            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBPS,
+            "bound": "alu", "achieved": tflops, "peak": PEAK_VALU_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_VALU_TFLOPS,
             "traffic": measured_traffic("round"),
             "kernel": "kda_verify_round kernel (replay from the stash + full-row scan, "
                       "2176 workgroups)",
+            "flops_per_launch": sum(f_flops) / len(f_flops),
             "bytes_per_launch": sum(f_bytes) / len(f_bytes),
             "mean_launch_us": float(np.mean(f_us)),
+            "hbm": {"achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                    "frac": achieved / PEAK_HBM_GBPS},
         },
         "round_us": stats_us(f_us),
         "round_us_mall_cold": ({"mean": float(np.mean(cold_us)), "p50": pctl(cold_us, 50)}

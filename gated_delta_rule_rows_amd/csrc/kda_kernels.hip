@@ -27,8 +27,8 @@
 //
 // Bit identity.  Every entry point (T-row scan, replay, batched t=1) runs the
 // same row code with the same tiling, explicit fmaf, -ffp-contract=off, one
-// expf, and a reduction tree that does not depend on T, B, L, H or the entry
-// point.  The state crosses HBM as exact f32 words, so a T-row launch equals
+// decay routine, and a reduction tree that does not depend on T, B, L, H or
+// the entry point.  The state crosses HBM as exact f32 words, so a T-row launch equals
 // T chained one-row launches bit for bit.
 //
 // Rollback.  A scan can also write each row's delta vector e (the "stash"
@@ -126,8 +126,13 @@ __device__ __forceinline__ void opaque(float4& x) {
     asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w)::"memory");
 }
 
+// exp(clamp(g, -5, 0)) as 2^(gc * log2(e)) on the hardware exp2 (v_exp_f32,
+// about 1 ulp on this range).  With the f32 rounding of gc * log2(e) the
+// decay is within about 3 ulp of exp(gc) -- and it is the one decay routine
+// every entry point uses, so their results stay bit-identical.
+constexpr float kLog2e = 1.44269504088896340736f;
 __device__ __forceinline__ float decay_of(float g) {
-    return expf(fminf(fmaxf(g, kGateLo), kGateHi));
+    return __builtin_amdgcn_exp2f(__builtin_amdgcn_fmed3f(g, kGateLo, kGateHi) * kLog2e);
 }
 
 // Pointers known to address global memory: loads and stores through them are
