@@ -14,6 +14,9 @@ replay(snap, q, k, v, g, beta, keep, threads=1)
     The state after rows 0..keep-1, rebuilt from the pre-round snapshot.
 batched(states, q, k, v, g, beta, want_o=True, threads=1)
     B independent sessions, one row each; returns (new_states, o).
+accept_greedy(logits, drafts)
+    Per-row argmax (lowest index wins; NaN row -> 0xFFFFFFFF) and the accepted
+    draft count j with its bonus token; returns (vam, j, bonus).
 
 Inputs are float32 arrays, or uint16 arrays holding bf16 bit patterns (all
 five row inputs in the same dtype); the oracle widens bf16 itself.
@@ -61,6 +64,8 @@ def load():
     lib.kda_oracle_scan_rows.restype = i
     lib.kda_oracle_batched.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i]
     lib.kda_oracle_batched.restype = i
+    lib.kda_oracle_accept_greedy.argtypes = [p, i, i, ctypes.c_long, i, p, p, p]
+    lib.kda_oracle_accept_greedy.restype = i
     lib.kda_oracle_version.restype = i
     lib.kda_oracle_max_threads.restype = i
     _lib = lib
@@ -142,6 +147,30 @@ def batched(states, q, k, v, g, beta, want_o=True, threads=1):
     if rc != 0:
         raise MemoryError("oracle work buffer allocation failed")
     return st, o
+
+
+def accept_greedy(logits, drafts):
+    """logits [t][V] float32 (or uint16 bf16 bits); drafts: t - 1 token ids."""
+    lib = load()
+    lg = np.ascontiguousarray(logits)
+    if lg.dtype == np.float32:
+        bf16 = 0
+    elif lg.dtype == np.uint16:
+        bf16 = 1
+    else:
+        raise TypeError("logits must be float32 or uint16 (bf16 bits)")
+    t, V = lg.shape
+    dr = np.ascontiguousarray(np.asarray(drafts, dtype=np.uint32).reshape(-1))
+    if dr.size != t - 1:
+        raise ValueError("need t - 1 drafts")
+    if dr.size == 0:
+        dr = np.zeros(1, np.uint32)
+    vam = np.empty(t, np.uint32)
+    out2 = np.empty(2, np.uint32)
+    rc = lib.kda_oracle_accept_greedy(_ptr(lg), t, V, V, bf16, _ptr(dr), _ptr(vam), _ptr(out2))
+    if rc != 0:
+        raise ValueError("bad accept arguments")
+    return vam, int(out2[0]), int(out2[1])
 
 
 def max_threads() -> int:

@@ -270,3 +270,39 @@ int kda_oracle_max_threads(void) {
     long n = sysconf(_SC_NPROCESSORS_ONLN);
     return n > 0 ? (int)n : 1;
 }
+
+/*
+ * Greedy accept over t verify rows (glm_spec.rs, 0.123.0, the greedy branch
+ * of glm5_spec_round: per-row device argmax with the host argmax's tie-break,
+ * lowest index wins, then the longest matching prefix; a device argmax emits
+ * a sentinel on a NaN row).
+ *   logits : t rows of V values (f32, or bf16 bits when in_bf16), row r at
+ *            element offset r * ld.
+ *   drafts : the t - 1 drafted tokens (draft r is compared with row r's argmax).
+ *   vam    : out, t entries: argmax of row r, lowest index among equal maxima,
+ *            or 0xFFFFFFFF if the row holds a NaN.
+ *   out2   : out, {j, bonus}: j = leading drafts equal to vam[0..], bonus = vam[j].
+ */
+int kda_oracle_accept_greedy(const void* logits, int t, int V, long ld, int in_bf16,
+                             const uint32_t* drafts, uint32_t* vam, uint32_t* out2) {
+    if (t < 1 || V < 1) return -1;
+    for (int r = 0; r < t; ++r) {
+        uint32_t best = 0;
+        float bv = fetch(logits, (long)r * ld, in_bf16);
+        int nan = bv != bv;
+        for (int i = 1; i < V; ++i) {
+            const float x = fetch(logits, (long)r * ld + i, in_bf16);
+            if (x != x) nan = 1;
+            if (x > bv) {
+                bv = x;
+                best = (uint32_t)i;
+            }
+        }
+        vam[r] = nan ? 0xFFFFFFFFu : best;
+    }
+    int j = 0;
+    while (j < t - 1 && drafts[j] == vam[j]) ++j;
+    out2[0] = (uint32_t)j;
+    out2[1] = vam[j];
+    return 0;
+}

@@ -32,6 +32,12 @@ MUTANTS = [
     ("beta stride", "fetch(beta, (long)t * beta_stride, in_bf16)", "fetch(beta, (long)t, in_bf16)"),
     ("bf16 widen shift", "((uint32_t)bits) << 16", "((uint32_t)bits) << 15"),
     ("o row stride", "o[(long)t * o_stride + j]", "o[(long)t * d + j]"),
+    ("argmax ties to highest index", "if (x > bv) {", "if (x >= bv) {"),
+    ("NaN row not flagged", "if (x != x) nan = 1;", ""),
+    ("accept stops one draft early", "while (j < t - 1 && drafts[j] == vam[j]) ++j;",
+     "while (j < t - 2 && drafts[j] == vam[j]) ++j;"),
+    ("accept compares the next row", "drafts[j] == vam[j]) ++j;", "drafts[j] == vam[j + 1]) ++j;"),
+    ("bonus from the last accepted row", "out2[1] = vam[j];", "out2[1] = vam[j > 0 ? j - 1 : 0];"),
 ]
 
 PIN_TESTS = [
@@ -44,6 +50,9 @@ PIN_TESTS = [
     lambda: [pins.test_matrix_form_with_decay(*a) for a in [(4, 6, 0), (8, 9, 2)]],
     lambda: pins.test_chains_are_independent_and_layout_strides_are_right(),
     lambda: pins.test_bf16_widening_matches_ieee_table(),
+    lambda: pins.test_accept_argmax_matches_numpy_first_occurrence(),
+    lambda: pins.test_accept_tie_break_and_special_values(),
+    lambda: [pins.test_accept_prefix_walk(m) for m in (0, 3, 7)],
 ]
 
 
@@ -63,7 +72,7 @@ def _swap_in(path):
     lib = ctypes.CDLL(path)
     real = oracle.load()
     for fn in ("kda_oracle_scan_rows", "kda_oracle_batched", "kda_oracle_version",
-               "kda_oracle_max_threads"):
+               "kda_oracle_max_threads", "kda_oracle_accept_greedy"):
         getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         getattr(lib, fn).restype = getattr(real, fn).restype
     return lib

@@ -334,3 +334,57 @@ def test_bf16_scan_equals_f32_scan_of_torch_widened_values():
     a = oracle.scan_rows(S0, *bits)
     b = oracle.scan_rows(S0, *widened)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------- greedy accept
+
+def test_accept_argmax_matches_numpy_first_occurrence():
+    rng = np.random.default_rng(40)
+    for t, V in ((1, 1), (3, 32), (15, 1000), (4, 4097)):
+        lg = rng.standard_normal((t, V)).astype(np.float32)
+        lg[:, rng.integers(V)] += 0.0
+        vam, _, _ = oracle.accept_greedy(lg, np.zeros(t - 1, np.uint32))
+        assert np.array_equal(vam, np.argmax(lg, axis=1).astype(np.uint32))
+
+
+def test_accept_tie_break_and_special_values():
+    ninf, pinf = -np.inf, np.inf
+    rows = np.array([
+        [1.0, 5.0, 2.0, 5.0, 5.0],      # ties: lowest index (1)
+        [ninf, ninf, ninf, ninf, ninf],  # all -inf: index 0
+        [0.0, pinf, 3.0, pinf, 1.0],     # first +inf
+        [-0.0, 0.0, -1.0, -0.0, -2.0],   # +0 == -0: index 0
+        [2.0, 1.0, np.nan, 3.0, 0.0],    # a NaN anywhere: sentinel
+        [np.nan, 1.0, 2.0, 3.0, 4.0],    # NaN first: sentinel
+    ], np.float32)
+    vam, _, _ = oracle.accept_greedy(rows, np.zeros(len(rows) - 1, np.uint32))
+    assert vam.tolist() == [1, 0, 1, 0, 0xFFFFFFFF, 0xFFFFFFFF]
+
+
+@pytest.mark.parametrize("m", [0, 1, 3, 7])
+def test_accept_prefix_walk(m):
+    # row r's argmax is planted at position p[r]; drafts agree on the first m rows
+    rng = np.random.default_rng(50 + m)
+    t, V = 8, 64
+    lg = rng.uniform(-1, 0, (t, V)).astype(np.float32)
+    p = rng.integers(V, size=t)
+    lg[np.arange(t), p] = 1.0
+    drafts = p[: t - 1].copy()
+    if m < t - 1:
+        drafts[m] = (p[m] + 1) % V          # first disagreement at draft m
+    vam, j, bonus = oracle.accept_greedy(lg, drafts)
+    assert j == m and bonus == p[m]
+    assert np.array_equal(vam, p.astype(np.uint32))
+
+
+def test_accept_single_row_and_bf16():
+    lg = np.array([[0.5, 2.0, 2.0]], np.float32)
+    vam, j, bonus = oracle.accept_greedy(lg, [])
+    assert (vam.tolist(), j, bonus) == ([1], 0, 1)
+    from gated_delta_rule_rows_amd import synth
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((5, 300)).astype(np.float32)
+    bits = synth.to_bf16_bits(x)
+    wide = (bits.astype(np.uint32) << 16).view(np.float32)
+    vam, _, _ = oracle.accept_greedy(bits, np.zeros(4, np.uint32))
+    assert np.array_equal(vam, np.argmax(wide, axis=1).astype(np.uint32))
