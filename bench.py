@@ -16,6 +16,9 @@ Two pipelines of the same round are timed in one run:
   split: kda_scan_rows out of place (the untouched input is the snapshot),
       then kda_replay of the kept rows when j < 14.
 
+Also timed: kda_accept_greedy over one round's logits (t = 15, V = 150,000,
+f32), the greedy accept that decides j on the device.
+
 Prints ONE JSON line.  `value` is verify rows x heads x layers per second of
 the fused pipeline (T rows counted per round).  `roofline` covers its
 dominant kernel (the fused round kernel): algorithmic bytes per launch / mean
@@ -145,6 +148,8 @@ def main() -> int:
                     help="extra round launches timed after a 512 MiB write, for the MALL-cold figure")
     ap.add_argument("--copy-launches", type=int, default=8,
                     help="kda_snapshot launches of the full state, timed for the copy ceiling")
+    ap.add_argument("--accept-launches", type=int, default=32,
+                    help="kda_accept_greedy launches at t=15, V=150,000 (0 skips the figure)")
     ap.add_argument("--no-split", action="store_true", help="skip the split scan + replay pipeline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -313,6 +318,44 @@ def main() -> int:
         copy_gbps = 2 * src.numel() * 4 / (float(np.median(cu)) * 1e-6) / 1e9
         del dst
 
+    # greedy accept of one K=14 round over a 150,000-entry vocabulary (f32 logits)
+    accept = None
+    if args.accept_launches > 0:
+        at, aV = T, synth.VOCAB
+        lg, dr, planted = synth.accept_round(w.seed, 0, at, aV, K // 2)
+        lg_d = torch.from_numpy(lg).cuda()
+        dr_d = torch.from_numpy(dr.view(np.int32)).cuda()
+        vam = torch.empty(at, dtype=torch.int32, device="cuda")
+        out2 = torch.empty(2, dtype=torch.int32, device="cuda")
+        work = kda.accept_workspace()
+        for _ in range(4):
+            kda.kda_accept_greedy(lg_d, dr_d, vam, out2, work)
+        torch.cuda.synchronize()
+        au = []
+        for _ in range(args.accept_launches):
+            a, b = ev(), ev()
+            a.record(stream)
+            kda.kda_accept_greedy(lg_d, dr_d, vam, out2, work)
+            b.record(stream)
+            torch.cuda.synchronize()
+            au.append(a.elapsed_time(b) * 1e3)
+        # back to back, as a pipeline issues it behind the logits' producer
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(args.accept_launches):
+            kda.kda_accept_greedy(lg_d, dr_d, vam, out2, work)
+        b.record(stream)
+        torch.cuda.synchronize()
+        b2b_us = a.elapsed_time(b) * 1e3 / args.accept_launches
+        if out2.cpu().tolist() != [K // 2, int(planted[K // 2])]:
+            raise RuntimeError("kda_accept_greedy returned a wrong accept on the bench input")
+        a_bytes = at * aV * 4 + (at - 1) * 4 + at * 4 + 8
+        accept = {"t": at, "V": aV, "dtype": "f32", "launches": len(au),
+                  "us_synced": stats_us(au), "us_back_to_back": b2b_us, "bytes": a_bytes,
+                  "gbps_back_to_back": a_bytes / (b2b_us * 1e-6) / 1e9,
+                  "note": "two launches per call (split-row argmax, then finish + walk); "
+                          "logits resident (9 MB, warm in the last-level cache)"}
+
     line = {
         "metric": "verify-scan rows*heads/s and achieved HBM GB/s (% peak), K=14, 64 heads",
         "value": value,
@@ -353,6 +396,7 @@ def main() -> int:
         "committed_rows_heads_per_s": sum(int(js[(args.warmup + s) % w.rounds]) + 1
                                           for s in range(args.steps)) * H * L / (f_ms * 1e-3),
         "split": split,
+        "accept": accept,
         "copy_ceiling_gbps": copy_gbps,
         "frac_of_copy_ceiling": (achieved / copy_gbps) if copy_gbps else None,
         "wall_s_timed": f_wall,

@@ -16,6 +16,9 @@ Shapes (D = 128):
                    writes and a replay (or the next fused round) reads
   batched arm      rows [L][B][H][D], beta [L][B][H], o [L][B][H][D];
                    s_ptrs = state_table(...) -> int64 device tensor [L*B]
+  greedy accept    logits [t][V] (row stride free, elements contiguous),
+                   drafts [t-1], vam [t], out2 [2] as int32 or uint32,
+                   work = accept_workspace()
 """
 from __future__ import annotations
 
@@ -29,6 +32,8 @@ T_MAX = 15
 B_MAX = 15
 KDA_IN_F32 = 0
 KDA_IN_BF16 = 1
+ACCEPT_WORK_BYTES = 12288
+NO_TOKEN = 0xFFFFFFFF
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 _lib = None
@@ -62,8 +67,9 @@ def load():
     lib.kda_scan_batched.argtypes = [p, p, p, p, p, p, p, i, i, i, i, p]
     lib.kda_verify_round.argtypes = [p, p, p, p, p, p, p, i, i, p, p, p, p, p, p, p,
                                      i, i, i, i, p]
+    lib.kda_accept_greedy.argtypes = [p, i, i, ctypes.c_longlong, i, p, p, p, p, p]
     for fn in (lib.kda_scan_rows, lib.kda_snapshot, lib.kda_replay, lib.kda_scan_batched,
-               lib.kda_verify_round, lib.kda_abi_version):
+               lib.kda_verify_round, lib.kda_accept_greedy, lib.kda_abi_version):
         fn.restype = i
     lib.kda_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -276,6 +282,57 @@ def kda_scan_batched(s_ptrs, q, k, v, g, beta, o=None, stream=None) -> None:
                                 _stream(stream)))
 
 
+def accept_workspace(device=None) -> torch.Tensor:
+    """Scratch for kda_accept_greedy (uint8 [ACCEPT_WORK_BYTES], contents irrelevant).
+
+    One workspace serves any number of calls issued on one stream; calls that
+    may run at the same time on different streams need their own.
+    """
+    return torch.empty(ACCEPT_WORK_BYTES, dtype=torch.uint8,
+                       device=device if device is not None else "cuda")
+
+
+def _u32(t, n, name):
+    if t.dtype not in (torch.int32, torch.uint32):
+        raise TypeError(f"{name} must be int32 or uint32")
+    _shape(t, (n,), name)
+
+
+def kda_accept_greedy(logits, drafts, vam, out2, work, stream=None) -> None:
+    """Greedy accept: vam[r] = argmax of logits row r (lowest index on ties,
+    NO_TOKEN for a row holding a NaN), out2 = (j, bonus) with j the number of
+    leading drafts equal to vam and bonus = vam[j].
+
+    logits: [t][V] float32 or bfloat16, unit element stride (any row stride).
+    drafts: [t-1] token ids (None allowed when t == 1).
+    """
+    lib = load()
+    if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
+        raise ValueError("logits must be a [t][V] tensor")
+    if not logits.is_cuda:
+        raise ValueError("logits must be a device tensor")
+    t, V = logits.shape
+    if logits.dtype == torch.float32:
+        dt = KDA_IN_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = KDA_IN_BF16
+    else:
+        raise TypeError(f"logits must be float32 or bfloat16, got {logits.dtype}")
+    if V > 1 and logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    ld = logits.stride(0) if t > 1 else V
+    if drafts is not None:
+        _u32(drafts, max(t - 1, 0), "drafts")
+    _u32(vam, t, "vam")
+    _u32(out2, 2, "out2")
+    if work.dtype != torch.uint8 or work.numel() < ACCEPT_WORK_BYTES:
+        raise ValueError(f"work must be a uint8 tensor of >= {ACCEPT_WORK_BYTES} bytes")
+    lp = ctypes.c_void_p(logits.data_ptr())
+    dp = _dev(drafts, "drafts") if drafts is not None and t > 1 else None
+    _check(lib.kda_accept_greedy(lp, int(t), int(V), int(ld), dt, dp, _dev(vam, "vam"),
+                                 _dev(out2, "out2"), _dev(work, "work"), _stream(stream)))
+
+
 def kda_abi_version() -> int:
     return int(load().kda_abi_version())
 
@@ -287,5 +344,5 @@ def kda_last_error() -> str:
 __all__ = [
     "D", "T_MAX", "B_MAX", "KdaError", "load", "lib_path", "kda_scan_rows", "kda_snapshot",
     "kda_replay", "kda_scan_batched", "kda_verify_round", "state_table", "kda_abi_version",
-    "kda_last_error",
+    "kda_last_error", "kda_accept_greedy", "accept_workspace", "ACCEPT_WORK_BYTES", "NO_TOKEN",
 ]

@@ -110,6 +110,8 @@ int launched(const char* fn, hipError_t e) {
 
 constexpr unsigned long long kStateBytes = 4ull * kda::kD * kda::kD;
 constexpr unsigned long long kRowElems = kda::kD;
+static_assert(sizeof(kda::AcceptScratch) <= KDA_ACCEPT_WORK_BYTES, "accept workspace too small");
+static_assert(kda::kNoToken == KDA_NO_TOKEN, "one sentinel");
 
 }  // namespace
 
@@ -290,6 +292,39 @@ int kda_verify_round(const float* snap_prev, float* snap_out, const void* pk, co
     const kda::Launch kind = stash ? kda::Launch::kRoundStash : kda::Launch::kRound;
     return launched(fn, kda::launch_scan(a, kind, in_dtype == KDA_IN_BF16,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dtype,
+                      const uint32_t* drafts, uint32_t* vam, uint32_t* out2, void* work,
+                      void* stream) {
+    const char* fn = "kda_accept_greedy";
+    int rc;
+    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_rows(fn, "t", t))) return rc;
+    if (V < 1) return refuse(KDA_ERR_RANGE, "%s: V=%d, need V >= 1", fn, V);
+    if (t == 1) ld = V;
+    if (ld < V) return refuse(KDA_ERR_RANGE, "%s: ld=%lld < V=%d (rows would overlap)", fn, ld, V);
+    if (ld > (1ll << 40)) return refuse(KDA_ERR_RANGE, "%s: ld=%lld too large", fn, ld);
+    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
+    const unsigned long long n_logits = static_cast<unsigned long long>(t - 1) * ld + V;
+    const Span in[] = {
+        {"logits", logits, n_logits * es, es, false},
+        {"drafts", t > 1 ? drafts : nullptr, (t - 1) * 4ull, 4, t == 1},
+    };
+    const Span out[] = {
+        {"vam", vam, t * 4ull, 4, false},
+        {"out2", out2, 8, 4, false},
+        {"work", work, KDA_ACCEPT_WORK_BYTES, 16, false},
+    };
+    if ((rc = check_spans(fn, in, 2)) || (rc = check_spans(fn, out, 3)) ||
+        (rc = check_alias(fn, out, 3, in, 2)))
+        return rc;
+    auto* ws = static_cast<kda::AcceptScratch*>(work);
+    kda::AcceptArgs a{};
+    a.logits = logits; a.ld = ld; a.t = t; a.V = V;
+    a.drafts = drafts; a.vam = vam; a.out2 = out2;
+    a.pv = ws->pv; a.pi = ws->pi; a.pn = ws->pn;
+    return launched(fn, kda::launch_accept(a, in_dtype == KDA_IN_BF16,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -497,6 +497,154 @@ __global__ void __launch_bounds__(256) kda_copy_kernel(const float4* __restrict_
     for (; i < n4; i += stride) dst[i] = src[i];
 }
 
+// ------------------------------------------------------------------ greedy accept
+
+// Per verify row, the argmax of its logits -- the lowest index among equal
+// maxima, or kNoToken if the row holds a NaN -- then the greedy accept: j is
+// the number of leading drafts equal to the argmaxes of their rows, and the
+// bonus token is the argmax of row j (memra-engine 0.123.0 glm_spec.rs,
+// glm5_spec_round step 4, the greedy branch: device argmaxes with the host
+// argmax's tie-break, then the longest matching prefix).
+//
+// Two launches.  The first splits row r over P workgroups (blockIdx.y = r),
+// each reducing its chunks to a (value, index, nan) partial; all of a row's
+// loads are in flight at once, which is what an HBM-latency-bound read of a
+// few MB needs.  The second, one workgroup with a wave per row, folds each
+// row's P partials, then walks the drafts with one ballot.  The kernel
+// boundary orders the two, so no atomics or fences are involved, and the
+// lowest index of the maximum is unique, so the order partials meet in does
+// not change the result.
+constexpr int kArgThreads = 256;
+constexpr int kArgChunk = kArgThreads * 16;   // elements per workgroup step
+
+struct ArgBest {
+    float v;
+    uint32_t i;
+    uint32_t nan;
+};
+
+__device__ __forceinline__ void take(ArgBest& b, float x, uint32_t i) {
+    b.nan |= x != x ? 1u : 0u;
+    if (x > b.v || (x == b.v && i < b.i)) {
+        b.v = x;
+        b.i = i;
+    }
+}
+
+__device__ __forceinline__ void merge(ArgBest& b, const ArgBest& o) {
+    b.nan |= o.nan;
+    if (o.v > b.v || (o.v == b.v && o.i < b.i)) {
+        b.v = o.v;
+        b.i = o.i;
+    }
+}
+
+__device__ __forceinline__ ArgBest wave_best(ArgBest b) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        ArgBest o;
+        o.v = __shfl_xor(b.v, off);
+        o.i = static_cast<uint32_t>(__shfl_xor(static_cast<int>(b.i), off));
+        o.nan = static_cast<uint32_t>(__shfl_xor(static_cast<int>(b.nan), off));
+        merge(b, o);
+    }
+    return b;
+}
+
+template <bool BF16, bool VEC>
+__global__ void __launch_bounds__(kArgThreads) kda_argmax_part_kernel(AcceptArgs a) {
+    const int tid = threadIdx.x;
+    const int r = blockIdx.y;
+    const int p = blockIdx.x;
+    const int P = gridDim.x;
+    const uint32_t n = static_cast<uint32_t>(a.V);
+    const void* row = static_cast<const char*>(a.logits) +
+                      static_cast<long long>(r) * a.ld * (BF16 ? 2 : 4);
+
+    ArgBest b{-__builtin_inff(), kNoToken, 0u};
+    for (uint32_t c0 = static_cast<uint32_t>(p) * kArgChunk; c0 < n;
+         c0 += static_cast<uint32_t>(P) * kArgChunk) {
+        if constexpr (VEC) {
+            // four 4-element groups per lane, all issued before any compare
+            float4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t i = c0 + (u * kArgThreads + tid) * 4;
+                x[u] = i + 4 <= n ? load4<BF16>(row, i) : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t i = c0 + (u * kArgThreads + tid) * 4;
+                if (i + 4 <= n) {
+                    take(b, x[u].x, i);
+                    take(b, x[u].y, i + 1);
+                    take(b, x[u].z, i + 2);
+                    take(b, x[u].w, i + 3);
+                } else {
+                    for (uint32_t m = i; m < n && m < i + 4; ++m) take(b, load1<BF16>(row, m), m);
+                }
+            }
+        } else {
+            float x[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const uint32_t i = c0 + u * kArgThreads + tid;
+                x[u] = i < n ? load1<BF16>(row, i) : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const uint32_t i = c0 + u * kArgThreads + tid;
+                if (i < n) take(b, x[u], i);
+            }
+        }
+    }
+
+    b = wave_best(b);
+    __shared__ ArgBest wb[kArgThreads / 64];
+    if ((tid & 63) == 0) wb[tid >> 6] = b;
+    __syncthreads();
+    if (tid == 0) {
+#pragma unroll
+        for (int w = 1; w < kArgThreads / 64; ++w) merge(b, wb[w]);
+        const int slot = r * kAcceptPMax + p;
+        a.pv[slot] = b.v;
+        a.pi[slot] = b.i;
+        a.pn[slot] = b.nan;
+    }
+}
+
+// One workgroup of t waves: wave r folds row r's P partials into vam[r];
+// then wave 0 finds the first draft that misses (a ballot) and the bonus.
+__global__ void __launch_bounds__(64 * kTMax) kda_accept_finish_kernel(AcceptArgs a, int P) {
+    const int lane = threadIdx.x & 63;
+    const int r = threadIdx.x >> 6;
+    __shared__ uint32_t vs[kTMax];
+    ArgBest f{-__builtin_inff(), kNoToken, 0u};
+    if (lane < P) {
+        const int slot = r * kAcceptPMax + lane;
+        f.v = a.pv[slot];
+        f.i = a.pi[slot];
+        f.nan = a.pn[slot];
+    }
+    f = wave_best(f);
+    if (lane == 0) {
+        const uint32_t v = f.nan ? kNoToken : f.i;
+        a.vam[r] = v;
+        vs[r] = v;
+    }
+    __syncthreads();
+    if (r == 0) {
+        const uint32_t v = lane < a.t ? vs[lane] : 0u;
+        const bool miss = lane >= a.t - 1 || a.drafts[lane] != v;
+        const int j = __builtin_ctzll(__ballot(miss));   // lane t-1 always misses
+        const uint32_t bonus = static_cast<uint32_t>(__shfl(static_cast<int>(v), j));
+        if (lane == 0) {
+            a.out2[0] = static_cast<uint32_t>(j);
+            a.out2[1] = bonus;
+        }
+    }
+}
+
 template <bool BF16, Rows MA, Rows MB, bool TABLE>
 hipError_t launch_one(const ScanArgs& a, hipStream_t stream) {
     using TL = TileT;
@@ -524,6 +672,36 @@ hipError_t launch_dtype(const ScanArgs& a, Launch kind, hipStream_t stream) {
 
 hipError_t launch_scan(const ScanArgs& a, Launch kind, bool bf16, hipStream_t stream) {
     return bf16 ? launch_dtype<true>(a, kind, stream) : launch_dtype<false>(a, kind, stream);
+}
+
+int accept_workgroups_per_row(int V) {
+    const int chunks = (V + kArgChunk - 1) / kArgChunk;
+    return chunks < kAcceptPMax ? chunks : kAcceptPMax;
+}
+
+hipError_t launch_accept(const AcceptArgs& a, bool bf16, hipStream_t stream) {
+    const int es = bf16 ? 2 : 4;
+    // whole 4-element groups are aligned loads when every row starts aligned
+    const bool vec = reinterpret_cast<uintptr_t>(a.logits) % (4 * es) == 0 &&
+                     (a.t == 1 || a.ld % 4 == 0);
+    const int P = accept_workgroups_per_row(a.V);
+    const dim3 grid(P, a.t);
+    const dim3 block(kArgThreads);
+    if (bf16) {
+        if (vec)
+            kda_argmax_part_kernel<true, true><<<grid, block, 0, stream>>>(a);
+        else
+            kda_argmax_part_kernel<true, false><<<grid, block, 0, stream>>>(a);
+    } else {
+        if (vec)
+            kda_argmax_part_kernel<false, true><<<grid, block, 0, stream>>>(a);
+        else
+            kda_argmax_part_kernel<false, false><<<grid, block, 0, stream>>>(a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    kda_accept_finish_kernel<<<dim3(1), dim3(64 * a.t), 0, stream>>>(a, P);
+    return hipGetLastError();
 }
 
 hipError_t launch_copy(const float* src, float* dst, size_t n_floats, hipStream_t stream) {

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
+#include <cstdint>
 
 namespace kda {
 
@@ -57,5 +58,33 @@ enum class Launch {
 hipError_t launch_scan(const ScanArgs& a, Launch kind, bool bf16, hipStream_t stream);
 
 hipError_t launch_copy(const float* src, float* dst, size_t n_floats, hipStream_t stream);
+
+constexpr uint32_t kNoToken = 0xFFFFFFFFu;   // argmax of a row that holds a NaN
+constexpr int kAcceptPMax = 64;              // workgroups per row, at most
+
+// Scratch of one greedy accept: the per-(row, workgroup) partial argmaxes
+// the first launch writes and the second reads.  Nothing in it needs to be
+// initialised.
+struct AcceptScratch {
+    float pv[kTMax * kAcceptPMax];
+    uint32_t pi[kTMax * kAcceptPMax];
+    uint32_t pn[kTMax * kAcceptPMax];
+};
+
+struct AcceptArgs {
+    const void* logits;      // row r at element r*ld
+    long long ld;
+    int t;                   // rows, 1..kTMax
+    int V;                   // logits per row, >= 1
+    const uint32_t* drafts;  // t-1 draft tokens
+    uint32_t* vam;           // t argmaxes
+    uint32_t* out2;          // {j, bonus}
+    float* pv;               // AcceptScratch members
+    uint32_t* pi;
+    uint32_t* pn;
+};
+
+int accept_workgroups_per_row(int V);
+hipError_t launch_accept(const AcceptArgs& a, bool bf16, hipStream_t stream);
 
 }  // namespace kda

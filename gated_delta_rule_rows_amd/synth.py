@@ -16,7 +16,14 @@ shape.  One call is keyed by (seed, stream, index): numpy's PCG64 seeded from
 ``SeedSequence([seed, stream, index])``, so a test can regenerate any single
 round or step without drawing the ones before it.
 
-Streams: 0 = verify rows, 1 = accept draws, 2 = warm-up rows.
+Greedy-accept inputs: logits ~ N(0, 3^2) per (row, vocabulary entry), f32,
+with one planted token per row raised to 64.0 (far above every normal draw,
+so it is the row's unique maximum), and draft tokens equal to the planted
+tokens of the rows before them, except for a planted mismatch at the
+accepted-draft count j.  Vocabulary size 150,000 mirrors the pages' head
+(about 600k floats over the four rows of a K = 3 round).
+
+Streams: 0 = verify rows, 1 = accept draws, 2 = warm-up rows, 3 = logits.
 """
 from __future__ import annotations
 
@@ -32,6 +39,9 @@ GATE_LO = -5.0
 STREAM_ROWS = 0
 STREAM_ACCEPT = 1
 STREAM_WARMUP = 2
+STREAM_LOGITS = 3
+VOCAB = 150_000
+PLANTED_LOGIT = 64.0
 
 
 def _rng(seed: int, stream: int, index: int) -> np.random.Generator:
@@ -80,6 +90,27 @@ def serving_ks(seed: int, n: int, choices=(1, 3, 5, 7, 14)) -> np.ndarray:
     """Per-round draft counts K drawn uniformly from `choices`."""
     rng = _rng(seed, STREAM_ACCEPT, 1)
     return np.asarray(choices)[rng.integers(0, len(choices), size=n)]
+
+
+def accept_round(seed: int, index: int, t: int, V: int, j: int):
+    """One greedy-accept round: (logits [t][V] f32, drafts [t-1] uint32, planted [t] uint32).
+
+    Row r's planted token is its unique maximum; drafts[r] = planted[r] for
+    r < j and drafts[j] != planted[j] (when j < t - 1), so exactly j drafts
+    are accepted and the bonus token is planted[j].
+    """
+    if not (1 <= t and 1 <= V and 0 <= j <= t - 1):
+        raise ValueError("need t >= 1, V >= 1, 0 <= j <= t - 1")
+    rng = _rng(seed, STREAM_LOGITS, index)
+    logits = (rng.standard_normal((t, V)) * 3.0).astype(np.float32)
+    planted = rng.integers(0, V, size=t).astype(np.uint32)
+    logits[np.arange(t), planted] = PLANTED_LOGIT
+    drafts = planted[: t - 1].copy()
+    if j < t - 1:
+        drafts[j] = (planted[j] + 1 + rng.integers(0, max(V - 1, 1))) % max(V, 2)
+        if V == 1:
+            drafts[j] = 1   # the only token is 0, so any other id misses
+    return logits, drafts, planted
 
 
 def warmup_rows(seed: int, n_rows: int, L: int, H: int, d: int = D) -> dict:

@@ -43,6 +43,8 @@
 #ifndef KDA_H
 #define KDA_H
 
+#include <stdint.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -50,7 +52,9 @@ extern "C" {
 #define KDA_HEAD_DIM 128   /* d_k = d_v; glm5_spec_ppn_gate.rs fixture head_dim */
 #define KDA_T_MAX 15       /* verify rows per round: K + 1 <= 15 (glm_spec.rs, WALK-REUSE) */
 #define KDA_B_MAX 15       /* batched-decode sessions per step (same knee) */
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
+#define KDA_ACCEPT_WORK_BYTES 12288   /* workspace of kda_accept_greedy */
+#define KDA_NO_TOKEN 0xFFFFFFFFu      /* argmax slot of a logits row holding a NaN */
 
 enum { KDA_IN_F32 = 0, KDA_IN_BF16 = 1 };
 
@@ -170,6 +174,35 @@ int kda_verify_round(const float* snap_prev, float* snap_out, const void* pk, co
                      const void* q, const void* k, const void* v, const void* g,
                      const void* beta, float* o, float* e, int L, int T, int H, int in_dtype,
                      void* stream);
+
+/*
+ * Greedy accept of one verify round.
+ *   glm_spec.rs (0.123.0), glm5_spec_round step 4, greedy branch: one device
+ *   argmax per verify row, the lowest index winning among equal maxima; then
+ *   j = the length of the longest prefix of drafts that equal the argmaxes of
+ *   their rows, and the bonus token is the argmax of row j.  A row holding a
+ *   NaN has no argmax: its slot is KDA_NO_TOKEN, which the caller must refuse
+ *   (the same file's sentinel guard on device argmaxes).
+ *   logits : t rows of V logits in in_dtype (bf16 widens exactly by bits << 16);
+ *            row r starts at element r*ld, ld >= V when t > 1 (ignored when
+ *            t == 1).  Element alignment; 16-byte aligned rows (and ld a
+ *            multiple of 4) take the vector-load kernel.
+ *   t      : verify rows, 1..KDA_T_MAX (K + 1).
+ *   drafts : t-1 u32 draft tokens, drafts[r] being the token fed after row r;
+ *            may be NULL when t == 1.
+ *   vam    : t u32, receives each row's argmax (or KDA_NO_TOKEN).
+ *   out2   : 2 u32, receives {j, bonus}: 0 <= j <= t-1 accepted drafts and
+ *            bonus = vam[j]; the round then commits keep = j + 1 rows.
+ *   work   : KDA_ACCEPT_WORK_BYTES of device memory, 16-byte aligned, owned by
+ *            the caller: scratch for per-row partial results, in any state on
+ *            entry.  Calls that can run at the same time (on different
+ *            streams) need different work buffers.
+ * Comparisons are f32: -0 equals +0 (the lower index wins), -inf is an
+ * ordinary value.  The outputs depend only on the inputs, never on timing.
+ */
+int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dtype,
+                      const uint32_t* drafts, uint32_t* vam, uint32_t* out2, void* work,
+                      void* stream);
 
 /* Message for the last nonzero status returned on the calling thread. */
 const char* kda_last_error(void);

@@ -41,7 +41,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"kda_scan_rows", "kda_snapshot", "kda_replay", "kda_scan_batched",
-                          "kda_verify_round", "kda_last_error", "kda_abi_version"}
+                          "kda_verify_round", "kda_accept_greedy", "kda_last_error",
+                          "kda_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -51,6 +52,9 @@ def test_abi_version_matches_header(lib):
     assert _header_constant("KDA_HEAD_DIM") == kda.D == 128
     assert _header_constant("KDA_T_MAX") == kda.T_MAX == 15
     assert _header_constant("KDA_B_MAX") == kda.B_MAX == 15
+    assert _header_constant("KDA_ACCEPT_WORK_BYTES") == kda.ACCEPT_WORK_BYTES
+    assert re.search(r"#define\s+KDA_NO_TOKEN\s+0xFFFFFFFFu", open(HEADER).read())
+    assert kda.NO_TOKEN == 0xFFFFFFFF
 
 
 class Bufs:
@@ -117,6 +121,14 @@ def _batched(lib, b, **kw):
     a.update(kw)
     return lib.kda_scan_batched(a["ptrs"], a["q"], a["k"], a["v"], a["g"], a["beta"], a["o"],
                                 a["L"], a["B"], a["H"], a["dt"], None)
+
+
+def _accept(lib, b, **kw):
+    a = dict(logits=b["q"], t=4, V=1000, ld=1000, dt=0, drafts=b["k"], vam=b["o"], out2=b["v"],
+             work=b["snap"])
+    a.update(kw)
+    return lib.kda_accept_greedy(a["logits"], a["t"], a["V"], a["ld"], a["dt"], a["drafts"],
+                                 a["vam"], a["out2"], a["work"], None)
 
 
 def _msg(lib):
@@ -228,6 +240,38 @@ def test_batched_refusals(lib, b, kw, code, needle):
 
 def test_batched_alias(lib, b):
     assert _batched(lib, b, o=b["q"]) == ERR_ALIAS and "o overlaps q" in _msg(lib)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(t=0), ERR_RANGE, "t=0"),
+    (dict(t=16), ERR_RANGE, "t=16"),
+    (dict(V=0), ERR_RANGE, "V=0"),
+    (dict(V=-5), ERR_RANGE, "V=-5"),
+    (dict(ld=999), ERR_RANGE, "ld=999"),
+    (dict(dt=2), ERR_ARG, "in_dtype"),
+    (dict(logits=None), ERR_ARG, "logits is NULL"),
+    (dict(drafts=None), ERR_ARG, "drafts is NULL"),
+    (dict(vam=None), ERR_ARG, "vam is NULL"),
+    (dict(out2=None), ERR_ARG, "out2 is NULL"),
+    (dict(work=None), ERR_ARG, "work is NULL"),
+    # t == 1 needs no drafts and ignores ld: the refusal comes from the NULL vam
+    (dict(t=1, drafts=None, ld=0, vam=None), ERR_ARG, "vam is NULL"),
+])
+def test_accept_refusals(lib, b, kw, code, needle):
+    assert _accept(lib, b, **kw) == code
+    assert needle in _msg(lib)
+
+
+def test_accept_alignment_and_alias(lib, b):
+    off = lambda n, k: ctypes.c_void_p(b.addr[n] + k)
+    assert _accept(lib, b, work=off("snap", 4)) == ERR_ALIGN and "work is not 16" in _msg(lib)
+    assert _accept(lib, b, vam=off("o", 2)) == ERR_ALIGN and "vam is not 4" in _msg(lib)
+    assert _accept(lib, b, logits=off("q", 2)) == ERR_ALIGN and "logits is not 4" in _msg(lib)
+    assert _accept(lib, b, logits=off("q", 1), dt=1) == ERR_ALIGN and "2-byte" in _msg(lib)
+    assert _accept(lib, b, vam=off("q", 3996)) == ERR_ALIAS and "vam overlaps logits" in _msg(lib)
+    assert _accept(lib, b, out2=b["k"]) == ERR_ALIAS and "out2 overlaps drafts" in _msg(lib)
+    assert _accept(lib, b, out2=off("snap", 64)) == ERR_ALIAS and "out2 overlaps work" in _msg(lib)
+    assert _accept(lib, b, vam=b["v"]) == ERR_ALIAS and "vam overlaps out2" in _msg(lib)
 
 
 def test_snapshot_refusals(lib, b):
