@@ -66,6 +66,8 @@ def load():
     lib.kda_oracle_batched.restype = i
     lib.kda_oracle_accept_greedy.argtypes = [p, i, i, ctypes.c_long, i, p, p, p]
     lib.kda_oracle_accept_greedy.restype = i
+    lib.kda_oracle_conv_reroll.argtypes = [p, p, p, i, i, i, ctypes.c_long, i]
+    lib.kda_oracle_conv_reroll.restype = i
     lib.kda_oracle_version.restype = i
     lib.kda_oracle_max_threads.restype = i
     _lib = lib
@@ -171,6 +173,30 @@ def accept_greedy(logits, drafts):
     if rc != 0:
         raise ValueError("bad accept arguments")
     return vam, int(out2[0]), int(out2[1])
+
+
+RING_ROWS = 3   # short-conv kernel size 4 keeps 3 prior raw rows
+
+
+def conv_reroll(ring_snap, raw, keep):
+    """Conv ring after `keep` accepted rows: ring_snap [L][3][C] f32 rolled once per
+    kept row over raw [L][T_round][C] (float32, or uint16 bf16 bits)."""
+    lib = load()
+    rs = np.ascontiguousarray(ring_snap, np.float32)
+    rw = np.ascontiguousarray(raw)
+    if rw.dtype == np.float32:
+        bf16 = 0
+    elif rw.dtype == np.uint16:
+        bf16 = 1
+    else:
+        raise TypeError("raw must be float32 or uint16 (bf16 bits)")
+    L, T, C = rw.shape
+    if rs.shape != (L, RING_ROWS, C):
+        raise ValueError("ring_snap must be [L][3][C] matching raw")
+    out = np.empty_like(rs)
+    if lib.kda_oracle_conv_reroll(_ptr(rs), _ptr(rw), _ptr(out), L, T, int(keep), C, bf16) != 0:
+        raise ValueError("bad conv_reroll arguments")
+    return out
 
 
 def max_threads() -> int:

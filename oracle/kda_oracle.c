@@ -306,3 +306,33 @@ int kda_oracle_accept_greedy(const void* logits, int t, int V, long ld, int in_b
     out2[1] = vam[j];
     return 0;
 }
+
+/*
+ * Conv-ring rollback (glm_spec.rs, 0.123.0, module doc VERIFY-ROW BATCHING and
+ * the Glm5VerifyCkpt doc): the short-conv ring of a KDA layer holds the last
+ * W-1 = 3 raw conv inputs (kernel size 4, glm5_spec_ppn_gate.rs fixture
+ * short_conv_kernel_size); after accepting keep rows it is rebuilt from the
+ * pre-round ring snapshot by rolling it forward once per kept row over the
+ * round's raw input rows.
+ *   ring_snap, ring_out : [L][3][C] f32, row 0 the oldest
+ *   raw                 : [L][T_round][C] f32 or bf16 bits
+ * Each roll drops the oldest ring row and appends the next raw row.
+ */
+#define ORACLE_RING_ROWS 3
+
+int kda_oracle_conv_reroll(const float* ring_snap, const void* raw, float* ring_out, int L,
+                           int T_round, int keep, long C, int in_bf16) {
+    if (L < 1 || T_round < 1 || keep < 1 || keep > T_round || C < 1) return -1;
+    for (long l = 0; l < L; ++l) {
+        float* ring = ring_out + l * ORACLE_RING_ROWS * C;
+        memcpy(ring, ring_snap + l * ORACLE_RING_ROWS * C, sizeof(float) * ORACLE_RING_ROWS * C);
+        for (int r = 0; r < keep; ++r) {
+            for (int m = 0; m + 1 < ORACLE_RING_ROWS; ++m)
+                memcpy(ring + m * C, ring + (m + 1) * C, sizeof(float) * C);
+            for (long c = 0; c < C; ++c)
+                ring[(ORACLE_RING_ROWS - 1) * C + c] =
+                    fetch(raw, (l * T_round + r) * C + c, in_bf16);
+        }
+    }
+    return 0;
+}

@@ -38,6 +38,12 @@ MUTANTS = [
      "while (j < t - 2 && drafts[j] == vam[j]) ++j;"),
     ("accept compares the next row", "drafts[j] == vam[j]) ++j;", "drafts[j] == vam[j + 1]) ++j;"),
     ("bonus from the last accepted row", "out2[1] = vam[j];", "out2[1] = vam[j > 0 ? j - 1 : 0];"),
+    ("ring never shifts", "for (int m = 0; m + 1 < ORACLE_RING_ROWS; ++m)",
+     "for (int m = 0; m + 1 < 0; ++m)"),
+    ("ring appends the previous raw row", "fetch(raw, (l * T_round + r) * C + c, in_bf16)",
+     "fetch(raw, (l * T_round + (r > 0 ? r - 1 : 0)) * C + c, in_bf16)"),
+    ("ring ignores the layer", "fetch(raw, (l * T_round + r) * C + c, in_bf16)",
+     "fetch(raw, (long)r * C + c, in_bf16)"),
 ]
 
 PIN_TESTS = [
@@ -53,6 +59,9 @@ PIN_TESTS = [
     lambda: pins.test_accept_argmax_matches_numpy_first_occurrence(),
     lambda: pins.test_accept_tie_break_and_special_values(),
     lambda: [pins.test_accept_prefix_walk(m) for m in (0, 3, 7)],
+    lambda: [pins.test_reroll_is_the_last_three_rows_of_snapshot_then_kept_rows(k)
+             for k in (1, 2, 4)],
+    lambda: pins.test_reroll_composes_and_keeps_layers_apart(),
 ]
 
 
@@ -72,7 +81,7 @@ def _swap_in(path):
     lib = ctypes.CDLL(path)
     real = oracle.load()
     for fn in ("kda_oracle_scan_rows", "kda_oracle_batched", "kda_oracle_version",
-               "kda_oracle_max_threads", "kda_oracle_accept_greedy"):
+               "kda_oracle_max_threads", "kda_oracle_accept_greedy", "kda_oracle_conv_reroll"):
         getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         getattr(lib, fn).restype = getattr(real, fn).restype
     return lib

@@ -388,3 +388,51 @@ def test_accept_single_row_and_bf16():
     wide = (bits.astype(np.uint32) << 16).view(np.float32)
     vam, _, _ = oracle.accept_greedy(bits, np.zeros(4, np.uint32))
     assert np.array_equal(vam, np.argmax(wide, axis=1).astype(np.uint32))
+
+
+# ---------------------------------------------------------------- conv ring re-roll
+
+def _ring_case(seed, L=2, T=6, C=5):
+    rng = np.random.default_rng(seed)
+    snap = rng.standard_normal((L, 3, C)).astype(np.float32)
+    raw = rng.standard_normal((L, T, C)).astype(np.float32)
+    return snap, raw
+
+
+@pytest.mark.parametrize("keep", [1, 2, 3, 4, 6])
+def test_reroll_is_the_last_three_rows_of_snapshot_then_kept_rows(keep):
+    # closed form: the committed ring is the window of the last 3 entries of the
+    # sequence (ring rows 0..2, raw rows 0..keep-1), oldest first
+    snap, raw = _ring_case(60 + keep)
+    out = oracle.conv_reroll(snap, raw, keep)
+    seq = np.concatenate([snap, raw[:, :keep]], axis=1)
+    assert np.array_equal(out, seq[:, -3:])
+    if keep >= 3:
+        assert np.array_equal(out, raw[:, keep - 3:keep])
+
+
+def test_reroll_composes_and_keeps_layers_apart():
+    snap, raw = _ring_case(70, L=3, T=7, C=9)
+    full = oracle.conv_reroll(snap, raw, 5)
+    # rolling 2 rows, then the next 3 from that ring, is rolling 5
+    mid = oracle.conv_reroll(snap, raw, 2)
+    two_step = oracle.conv_reroll(mid, np.ascontiguousarray(raw[:, 2:]), 3)
+    assert np.array_equal(full, two_step)
+    # each layer depends on its own ring and rows only
+    raw2 = raw.copy()
+    raw2[1] += 1.0
+    out2 = oracle.conv_reroll(snap, raw2, 5)
+    assert np.array_equal(out2[0], full[0]) and np.array_equal(out2[2], full[2])
+    assert not np.array_equal(out2[1], full[1])
+
+
+def test_reroll_bf16_rows_widen_exactly():
+    from gated_delta_rule_rows_amd import synth
+    snap, raw = _ring_case(80)
+    bits = synth.to_bf16_bits(raw)
+    wide = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(oracle.conv_reroll(snap, bits, 4), oracle.conv_reroll(snap, wide, 4))
+    with pytest.raises(ValueError):
+        oracle.conv_reroll(snap, raw, 0)
+    with pytest.raises(ValueError):
+        oracle.conv_reroll(snap, raw, 7)
