@@ -17,7 +17,9 @@ Two pipelines of the same round are timed in one run:
       then kda_replay of the kept rows when j < 14.
 
 Also timed: kda_accept_greedy over one round's logits (t = 15, V = 150,000,
-f32), the greedy accept that decides j on the device.
+f32), the greedy accept that decides j on the device; kda_conv_reroll of the
+34 layers' short-conv rings; kda_copy_batch of 34 separately allocated layer
+states in one launch.
 
 Prints ONE JSON line.  `value` is verify rows x heads x layers per second of
 the fused pipeline (T rows counted per round).  `roofline` covers its
@@ -356,6 +358,43 @@ def main() -> int:
                   "note": "two launches per call (split-row argmax, then finish + walk); "
                           "logits resident (9 MB, warm in the last-level cache)"}
 
+    # conv-ring rollback (34 layers x 3 rows x 24,576 q/k/v channels) and the
+    # pointer-table copy of 34 separately allocated 4 MiB layer states
+    rollback_extras = None
+    if args.copy_launches > 0:
+        C = 3 * H * D
+        ring_snap = torch.randn(L, 3, C, device="cuda")
+        raw = torch.randn(L, T, C, device="cuda")
+        ring_out = torch.empty_like(ring_snap)
+        srcs = [bufs[0][0][l] for l in range(L)]
+        dsts = [torch.empty_like(x) for x in srcs]
+        table = kda.copy_table(srcs, dsts)
+
+        def time_b2b(fn, n):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record(stream)
+            for _ in range(n):
+                fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / n
+
+        rr_us = time_b2b(lambda: kda.kda_conv_reroll(ring_snap, raw, 8, ring_out),
+                         args.copy_launches)
+        cb_us = time_b2b(lambda: kda.kda_copy_batch(table, L, H * D * D), args.copy_launches)
+        rr_bytes = 2 * L * 3 * C * 4
+        cb_bytes = 2 * L * H * D * D * 4
+        rollback_extras = {
+            "conv_reroll": {"keep": 8, "channels": C, "us": rr_us, "bytes": rr_bytes,
+                            "gbps": rr_bytes / (rr_us * 1e-6) / 1e9},
+            "copy_batch_34_states": {"us": cb_us, "bytes": cb_bytes,
+                                     "gbps": cb_bytes / (cb_us * 1e-6) / 1e9},
+        }
+        del ring_snap, raw, ring_out, dsts, table
+
     line = {
         "metric": "verify-scan rows*heads/s and achieved HBM GB/s (% peak), K=14, 64 heads",
         "value": value,
@@ -397,6 +436,7 @@ def main() -> int:
                                           for s in range(args.steps)) * H * L / (f_ms * 1e-3),
         "split": split,
         "accept": accept,
+        "rollback_extras": rollback_extras,
         "copy_ceiling_gbps": copy_gbps,
         "frac_of_copy_ceiling": (achieved / copy_gbps) if copy_gbps else None,
         "wall_s_timed": f_wall,

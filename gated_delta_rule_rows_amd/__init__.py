@@ -16,6 +16,8 @@ Shapes (D = 128):
                    writes and a replay (or the next fused round) reads
   batched arm      rows [L][B][H][D], beta [L][B][H], o [L][B][H][D];
                    s_ptrs = state_table(...) -> int64 device tensor [L*B]
+  conv ring        ring [L][3][C] float32, raw conv input rows [L][T][C]
+  batched copy     table = copy_table(srcs, dsts) -> int64 device tensor [2n]
   greedy accept    logits [t][V] (row stride free, elements contiguous),
                    drafts [t-1], vam [t], out2 [2] as int32 or uint32,
                    work = accept_workspace()
@@ -34,6 +36,7 @@ KDA_IN_F32 = 0
 KDA_IN_BF16 = 1
 ACCEPT_WORK_BYTES = 12288
 NO_TOKEN = 0xFFFFFFFF
+RING_ROWS = 3
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 _lib = None
@@ -68,8 +71,11 @@ def load():
     lib.kda_verify_round.argtypes = [p, p, p, p, p, p, p, i, i, p, p, p, p, p, p, p,
                                      i, i, i, i, p]
     lib.kda_accept_greedy.argtypes = [p, i, i, ctypes.c_longlong, i, p, p, p, p, p]
+    lib.kda_conv_reroll.argtypes = [p, p, p, i, i, i, ctypes.c_longlong, i, p]
+    lib.kda_copy_batch.argtypes = [p, i, ctypes.c_longlong, p]
     for fn in (lib.kda_scan_rows, lib.kda_snapshot, lib.kda_replay, lib.kda_scan_batched,
-               lib.kda_verify_round, lib.kda_accept_greedy, lib.kda_abi_version):
+               lib.kda_verify_round, lib.kda_accept_greedy, lib.kda_conv_reroll,
+               lib.kda_copy_batch, lib.kda_abi_version):
         fn.restype = i
     lib.kda_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -333,6 +339,45 @@ def kda_accept_greedy(logits, drafts, vam, out2, work, stream=None) -> None:
                                  _dev(out2, "out2"), _dev(work, "work"), _stream(stream)))
 
 
+def kda_conv_reroll(ring_snap, raw, keep: int, ring_out, stream=None) -> None:
+    """ring_out = the short-conv ring after `keep` accepted rows: ring_snap [L][3][C]
+    rolled once per kept row over the round's raw conv inputs raw [L][T_round][C]."""
+    lib = load()
+    if raw.dim() != 3:
+        raise ValueError(f"raw must be [L][T_round][C], got {tuple(raw.shape)}")
+    L, T, C = raw.shape
+    _state(ring_snap, (L, RING_ROWS, C), "ring_snap")
+    _state(ring_out, (L, RING_ROWS, C), "ring_out")
+    dt = _in_dtype((raw,))
+    _check(lib.kda_conv_reroll(_dev(ring_snap, "ring_snap"), _dev(raw, "raw"),
+                               _dev(ring_out, "ring_out"), L, T, int(keep), C, dt,
+                               _stream(stream)))
+
+
+def copy_table(srcs, dsts, device=None) -> torch.Tensor:
+    """Device pointer table [src_0..src_{n-1}, dst_0..dst_{n-1}] (int64) for
+    kda_copy_batch.  Every buffer is a contiguous float32 device tensor of one size."""
+    if len(srcs) != len(dsts) or not srcs:
+        raise ValueError("need as many destinations as sources, at least one")
+    words = srcs[0].numel()
+    for t in list(srcs) + list(dsts):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous()):
+            raise ValueError("copy buffers must be contiguous device tensors")
+        if t.dtype != torch.float32 or t.numel() != words:
+            raise ValueError("copy buffers must be float32 tensors of one size")
+    ptrs = [t.data_ptr() for t in srcs] + [t.data_ptr() for t in dsts]
+    return torch.tensor(ptrs, dtype=torch.int64, device=device or srcs[0].device)
+
+
+def kda_copy_batch(table, n: int, words: int, stream=None) -> None:
+    """Copy n buffers of `words` float32, named by a copy_table, in one launch."""
+    lib = load()
+    if table.dtype != torch.int64:
+        raise TypeError("table must be an int64 device tensor")
+    _shape(table, (2 * n,), "table")
+    _check(lib.kda_copy_batch(_dev(table, "table"), int(n), int(words), _stream(stream)))
+
+
 def kda_abi_version() -> int:
     return int(load().kda_abi_version())
 
@@ -345,4 +390,5 @@ __all__ = [
     "D", "T_MAX", "B_MAX", "KdaError", "load", "lib_path", "kda_scan_rows", "kda_snapshot",
     "kda_replay", "kda_scan_batched", "kda_verify_round", "state_table", "kda_abi_version",
     "kda_last_error", "kda_accept_greedy", "accept_workspace", "ACCEPT_WORK_BYTES", "NO_TOKEN",
+    "kda_conv_reroll", "copy_table", "kda_copy_batch", "RING_ROWS",
 ]

@@ -112,6 +112,7 @@ constexpr unsigned long long kStateBytes = 4ull * kda::kD * kda::kD;
 constexpr unsigned long long kRowElems = kda::kD;
 static_assert(sizeof(kda::AcceptScratch) <= KDA_ACCEPT_WORK_BYTES, "accept workspace too small");
 static_assert(kda::kNoToken == KDA_NO_TOKEN, "one sentinel");
+static_assert(kda::kRingRows == KDA_CONV_RING_ROWS, "one ring depth");
 
 }  // namespace
 
@@ -325,6 +326,45 @@ int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dty
     a.pv = ws->pv; a.pi = ws->pi; a.pn = ws->pn;
     return launched(fn, kda::launch_accept(a, in_dtype == KDA_IN_BF16,
                                            static_cast<hipStream_t>(stream)));
+}
+
+int kda_conv_reroll(const float* ring_snap, const void* raw, float* ring_out, int L,
+                    int T_round, int keep, long long C, int in_dtype, void* stream) {
+    const char* fn = "kda_conv_reroll";
+    int rc;
+    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_rows(fn, "T_round", T_round))) return rc;
+    if (L < 1) return refuse(KDA_ERR_RANGE, "%s: L=%d, need L >= 1", fn, L);
+    if (keep < 1 || keep > T_round)
+        return refuse(KDA_ERR_RANGE, "%s: keep=%d outside 1..T_round=%d", fn, keep, T_round);
+    if (C < 1 || C > (1ll << 40) / (static_cast<long long>(L) * T_round))
+        return refuse(KDA_ERR_RANGE, "%s: C=%lld outside 1..%lld", fn, C,
+                      (1ll << 40) / (static_cast<long long>(L) * T_round));
+    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
+    const unsigned long long ring = static_cast<unsigned long long>(L) * KDA_CONV_RING_ROWS * C;
+    const Span in[] = {
+        {"ring_snap", ring_snap, ring * 4, 4, false},
+        {"raw", raw, static_cast<unsigned long long>(L) * T_round * C * es, es, false},
+    };
+    const Span out[] = {{"ring_out", ring_out, ring * 4, 4, false}};
+    if ((rc = check_spans(fn, in, 2)) || (rc = check_spans(fn, out, 1)) ||
+        (rc = check_alias(fn, out, 1, in, 2)))
+        return rc;
+    kda::RerollArgs a{};
+    a.ring_snap = ring_snap; a.raw = raw; a.ring_out = ring_out;
+    a.C = C; a.L = L; a.T = T_round; a.keep = keep;
+    return launched(fn, kda::launch_reroll(a, in_dtype == KDA_IN_BF16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int kda_copy_batch(const uint64_t* table, int n, long long words, void* stream) {
+    const char* fn = "kda_copy_batch";
+    int rc;
+    if (n < 1 || n > 65535) return refuse(KDA_ERR_RANGE, "%s: n=%d outside 1..65535", fn, n);
+    if (words < 1 || words > (1ll << 40))
+        return refuse(KDA_ERR_RANGE, "%s: words=%lld outside 1..2^40", fn, words);
+    const Span in[] = {{"table", table, 16ull * n, 8, false}};
+    if ((rc = check_spans(fn, in, 1))) return rc;
+    return launched(fn, kda::launch_copy_batch(table, n, words, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -497,6 +497,103 @@ __global__ void __launch_bounds__(256) kda_copy_kernel(const float4* __restrict_
     for (; i < n4; i += stride) dst[i] = src[i];
 }
 
+// ------------------------------------------------------------------ conv ring
+
+// The committed short-conv ring after `keep` accepted rows.  The ring holds
+// the last 3 raw conv inputs (kernel size 4); rolling it once per kept row
+// over the round's raw rows leaves, in output row m, entry keep + m of the
+// sequence (ring rows 0..2, raw rows 0..T-1) -- memra-engine 0.123.0
+// glm_spec.rs, module doc VERIFY-ROW BATCHING: ring snapshot plus re-roll at
+// T = keep over the stolen raw rows.  Pure data movement: one thread moves
+// four channels of all three output rows.
+constexpr int kRerollThreads = 256;
+constexpr int kRerollChans = kRerollThreads * 4;   // channels per workgroup
+
+template <bool BF16, bool VEC>
+__global__ void __launch_bounds__(kRerollThreads) kda_reroll_kernel(RerollArgs a) {
+    const long long l = blockIdx.x / a.blocks_per_layer;
+    const long long c = (blockIdx.x % a.blocks_per_layer) * kRerollChans +
+                        static_cast<long long>(threadIdx.x) * 4;
+    if (c >= a.C) return;
+#pragma unroll
+    for (int m = 0; m < kRingRows; ++m) {
+        const int sidx = a.keep + m;
+        float4 x;
+        if (sidx < kRingRows) {
+            const float* src = a.ring_snap + (l * kRingRows + sidx) * a.C;
+            if constexpr (VEC) {
+                x = *reinterpret_cast<const float4*>(src + c);
+            } else {
+                x.x = src[c];
+                x.y = c + 1 < a.C ? src[c + 1] : 0.f;
+                x.z = c + 2 < a.C ? src[c + 2] : 0.f;
+                x.w = c + 3 < a.C ? src[c + 3] : 0.f;
+            }
+        } else {
+            const size_t off = static_cast<size_t>((l * a.T + (sidx - kRingRows)) * a.C + c);
+            if constexpr (VEC) {
+                x = load4<BF16>(a.raw, off);
+            } else {
+                x.x = load1<BF16>(a.raw, off);
+                x.y = c + 1 < a.C ? load1<BF16>(a.raw, off + 1) : 0.f;
+                x.z = c + 2 < a.C ? load1<BF16>(a.raw, off + 2) : 0.f;
+                x.w = c + 3 < a.C ? load1<BF16>(a.raw, off + 3) : 0.f;
+            }
+        }
+        float* dst = a.ring_out + (l * kRingRows + m) * a.C;
+        if constexpr (VEC) {
+            *reinterpret_cast<float4*>(dst + c) = x;
+        } else {
+            dst[c] = x.x;
+            if (c + 1 < a.C) dst[c + 1] = x.y;
+            if (c + 2 < a.C) dst[c + 2] = x.z;
+            if (c + 3 < a.C) dst[c + 3] = x.w;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ batched copy
+
+// n copies of `words` floats, driven by a device table [src_0..src_{n-1},
+// dst_0..dst_{n-1}] (memra-engine 0.123.0 glm_spec.rs, the batched GDN state
+// snapshot: one table refresh and one launch instead of a copy per layer).
+// blockIdx.y picks the buffer pair; its pointers are wave-uniform, so the
+// choice between 16-byte and 4-byte moves is made per pair at run time.
+__global__ void __launch_bounds__(256) kda_copy_batch_kernel(const uint64_t* table, int n,
+                                                             long long words) {
+    const int b = blockIdx.y;
+    const uint64_t s_raw = table[b];
+    const uint64_t d_raw = table[n + b];
+    const uint64_t s_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(s_raw)));
+    const uint64_t s_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(s_raw >> 32)));
+    const uint64_t d_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(d_raw)));
+    const uint64_t d_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(d_raw >> 32)));
+    const uint64_t sp = s_lo | (s_hi << 32);
+    const uint64_t dp = d_lo | (d_hi << 32);
+    const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
+    size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (((sp | dp) & 15) == 0 && (words & 3) == 0) {
+        const float4* s4 = reinterpret_cast<const float4*>(sp);
+        float4* d4 = reinterpret_cast<float4*>(dp);
+        const size_t n4 = static_cast<size_t>(words) / 4;
+        for (; i + 3 * stride < n4; i += 4 * stride) {
+            const float4 a0 = s4[i];
+            const float4 a1 = s4[i + stride];
+            const float4 a2 = s4[i + 2 * stride];
+            const float4 a3 = s4[i + 3 * stride];
+            d4[i] = a0;
+            d4[i + stride] = a1;
+            d4[i + 2 * stride] = a2;
+            d4[i + 3 * stride] = a3;
+        }
+        for (; i < n4; i += stride) d4[i] = s4[i];
+    } else {
+        const float* src = reinterpret_cast<const float*>(sp);
+        float* dst = reinterpret_cast<float*>(dp);
+        for (; i < static_cast<size_t>(words); i += stride) dst[i] = src[i];
+    }
+}
+
 // ------------------------------------------------------------------ greedy accept
 
 // Per verify row, the argmax of its logits -- the lowest index among equal
@@ -701,6 +798,34 @@ hipError_t launch_accept(const AcceptArgs& a, bool bf16, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     kda_accept_finish_kernel<<<dim3(1), dim3(64 * a.t), 0, stream>>>(a, P);
+    return hipGetLastError();
+}
+
+hipError_t launch_reroll(const RerollArgs& a0, bool bf16, hipStream_t stream) {
+    RerollArgs a = a0;
+    a.blocks_per_layer = (a.C + kRerollChans - 1) / kRerollChans;
+    const unsigned long long blocks = static_cast<unsigned long long>(a.L) * a.blocks_per_layer;
+    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    const int es = bf16 ? 2 : 4;
+    const bool vec = a.C % 4 == 0 && reinterpret_cast<uintptr_t>(a.ring_snap) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(a.ring_out) % 16 == 0 &&
+                     reinterpret_cast<uintptr_t>(a.raw) % (4 * es) == 0;
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if (bf16) {
+        if (vec) kda_reroll_kernel<true, true><<<grid, kRerollThreads, 0, stream>>>(a);
+        else kda_reroll_kernel<true, false><<<grid, kRerollThreads, 0, stream>>>(a);
+    } else {
+        if (vec) kda_reroll_kernel<false, true><<<grid, kRerollThreads, 0, stream>>>(a);
+        else kda_reroll_kernel<false, false><<<grid, kRerollThreads, 0, stream>>>(a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_batch(const uint64_t* table, int n, long long words, hipStream_t stream) {
+    // about 16 KiB per workgroup per pass, at most 1024 workgroups per buffer
+    const long long per = (words + 4095) / 4096;
+    const unsigned gx = static_cast<unsigned>(per < 1 ? 1 : (per > 1024 ? 1024 : per));
+    kda_copy_batch_kernel<<<dim3(gx, n), 256, 0, stream>>>(table, n, words);
     return hipGetLastError();
 }
 

@@ -59,6 +59,24 @@ hipError_t launch_scan(const ScanArgs& a, Launch kind, bool bf16, hipStream_t st
 
 hipError_t launch_copy(const float* src, float* dst, size_t n_floats, hipStream_t stream);
 
+constexpr int kRingRows = 3;   // short-conv history rows (kernel size 4)
+
+struct RerollArgs {
+    const float* ring_snap;   // [L][3][C]
+    const void* raw;          // [L][T][C] in the row dtype
+    float* ring_out;          // [L][3][C]
+    long long C;
+    long long blocks_per_layer;   // set by launch_reroll
+    int L;
+    int T;
+    int keep;
+};
+
+hipError_t launch_reroll(const RerollArgs& a, bool bf16, hipStream_t stream);
+
+// n uniform copies of `words` floats from a device table [src.., dst..].
+hipError_t launch_copy_batch(const uint64_t* table, int n, long long words, hipStream_t stream);
+
 constexpr uint32_t kNoToken = 0xFFFFFFFFu;   // argmax of a row that holds a NaN
 constexpr int kAcceptPMax = 64;              // workgroups per row, at most
 

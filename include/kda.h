@@ -52,16 +52,17 @@ extern "C" {
 #define KDA_HEAD_DIM 128   /* d_k = d_v; glm5_spec_ppn_gate.rs fixture head_dim */
 #define KDA_T_MAX 15       /* verify rows per round: K + 1 <= 15 (glm_spec.rs, WALK-REUSE) */
 #define KDA_B_MAX 15       /* batched-decode sessions per step (same knee) */
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 #define KDA_ACCEPT_WORK_BYTES 12288   /* workspace of kda_accept_greedy */
 #define KDA_NO_TOKEN 0xFFFFFFFFu      /* argmax slot of a logits row holding a NaN */
+#define KDA_CONV_RING_ROWS 3          /* short-conv history: kernel size 4 keeps 3 raw rows */
 
 enum { KDA_IN_F32 = 0, KDA_IN_BF16 = 1 };
 
 enum {
     KDA_OK = 0,
     KDA_ERR_ARG = 1,   /* null pointer or unknown dtype */
-    KDA_ERR_RANGE = 2, /* a count outside its range (T, keep, B, L, H) */
+    KDA_ERR_RANGE = 2, /* a count outside its range (T, keep, B, L, H, C, n, words) */
     KDA_ERR_ALIGN = 3, /* a pointer not 16-byte aligned */
     KDA_ERR_ALIAS = 4, /* an output overlaps an input (or another output) */
     KDA_ERR_HIP = 5    /* the HIP runtime refused a launch */
@@ -203,6 +204,41 @@ int kda_verify_round(const float* snap_prev, float* snap_out, const void* pk, co
 int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dtype,
                       const uint32_t* drafts, uint32_t* vam, uint32_t* out2, void* work,
                       void* stream);
+
+/*
+ * Conv-ring rollback.
+ *   glm_spec.rs (0.123.0), module doc VERIFY-ROW BATCHING and the
+ *   Glm5VerifyCkpt doc: a KDA layer's short-conv ring holds the last
+ *   KDA_CONV_RING_ROWS raw conv inputs (glm5_spec_ppn_gate.rs fixture:
+ *   short_conv_kernel_size 4); on a partial accept it is rebuilt from the
+ *   pre-round ring snapshot by rolling it once per kept row over the round's
+ *   retained raw rows.
+ *   ring_snap : [L][3][C] f32, the rings before the round, row 0 the oldest.
+ *   raw       : [L][T_round][C] in in_dtype, the round's raw conv inputs
+ *               (the q/k/v projections before the conv), element alignment.
+ *   ring_out  : [L][3][C] f32, receives, in row m, entry keep + m of the
+ *               sequence (ring_snap rows 0..2, raw rows 0..T_round-1).
+ *   1 <= keep <= T_round <= KDA_T_MAX, L >= 1, C >= 1.  ring_out must not
+ *   overlap ring_snap or raw.  16-byte aligned buffers with C a multiple of 4
+ *   take the vector kernel; any element-aligned layout is accepted.
+ */
+int kda_conv_reroll(const float* ring_snap, const void* raw, float* ring_out, int L,
+                    int T_round, int keep, long long C, int in_dtype, void* stream);
+
+/*
+ * Batched uniform copy: n buffers of `words` f32 each, in one launch.
+ *   glm_spec.rs (0.123.0), the batched GDN state snapshot: one pointer-table
+ *   refresh and one launch replace a copy per layer.
+ *   table : DEVICE array of 2n u64, [src_0 .. src_{n-1}, dst_0 .. dst_{n-1}],
+ *           8-byte aligned; each entry a device address of `words` f32
+ *           (4-byte aligned; pairs that are both 16-byte aligned, with words a
+ *           multiple of 4, move 16 bytes per access).
+ *   1 <= n <= 65535, words >= 1.
+ * The library cannot read the table on the host: the caller guarantees that
+ * every entry is a valid device buffer of that size and that no destination
+ * overlaps a source or another destination.
+ */
+int kda_copy_batch(const uint64_t* table, int n, long long words, void* stream);
 
 /* Message for the last nonzero status returned on the calling thread. */
 const char* kda_last_error(void);

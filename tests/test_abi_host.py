@@ -41,8 +41,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"kda_scan_rows", "kda_snapshot", "kda_replay", "kda_scan_batched",
-                          "kda_verify_round", "kda_accept_greedy", "kda_last_error",
-                          "kda_abi_version"}
+                          "kda_verify_round", "kda_accept_greedy", "kda_conv_reroll",
+                          "kda_copy_batch", "kda_last_error", "kda_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -55,6 +55,7 @@ def test_abi_version_matches_header(lib):
     assert _header_constant("KDA_ACCEPT_WORK_BYTES") == kda.ACCEPT_WORK_BYTES
     assert re.search(r"#define\s+KDA_NO_TOKEN\s+0xFFFFFFFFu", open(HEADER).read())
     assert kda.NO_TOKEN == 0xFFFFFFFF
+    assert _header_constant("KDA_CONV_RING_ROWS") == kda.RING_ROWS == 3
 
 
 class Bufs:
@@ -272,6 +273,46 @@ def test_accept_alignment_and_alias(lib, b):
     assert _accept(lib, b, out2=b["k"]) == ERR_ALIAS and "out2 overlaps drafts" in _msg(lib)
     assert _accept(lib, b, out2=off("snap", 64)) == ERR_ALIAS and "out2 overlaps work" in _msg(lib)
     assert _accept(lib, b, vam=b["v"]) == ERR_ALIAS and "vam overlaps out2" in _msg(lib)
+
+
+def _reroll(lib, b, **kw):
+    a = dict(snap=b["s_in"], raw=b["q"], out=b["s_out"], L=2, T=8, keep=3, C=1000, dt=0)
+    a.update(kw)
+    return lib.kda_conv_reroll(a["snap"], a["raw"], a["out"], a["L"], a["T"], a["keep"], a["C"],
+                               a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(keep=0), ERR_RANGE, "keep=0"),
+    (dict(keep=9), ERR_RANGE, "keep=9"),
+    (dict(T=0, keep=1), ERR_RANGE, "T_round=0"),
+    (dict(T=16, keep=1), ERR_RANGE, "T_round=16"),
+    (dict(L=0), ERR_RANGE, "L=0"),
+    (dict(C=0), ERR_RANGE, "C=0"),
+    (dict(dt=5), ERR_ARG, "in_dtype"),
+    (dict(snap=None), ERR_ARG, "ring_snap is NULL"),
+    (dict(raw=None), ERR_ARG, "raw is NULL"),
+    (dict(out=None), ERR_ARG, "ring_out is NULL"),
+])
+def test_conv_reroll_refusals(lib, b, kw, code, needle):
+    assert _reroll(lib, b, **kw) == code
+    assert needle in _msg(lib)
+
+
+def test_conv_reroll_alignment_and_alias(lib, b):
+    off = lambda n, k: ctypes.c_void_p(b.addr[n] + k)
+    assert _reroll(lib, b, snap=off("s_in", 2)) == ERR_ALIGN and "ring_snap is not 4" in _msg(lib)
+    assert _reroll(lib, b, raw=off("q", 1), dt=1) == ERR_ALIGN and "raw is not 2" in _msg(lib)
+    assert _reroll(lib, b, out=off("s_in", 4)) == ERR_ALIAS and "ring_out overlaps ring_snap" in _msg(lib)
+    assert _reroll(lib, b, out=off("q", 400)) == ERR_ALIAS and "ring_out overlaps raw" in _msg(lib)
+
+
+def test_copy_batch_refusals(lib, b):
+    assert lib.kda_copy_batch(b["ptrs"], 0, 100, None) == ERR_RANGE and "n=0" in _msg(lib)
+    assert lib.kda_copy_batch(b["ptrs"], 65536, 100, None) == ERR_RANGE
+    assert lib.kda_copy_batch(b["ptrs"], 2, 0, None) == ERR_RANGE and "words=0" in _msg(lib)
+    assert lib.kda_copy_batch(None, 2, 100, None) == ERR_ARG and "table is NULL" in _msg(lib)
+    assert lib.kda_copy_batch(ctypes.c_void_p(b.addr["ptrs"] + 4), 2, 100, None) == ERR_ALIGN
 
 
 def test_snapshot_refusals(lib, b):
