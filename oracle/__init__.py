@@ -68,6 +68,8 @@ def load():
     lib.kda_oracle_accept_greedy.restype = i
     lib.kda_oracle_conv_reroll.argtypes = [p, p, p, i, i, i, ctypes.c_long, i]
     lib.kda_oracle_conv_reroll.restype = i
+    lib.kda_oracle_row_ops.argtypes = [p] * 11 + [i, i, i, i, i]
+    lib.kda_oracle_row_ops.restype = i
     lib.kda_oracle_version.restype = i
     lib.kda_oracle_max_threads.restype = i
     _lib = lib
@@ -196,6 +198,39 @@ def conv_reroll(ring_snap, raw, keep):
     out = np.empty_like(rs)
     if lib.kda_oracle_conv_reroll(_ptr(rs), _ptr(rw), _ptr(out), L, T, int(keep), C, bf16) != 0:
         raise ValueError("bad conv_reroll arguments")
+    return out
+
+
+def row_ops(x, a, b, w, ring_in, H, d=128, want_ring=True):
+    """Pre-scan row ops of one round.  x [L][T][3*H*d], a [L][T][H*d], b [L][T][H]
+    (float32, or uint16 bf16 bits, all alike), w [L][3*H*d][4] f32, ring_in
+    [L][3][3*H*d] f32.  Returns dict q, k, v, g [L][T][H][d], beta [L][T][H] (f32)
+    and ring (the ring after all T rows, or None)."""
+    lib = load()
+    xs = [np.ascontiguousarray(z) for z in (x, a, b)]
+    if all(z.dtype == np.float32 for z in xs):
+        bf16 = 0
+    elif all(z.dtype == np.uint16 for z in xs):
+        bf16 = 1
+    else:
+        raise TypeError("x, a, b must all be float32 or all uint16 (bf16 bits)")
+    L, T, C = xs[0].shape
+    if C != 3 * H * d or xs[1].shape != (L, T, H * d) or xs[2].shape != (L, T, H):
+        raise ValueError("row-op input shapes do not match H, d")
+    wc = np.ascontiguousarray(w, np.float32)
+    rc = np.ascontiguousarray(ring_in, np.float32)
+    if wc.shape != (L, C, 4) or rc.shape != (L, RING_ROWS, C):
+        raise ValueError("w must be [L][3*H*d][4] and ring_in [L][3][3*H*d]")
+    out = {n: np.empty((L, T, H, d), np.float32) for n in ("q", "k", "v", "g")}
+    out["beta"] = np.empty((L, T, H), np.float32)
+    ring = np.empty_like(rc) if want_ring else None
+    rcode = lib.kda_oracle_row_ops(_ptr(xs[0]), _ptr(xs[1]), _ptr(xs[2]), _ptr(wc), _ptr(rc),
+                                   _ptr(ring) if want_ring else None, _ptr(out["q"]),
+                                   _ptr(out["k"]), _ptr(out["v"]), _ptr(out["g"]),
+                                   _ptr(out["beta"]), L, T, H, d, bf16)
+    if rcode != 0:
+        raise ValueError("bad row_ops arguments")
+    out["ring"] = ring
     return out
 
 

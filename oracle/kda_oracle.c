@@ -336,3 +336,85 @@ int kda_oracle_conv_reroll(const float* ring_snap, const void* raw, float* ring_
     }
     return 0;
 }
+
+/*
+ * Pre-scan row ops of one verify round (glm_spec.rs, 0.123.0, module doc
+ * VERIFY-ROW BATCHING: projections, gates and the short conv of one KDA layer
+ * run batched over the t = K+1 rows; glm5_spec_ppn_gate.rs fixture:
+ * short_conv_kernel_size 4, gate_lower_bound -5.0).  The pages fix those two
+ * numbers and the order; the rest is the plain reading:
+ *   conv  : per channel c of the 3*H*d raw q/k/v channels, causal over the
+ *           sequence (3 ring rows, then the round's rows):
+ *           y_t[c] = sum_{m=0..3} w[c][m] x_{t-3+m}[c], no bias, then SiLU
+ *           y * sigmoid(y);
+ *   q, k  : per (row, head) L2-normalised over d: x / sqrt(sum x^2 + 1e-6);
+ *   v     : the conv output;
+ *   g     : max(-softplus(a), -5), the log-decay with the fixture's bound;
+ *   beta  : sigmoid(b).
+ * Layouts: x [L][T][3*H*d] (q, k, v channel blocks of H*d), a [L][T][H*d],
+ * b [L][T][H], w [L][3*H*d][4] f32, ring_in/ring_out [L][3][3*H*d] f32 (row 0
+ * the oldest; ring_out = the ring after all T rows, may be NULL); outputs
+ * q, k, v, g [L][T][H][d] and beta [L][T][H], f32.  f64 inside, f32 out.
+ */
+#define ORACLE_NORM_EPS 1e-6
+#define ORACLE_CONV_TAPS 4
+
+static double silu(double y) { return y / (1.0 + exp(-y)); }
+
+static double softplus(double a) { return a > 0 ? a + log1p(exp(-a)) : log1p(exp(a)); }
+
+int kda_oracle_row_ops(const void* x, const void* a, const void* b, const float* w,
+                       const float* ring_in, float* ring_out, float* q, float* k, float* v,
+                       float* g, float* beta, int L, int T, int H, int d, int in_bf16) {
+    if (L < 1 || T < 1 || H < 1 || d < 1) return -1;
+    const long HD = (long)H * d, C = 3 * HD;
+    double* ring = malloc(sizeof(double) * ORACLE_RING_ROWS * C);
+    double* y = malloc(sizeof(double) * C);
+    if (!ring || !y) { free(ring); free(y); return -2; }
+    for (long l = 0; l < L; ++l) {
+        for (long i = 0; i < ORACLE_RING_ROWS * C; ++i) ring[i] = ring_in[l * ORACLE_RING_ROWS * C + i];
+        const float* wl = w + l * C * ORACLE_CONV_TAPS;
+        for (long t = 0; t < T; ++t) {
+            const long xr = (l * T + t) * C;
+            /* causal conv over (ring rows 0..2, this row), then SiLU */
+            for (long c = 0; c < C; ++c) {
+                const double xt = fetch(x, xr + c, in_bf16);
+                double acc = 0.0;
+                for (int m = 0; m < ORACLE_RING_ROWS; ++m)
+                    acc += (double)wl[c * ORACLE_CONV_TAPS + m] * ring[m * C + c];
+                acc += (double)wl[c * ORACLE_CONV_TAPS + ORACLE_RING_ROWS] * xt;
+                y[c] = silu(acc);
+            }
+            /* the ring rolls by this row's raw input */
+            for (int m = 0; m + 1 < ORACLE_RING_ROWS; ++m)
+                for (long c = 0; c < C; ++c) ring[m * C + c] = ring[(m + 1) * C + c];
+            for (long c = 0; c < C; ++c) ring[(ORACLE_RING_ROWS - 1) * C + c] = fetch(x, xr + c, in_bf16);
+            for (long h = 0; h < H; ++h) {
+                const long o = ((l * T + t) * H + h) * d;
+                double sq = 0.0, sk = 0.0;
+                for (long j = 0; j < d; ++j) {
+                    sq += y[h * d + j] * y[h * d + j];
+                    sk += y[HD + h * d + j] * y[HD + h * d + j];
+                }
+                const double nq = 1.0 / sqrt(sq + ORACLE_NORM_EPS);
+                const double nk = 1.0 / sqrt(sk + ORACLE_NORM_EPS);
+                for (long j = 0; j < d; ++j) {
+                    q[o + j] = (float)(y[h * d + j] * nq);
+                    k[o + j] = (float)(y[HD + h * d + j] * nk);
+                    v[o + j] = (float)y[2 * HD + h * d + j];
+                    double gg = -softplus(fetch(a, (l * T + t) * HD + h * d + j, in_bf16));
+                    if (gg < ORACLE_GATE_LO) gg = ORACLE_GATE_LO;
+                    g[o + j] = (float)gg;
+                }
+                beta[(l * T + t) * H + h] =
+                    (float)(1.0 / (1.0 + exp(-(double)fetch(b, (l * T + t) * H + h, in_bf16))));
+            }
+        }
+        if (ring_out)
+            for (long i = 0; i < ORACLE_RING_ROWS * C; ++i)
+                ring_out[l * ORACLE_RING_ROWS * C + i] = (float)ring[i];
+    }
+    free(ring);
+    free(y);
+    return 0;
+}

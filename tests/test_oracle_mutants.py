@@ -44,6 +44,18 @@ MUTANTS = [
      "fetch(raw, (l * T_round + (r > 0 ? r - 1 : 0)) * C + c, in_bf16)"),
     ("ring ignores the layer", "fetch(raw, (l * T_round + r) * C + c, in_bf16)",
      "fetch(raw, (long)r * C + c, in_bf16)"),
+    ("conv without SiLU", "y[c] = silu(acc);", "y[c] = acc;"),
+    ("conv taps reversed", "(double)wl[c * ORACLE_CONV_TAPS + m] * ring[m * C + c]",
+     "(double)wl[c * ORACLE_CONV_TAPS + (ORACLE_RING_ROWS - m)] * ring[m * C + c]"),
+    ("conv ring not rolled", "for (long c = 0; c < C; ++c) ring[m * C + c] = ring[(m + 1) * C + c];",
+     ""),
+    ("norm without epsilon", "1.0 / sqrt(sq + ORACLE_NORM_EPS)", "1.0 / sqrt(sq)"),
+    ("q and k blocks swapped", "q[o + j] = (float)(y[h * d + j] * nq);",
+     "q[o + j] = (float)(y[HD + h * d + j] * nq);"),
+    ("gate bound missing", "if (gg < ORACLE_GATE_LO) gg = ORACLE_GATE_LO;", ""),
+    ("gate sign", "double gg = -softplus(", "double gg = softplus("),
+    ("beta without sigmoid", "(float)(1.0 / (1.0 + exp(-(double)fetch(b, (l * T + t) * H + h, in_bf16))));",
+     "(float)fetch(b, (l * T + t) * H + h, in_bf16);"),
 ]
 
 PIN_TESTS = [
@@ -62,6 +74,11 @@ PIN_TESTS = [
     lambda: [pins.test_reroll_is_the_last_three_rows_of_snapshot_then_kept_rows(k)
              for k in (1, 2, 4)],
     lambda: pins.test_reroll_composes_and_keeps_layers_apart(),
+    lambda: pins.test_row_ops_identity_taps_give_silu_closed_forms(),
+    lambda: pins.test_row_ops_taps_reach_back_through_the_ring(),
+    lambda: pins.test_row_ops_norms_gate_and_beta_closed_forms(),
+    lambda: pins.test_row_ops_split_rounds_chain_through_the_ring(),
+    lambda: pins.test_row_ops_channels_heads_and_layers_stay_apart(),
 ]
 
 
@@ -81,7 +98,8 @@ def _swap_in(path):
     lib = ctypes.CDLL(path)
     real = oracle.load()
     for fn in ("kda_oracle_scan_rows", "kda_oracle_batched", "kda_oracle_version",
-               "kda_oracle_max_threads", "kda_oracle_accept_greedy", "kda_oracle_conv_reroll"):
+               "kda_oracle_max_threads", "kda_oracle_accept_greedy", "kda_oracle_conv_reroll",
+               "kda_oracle_row_ops"):
         getattr(lib, fn).argtypes = getattr(real, fn).argtypes
         getattr(lib, fn).restype = getattr(real, fn).restype
     return lib

@@ -436,3 +436,128 @@ def test_reroll_bf16_rows_widen_exactly():
         oracle.conv_reroll(snap, raw, 0)
     with pytest.raises(ValueError):
         oracle.conv_reroll(snap, raw, 7)
+
+
+# ---------------------------------------------------------------- pre-scan row ops
+
+LN3 = float(np.log(3.0))
+
+
+def _ops_inputs(L, T, H, d, seed=0, taps=None):
+    rng = np.random.default_rng(seed)
+    C = 3 * H * d
+    x = rng.standard_normal((L, T, C)).astype(np.float32)
+    a = rng.standard_normal((L, T, H * d)).astype(np.float32)
+    b = rng.standard_normal((L, T, H)).astype(np.float32)
+    if taps is None:
+        w = rng.uniform(-0.6, 0.6, (L, C, 4)).astype(np.float32)
+    else:
+        w = np.broadcast_to(np.asarray(taps, np.float32), (L, C, 4)).copy()
+    ring = rng.standard_normal((L, 3, C)).astype(np.float32)
+    return x, a, b, w, ring
+
+
+def test_row_ops_identity_taps_give_silu_closed_forms():
+    # taps (0,0,0,1): the conv passes the current row, so v = SiLU(x);
+    # SiLU(0) = 0, SiLU(ln 3) = (3/4) ln 3, SiLU(-ln 3) = -(1/4) ln 3
+    L, T, H, d = 1, 2, 2, 4
+    x, a, b, w, ring = _ops_inputs(L, T, H, d, taps=(0, 0, 0, 1))
+    HD = H * d
+    x[0, 0, 2 * HD:] = [0, LN3, -LN3, 0, LN3, LN3, 0, -LN3]
+    out = oracle.row_ops(x, a, b, w, ring, H, d)
+    want = np.array([0, 0.75 * LN3, -0.25 * LN3, 0, 0.75 * LN3, 0.75 * LN3, 0, -0.25 * LN3])
+    np.testing.assert_allclose(out["v"][0, 0].reshape(-1), want, rtol=1e-6, atol=1e-7)
+
+
+def test_row_ops_taps_reach_back_through_the_ring():
+    # taps (1,0,0,0): row t sees the raw input three rows earlier, from the
+    # ring for t < 3 and from the round's own rows after that
+    L, T, H, d = 1, 5, 1, 4
+    x, a, b, w, ring = _ops_inputs(L, T, H, d, taps=(1, 0, 0, 0))
+    v0 = 2 * H * d
+    ring[0, :, v0:] = 0.0
+    ring[0, 0, v0] = LN3         # oldest ring row -> output row 0
+    ring[0, 2, v0 + 1] = -LN3    # newest ring row -> output row 2
+    x[0, :, v0:] = 0.0
+    x[0, 0, v0 + 2] = LN3        # round row 0 -> output row 3
+    x[0, 1, v0 + 3] = LN3        # round row 1 -> output row 4
+    out = oracle.row_ops(x, a, b, w, ring, H, d)
+    v = out["v"][0, :, 0, :]
+    want = np.zeros((5, 4))
+    want[0, 0] = 0.75 * LN3
+    want[2, 1] = -0.25 * LN3
+    want[3, 2] = 0.75 * LN3
+    want[4, 3] = 0.75 * LN3
+    np.testing.assert_allclose(v, want, rtol=1e-6, atol=1e-7)
+
+
+def test_row_ops_norms_gate_and_beta_closed_forms():
+    L, T, H, d = 1, 1, 3, 4
+    x, a, b, w, ring = _ops_inputs(L, T, H, d, taps=(0, 0, 0, 1))
+    HD = H * d
+    x[0, 0, :2 * HD] = 0.0
+    x[0, 0, 0] = LN3             # q head 0 = SiLU(ln 3) e_0 -> unit vector e_0
+    x[0, 0, HD + 4 + 1] = 1.0    # k head 1 = SiLU(1) e_1 -> e_1
+    a[0, 0, :] = 0.0             # softplus(0) = ln 2
+    a[0, 0, 4] = 10.0            # -softplus(10) < -5: the bound
+    a[0, 0, 5] = float(np.log(np.e ** 2 - 1))   # softplus = 2
+    a[0, 0, 6] = -20.0           # ~ -2.06e-9
+    b[0, 0, :] = [0.0, LN3, -LN3]
+    out = oracle.row_ops(x, a, b, w, ring, H, d)
+    q, k, g = out["q"][0, 0], out["k"][0, 0], out["g"][0, 0]
+    # unit vectors up to the 1e-6 under the square root; zero rows stay zero
+    np.testing.assert_allclose(q[0], [1, 0, 0, 0], atol=2e-6)
+    np.testing.assert_array_equal(q[1], 0)
+    np.testing.assert_allclose(k[1], [0, 1, 0, 0], atol=2e-6)
+    np.testing.assert_array_equal(k[0], 0)
+    assert g[0, 0] == np.float32(-np.log(2.0))
+    assert g[1, 0] == -5.0 and g[1, 1] == np.float32(-2.0)
+    np.testing.assert_allclose(g[1, 2], -np.exp(-20.0), rtol=1e-6)
+    np.testing.assert_allclose(out["beta"][0, 0], [0.5, 0.75, 0.25], rtol=1e-7)
+    # normalised rows have unit length whatever the conv produced
+    x2, a2, b2, w2, r2 = _ops_inputs(2, 3, 2, 8, seed=4)
+    o2 = oracle.row_ops(x2, a2, b2, w2, r2, 2, 8)
+    for n in ("q", "k"):
+        np.testing.assert_allclose(np.linalg.norm(o2[n], axis=-1), 1.0, rtol=1e-5)
+
+
+def test_row_ops_split_rounds_chain_through_the_ring():
+    # causality: rows 0..2 then rows 3..5 (ring carried) equal rows 0..5;
+    # the ring after the round is the conv-ring roll of all T rows
+    L, T, H, d = 2, 6, 2, 8
+    x, a, b, w, ring = _ops_inputs(L, T, H, d, seed=9)
+    full = oracle.row_ops(x, a, b, w, ring, H, d)
+    first = oracle.row_ops(x[:, :3].copy(), a[:, :3].copy(), b[:, :3].copy(), w, ring, H, d)
+    second = oracle.row_ops(x[:, 3:].copy(), a[:, 3:].copy(), b[:, 3:].copy(), w,
+                            first["ring"], H, d)
+    for n in ("q", "k", "v", "g", "beta"):
+        np.testing.assert_array_equal(np.concatenate([first[n], second[n]], axis=1), full[n])
+    np.testing.assert_array_equal(full["ring"], oracle.conv_reroll(ring, x, T))
+
+
+def test_row_ops_channels_heads_and_layers_stay_apart():
+    L, T, H, d = 2, 3, 3, 8
+    x, a, b, w, ring = _ops_inputs(L, T, H, d, seed=12)
+    base = oracle.row_ops(x, a, b, w, ring, H, d)
+    HD = H * d
+    x2 = x.copy()
+    x2[1, 1, HD + 2 * d + 3] += 1.0   # layer 1, row 1, a k channel of head 2
+    o = oracle.row_ops(x2, a, b, w, ring, H, d)
+    changed = {n: np.argwhere(o[n] != base[n]) for n in ("q", "k", "v", "g", "beta")}
+    assert changed["q"].size == 0 and changed["v"].size == 0 and changed["g"].size == 0
+    assert changed["beta"].size == 0
+    # the raw input of row 1 also reaches rows 2.. through the causal conv
+    ks = set(map(tuple, changed["k"][:, :3]))
+    assert ks == {(1, 1, 2), (1, 2, 2)}
+
+
+def test_row_ops_bf16_inputs_widen_exactly():
+    from gated_delta_rule_rows_amd import synth
+    L, T, H, d = 1, 4, 2, 8
+    x, a, b, w, ring = _ops_inputs(L, T, H, d, seed=15)
+    bits = [synth.to_bf16_bits(z) for z in (x, a, b)]
+    wide = [(z.astype(np.uint32) << 16).view(np.float32) for z in bits]
+    o1 = oracle.row_ops(*bits, w, ring, H, d)
+    o2 = oracle.row_ops(*wide, w, ring, H, d)
+    for n in ("q", "k", "v", "g", "beta", "ring"):
+        np.testing.assert_array_equal(o1[n], o2[n])
