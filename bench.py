@@ -19,7 +19,8 @@ Two pipelines of the same round are timed in one run:
 Also timed: kda_accept_greedy over one round's logits (t = 15, V = 150,000,
 f32), the greedy accept that decides j on the device; kda_conv_reroll of the
 34 layers' short-conv rings; kda_copy_batch of 34 separately allocated layer
-states in one launch.
+states in one launch; kda_row_ops turning one round's projections into scan
+inputs.
 
 Prints ONE JSON line.  `value` is verify rows x heads x layers per second of
 the fused pipeline (T rows counted per round).  `roofline` covers its
@@ -384,6 +385,18 @@ def main() -> int:
 
         rr_us = time_b2b(lambda: kda.kda_conv_reroll(ring_snap, raw, 8, ring_out),
                          args.copy_launches)
+        # pre-scan row ops of one round: projections -> this round's scan inputs
+        ops_a = torch.randn(L, T, H * D, device="cuda")
+        ops_b = torch.randn(L, T, H, device="cuda")
+        ops_w = torch.rand(L, C, 4, device="cuda") - 0.5
+        ops_out = [torch.empty(L, T, H, D, device="cuda") for _ in range(4)]
+        ops_beta = torch.empty(L, T, H, device="cuda")
+        ops_us = time_b2b(lambda: kda.kda_row_ops(raw, ops_a, ops_b, ops_w, ring_snap, *ops_out,
+                                                  ops_beta, ring_out=ring_out),
+                          args.copy_launches)
+        ops_bytes = 4 * (L * T * C + L * T * H * D + L * T * H + L * C * 4 + 2 * L * 3 * C
+                         + 4 * L * T * H * D + L * T * H)
+        del ops_a, ops_b, ops_w, ops_out, ops_beta
         cb_us = time_b2b(lambda: kda.kda_copy_batch(table, L, H * D * D), args.copy_launches)
         rr_bytes = 2 * L * 3 * C * 4
         cb_bytes = 2 * L * H * D * D * 4
@@ -392,6 +405,8 @@ def main() -> int:
                             "gbps": rr_bytes / (rr_us * 1e-6) / 1e9},
             "copy_batch_34_states": {"us": cb_us, "bytes": cb_bytes,
                                      "gbps": cb_bytes / (cb_us * 1e-6) / 1e9},
+            "row_ops": {"T": T, "us": ops_us, "bytes": ops_bytes,
+                        "gbps": ops_bytes / (ops_us * 1e-6) / 1e9},
         }
         del ring_snap, raw, ring_out, dsts, table
 

@@ -16,6 +16,8 @@ Shapes (D = 128):
                    writes and a replay (or the next fused round) reads
   batched arm      rows [L][B][H][D], beta [L][B][H], o [L][B][H][D];
                    s_ptrs = state_table(...) -> int64 device tensor [L*B]
+  row ops          x [L][T][3*H*D], a [L][T][H*D], b [L][T][H] (float32 or
+                   bfloat16), conv_w [L][3*H*D][4], ring [L][3][3*H*D] float32
   conv ring        ring [L][3][C] float32, raw conv input rows [L][T][C]
   batched copy     table = copy_table(srcs, dsts) -> int64 device tensor [2n]
   greedy accept    logits [t][V] (row stride free, elements contiguous),
@@ -73,9 +75,10 @@ def load():
     lib.kda_accept_greedy.argtypes = [p, i, i, ctypes.c_longlong, i, p, p, p, p, p]
     lib.kda_conv_reroll.argtypes = [p, p, p, i, i, i, ctypes.c_longlong, i, p]
     lib.kda_copy_batch.argtypes = [p, i, ctypes.c_longlong, p]
+    lib.kda_row_ops.argtypes = [p] * 11 + [i, i, i, i, p]
     for fn in (lib.kda_scan_rows, lib.kda_snapshot, lib.kda_replay, lib.kda_scan_batched,
                lib.kda_verify_round, lib.kda_accept_greedy, lib.kda_conv_reroll,
-               lib.kda_copy_batch, lib.kda_abi_version):
+               lib.kda_copy_batch, lib.kda_row_ops, lib.kda_abi_version):
         fn.restype = i
     lib.kda_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -339,6 +342,31 @@ def kda_accept_greedy(logits, drafts, vam, out2, work, stream=None) -> None:
                                  _dev(out2, "out2"), _dev(work, "work"), _stream(stream)))
 
 
+def kda_row_ops(x, a, b, conv_w, ring_in, q, k, v, g, beta, ring_out=None, stream=None) -> None:
+    """Scan inputs from one round's projections: causal short conv + SiLU over the
+    ring, q/k L2 norm, bounded gate, beta sigmoid (see include/kda.h).  ring_out
+    (optional, may be ring_in) receives the ring after all T rows."""
+    lib = load()
+    if x.dim() != 3 or x.shape[2] % (3 * D) != 0:
+        raise ValueError(f"x must be [L][T][3*H*{D}], got {tuple(x.shape)}")
+    L, T, C = x.shape
+    H = C // (3 * D)
+    _shape(a, (L, T, H * D), "a")
+    _shape(b, (L, T, H), "b")
+    _state(conv_w, (L, C, 4), "conv_w")
+    _state(ring_in, (L, RING_ROWS, C), "ring_in")
+    if ring_out is not None:
+        _state(ring_out, (L, RING_ROWS, C), "ring_out")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (g, "g")):
+        _state(t, (L, T, H, D), n)
+    _state(beta, (L, T, H), "beta")
+    dt = _in_dtype((x, a, b))
+    _check(lib.kda_row_ops(_dev(x, "x"), _dev(a, "a"), _dev(b, "b"), _dev(conv_w, "conv_w"),
+                           _dev(ring_in, "ring_in"), _dev(ring_out, "ring_out"), _dev(q, "q"),
+                           _dev(k, "k"), _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"),
+                           L, T, H, dt, _stream(stream)))
+
+
 def kda_conv_reroll(ring_snap, raw, keep: int, ring_out, stream=None) -> None:
     """ring_out = the short-conv ring after `keep` accepted rows: ring_snap [L][3][C]
     rolled once per kept row over the round's raw conv inputs raw [L][T_round][C]."""
@@ -390,5 +418,5 @@ __all__ = [
     "D", "T_MAX", "B_MAX", "KdaError", "load", "lib_path", "kda_scan_rows", "kda_snapshot",
     "kda_replay", "kda_scan_batched", "kda_verify_round", "state_table", "kda_abi_version",
     "kda_last_error", "kda_accept_greedy", "accept_workspace", "ACCEPT_WORK_BYTES", "NO_TOKEN",
-    "kda_conv_reroll", "copy_table", "kda_copy_batch", "RING_ROWS",
+    "kda_conv_reroll", "copy_table", "kda_copy_batch", "RING_ROWS", "kda_row_ops",
 ]

@@ -328,6 +328,43 @@ int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dty
                                            static_cast<hipStream_t>(stream)));
 }
 
+int kda_row_ops(const void* x, const void* a, const void* b, const float* conv_w,
+                const float* ring_in, float* ring_out, float* q, float* k, float* v, float* g,
+                float* beta, int L, int T, int H, int in_dtype, void* stream) {
+    const char* fn = "kda_row_ops";
+    int rc;
+    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H)) ||
+        (rc = check_rows(fn, "T", T)))
+        return rc;
+    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
+    const unsigned long long LH = static_cast<unsigned long long>(L) * H;
+    const unsigned long long chans = LH * kda::kD;          // per row, all layers
+    const unsigned long long ring = 3ull * KDA_CONV_RING_ROWS * chans * 4;
+    const Span in[] = {
+        {"x", x, 3 * chans * T * es, es, false},
+        {"a", a, chans * T * es, es, false},
+        {"b", b, LH * T * es, es, false},
+        {"conv_w", conv_w, 3 * chans * 4 * 4, 16, false},
+        {"ring_in", ring_in, ring, 4, false},
+    };
+    const Span out[] = {
+        {"ring_out", ring_out, ring, 4, true},
+        {"q", q, chans * T * 4, 16, false},
+        {"k", k, chans * T * 4, 16, false},
+        {"v", v, chans * T * 4, 16, false},
+        {"g", g, chans * T * 4, 16, false},
+        {"beta", beta, LH * T * 4, 4, false},
+    };
+    if ((rc = check_spans(fn, in, 5)) || (rc = check_spans(fn, out, 6)) ||
+        (rc = check_alias(fn, out, 6, in, 5, &out[0], &in[4])))
+        return rc;
+    kda::RowOpsArgs r{};
+    r.x = x; r.a = a; r.b = b; r.w = conv_w; r.ring_in = ring_in; r.ring_out = ring_out;
+    r.q = q; r.k = k; r.v = v; r.g = g; r.beta = beta; r.L = L; r.T = T; r.H = H;
+    return launched(fn, kda::launch_row_ops(r, in_dtype == KDA_IN_BF16,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int kda_conv_reroll(const float* ring_snap, const void* raw, float* ring_out, int L,
                     int T_round, int keep, long long C, int in_dtype, void* stream) {
     const char* fn = "kda_conv_reroll";

@@ -552,6 +552,120 @@ __global__ void __launch_bounds__(kRerollThreads) kda_reroll_kernel(RerollArgs a
     }
 }
 
+// ------------------------------------------------------------------ pre-scan row ops
+
+// The per-row ops that turn one layer's projections into scan inputs for the
+// t = K+1 verify rows (memra-engine 0.123.0 glm_spec.rs, module doc
+// VERIFY-ROW BATCHING: gates and conv batched over the rows;
+// glm5_spec_ppn_gate.rs fixture: short conv kernel 4, gate bound -5):
+//   q, k, v : causal depthwise conv over (3 ring rows, the round's rows),
+//             taps w[c][0..3] oldest first, then SiLU; q and k L2-normalised
+//             per (row, head) with 1e-6 under the square root;
+//   g       : max(-softplus(a), -5);     beta : sigmoid(b).
+// One workgroup per (layer, head), one lane per head channel (q, k, v and g
+// of that channel); every row's loads are issued before any arithmetic.
+constexpr int kOpsThreads = kD;   // 2 waves
+constexpr float kNormEps = 1e-6f;
+
+__device__ __forceinline__ float silu_f(float y) { return y / (1.0f + __expf(-y)); }
+
+__device__ __forceinline__ float softplus_f(float a) {
+    return a > 0.0f ? a + log1pf(__expf(-a)) : log1pf(__expf(a));
+}
+
+template <bool BF16>
+__global__ void __launch_bounds__(kOpsThreads) kda_row_ops_kernel(RowOpsArgs a) {
+    const int j = threadIdx.x;
+    const int wave = j >> 6;
+    const long long l = blockIdx.x / a.H;
+    const long long h = blockIdx.x % a.H;
+    const long long HD = static_cast<long long>(a.H) * kD;
+    const long long C = 3 * HD;
+    const int T = a.T;
+    // this lane's q, k, v channels
+    const long long cq = h * kD + j, ck = HD + cq, cv = 2 * HD + cq;
+
+    float xq[kTMax], xk[kTMax], xv[kTMax], xa[kTMax];
+#pragma unroll
+    for (int t = 0; t < kTMax; ++t) {
+        if (t < T) {
+            const size_t r = static_cast<size_t>((l * T + t) * C);
+            const size_t ra = static_cast<size_t>((l * T + t) * HD);
+            xq[t] = load1<BF16>(a.x, r + cq);
+            xk[t] = load1<BF16>(a.x, r + ck);
+            xv[t] = load1<BF16>(a.x, r + cv);
+            xa[t] = load1<BF16>(a.a, ra + cq);
+        }
+    }
+    const float4 wq = *reinterpret_cast<const float4*>(a.w + (l * C + cq) * 4);
+    const float4 wk = *reinterpret_cast<const float4*>(a.w + (l * C + ck) * 4);
+    const float4 wv = *reinterpret_cast<const float4*>(a.w + (l * C + cv) * 4);
+    const float* ring = a.ring_in + l * kRingRows * C;
+    float rq0 = ring[cq], rq1 = ring[C + cq], rq2 = ring[2 * C + cq];
+    float rk0 = ring[ck], rk1 = ring[C + ck], rk2 = ring[2 * C + ck];
+    float rv0 = ring[cv], rv1 = ring[C + cv], rv2 = ring[2 * C + cv];
+    float bt = 0.0f;
+    if (j < T) bt = load1<BF16>(a.b, static_cast<size_t>((l * T + j) * a.H + h));
+
+    // conv + SiLU per row; the ring rolls in registers
+    __shared__ float part[kTMax][2][2];   // [row][wave][q, k] partial sums of squares
+    float yq[kTMax], yk[kTMax];
+#pragma unroll
+    for (int t = 0; t < kTMax; ++t) {
+        if (t < T) {
+            float cqv = wq.x * rq0;
+            cqv = fmaf(wq.y, rq1, cqv);
+            cqv = fmaf(wq.z, rq2, cqv);
+            cqv = fmaf(wq.w, xq[t], cqv);
+            float ckv = wk.x * rk0;
+            ckv = fmaf(wk.y, rk1, ckv);
+            ckv = fmaf(wk.z, rk2, ckv);
+            ckv = fmaf(wk.w, xk[t], ckv);
+            float cvv = wv.x * rv0;
+            cvv = fmaf(wv.y, rv1, cvv);
+            cvv = fmaf(wv.z, rv2, cvv);
+            cvv = fmaf(wv.w, xv[t], cvv);
+            rq0 = rq1; rq1 = rq2; rq2 = xq[t];
+            rk0 = rk1; rk1 = rk2; rk2 = xk[t];
+            rv0 = rv1; rv1 = rv2; rv2 = xv[t];
+            yq[t] = silu_f(cqv);
+            yk[t] = silu_f(ckv);
+            const size_t o = static_cast<size_t>(((l * T + t) * a.H + h) * kD + j);
+            a.v[o] = silu_f(cvv);
+            a.g[o] = fmaxf(-softplus_f(xa[t]), kGateLo);
+            float sq = yq[t] * yq[t];
+            float sk = yk[t] * yk[t];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                sq += __shfl_xor(sq, off);
+                sk += __shfl_xor(sk, off);
+            }
+            if ((j & 63) == 0) {
+                part[t][wave][0] = sq;
+                part[t][wave][1] = sk;
+            }
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < kTMax; ++t) {
+        if (t < T) {
+            const float nq = 1.0f / sqrtf(part[t][0][0] + part[t][1][0] + kNormEps);
+            const float nk = 1.0f / sqrtf(part[t][0][1] + part[t][1][1] + kNormEps);
+            const size_t o = static_cast<size_t>(((l * T + t) * a.H + h) * kD + j);
+            a.q[o] = yq[t] * nq;
+            a.k[o] = yk[t] * nk;
+        }
+    }
+    if (j < T) a.beta[(l * T + j) * a.H + h] = 1.0f / (1.0f + __expf(-bt));
+    if (a.ring_out) {
+        float* ro = a.ring_out + l * kRingRows * C;
+        ro[cq] = rq0; ro[C + cq] = rq1; ro[2 * C + cq] = rq2;
+        ro[ck] = rk0; ro[C + ck] = rk1; ro[2 * C + ck] = rk2;
+        ro[cv] = rv0; ro[C + cv] = rv1; ro[2 * C + cv] = rv2;
+    }
+}
+
 // ------------------------------------------------------------------ batched copy
 
 // n copies of `words` floats, driven by a device table [src_0..src_{n-1},
@@ -818,6 +932,16 @@ hipError_t launch_reroll(const RerollArgs& a0, bool bf16, hipStream_t stream) {
         if (vec) kda_reroll_kernel<false, true><<<grid, kRerollThreads, 0, stream>>>(a);
         else kda_reroll_kernel<false, false><<<grid, kRerollThreads, 0, stream>>>(a);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_row_ops(const RowOpsArgs& a, bool bf16, hipStream_t stream) {
+    const unsigned long long blocks = static_cast<unsigned long long>(a.L) * a.H;
+    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    if (bf16)
+        kda_row_ops_kernel<true><<<dim3(static_cast<unsigned>(blocks)), kOpsThreads, 0, stream>>>(a);
+    else
+        kda_row_ops_kernel<false><<<dim3(static_cast<unsigned>(blocks)), kOpsThreads, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -74,6 +74,25 @@ struct RerollArgs {
 
 hipError_t launch_reroll(const RerollArgs& a, bool bf16, hipStream_t stream);
 
+struct RowOpsArgs {
+    const void* x;          // [L][T][3*H*128] raw q, k, v projections (row dtype)
+    const void* a;          // [L][T][H*128] gate pre-activations
+    const void* b;          // [L][T][H] beta pre-activations
+    const float* w;         // [L][3*H*128][4] conv taps, oldest first
+    const float* ring_in;   // [L][3][3*H*128]
+    float* ring_out;        // [L][3][3*H*128] after all T rows, or nullptr
+    float* q;               // [L][T][H][128]
+    float* k;
+    float* v;
+    float* g;
+    float* beta;            // [L][T][H]
+    int L;
+    int T;
+    int H;
+};
+
+hipError_t launch_row_ops(const RowOpsArgs& a, bool bf16, hipStream_t stream);
+
 // n uniform copies of `words` floats from a device table [src.., dst..].
 hipError_t launch_copy_batch(const uint64_t* table, int n, long long words, hipStream_t stream);
 

@@ -23,7 +23,14 @@ tokens of the rows before them, except for a planted mismatch at the
 accepted-draft count j.  Vocabulary size 150,000 mirrors the pages' head
 (about 600k floats over the four rows of a K = 3 round).
 
-Streams: 0 = verify rows, 1 = accept draws, 2 = warm-up rows, 3 = logits.
+Pre-scan row-op inputs (the projections ahead of the scan): raw q/k/v
+projections x ~ N(0, 1) over 3 * H * 128 channels, gate pre-activations
+a ~ N(0, 2^2) (so about 2% of channels reach the -5 bound), beta
+pre-activations b ~ N(0, 1) (beta = sigmoid(N(0, 1)), as above), conv taps
+~ U(-0.5, 0.5) and conv-ring rows ~ N(0, 1), all f32.
+
+Streams: 0 = verify rows, 1 = accept draws, 2 = warm-up rows, 3 = logits,
+4 = row-op inputs.
 """
 from __future__ import annotations
 
@@ -40,6 +47,7 @@ STREAM_ROWS = 0
 STREAM_ACCEPT = 1
 STREAM_WARMUP = 2
 STREAM_LOGITS = 3
+STREAM_ROW_OPS = 4
 VOCAB = 150_000
 PLANTED_LOGIT = 64.0
 
@@ -111,6 +119,20 @@ def accept_round(seed: int, index: int, t: int, V: int, j: int):
         if V == 1:
             drafts[j] = 1   # the only token is 0, so any other id misses
     return logits, drafts, planted
+
+
+def row_op_inputs(seed: int, index: int, L: int, T: int, H: int, d: int = D) -> dict:
+    """Projections for one round of row ops: x [L][T][3*H*d], a [L][T][H*d],
+    b [L][T][H], w [L][3*H*d][4], ring [L][3][3*H*d], all f32.  Draw order:
+    x, a, b, w, ring."""
+    rng = _rng(seed, STREAM_ROW_OPS, index)
+    C = 3 * H * d
+    x = rng.standard_normal((L, T, C)).astype(np.float32)
+    a = (rng.standard_normal((L, T, H * d)) * 2.0).astype(np.float32)
+    b = rng.standard_normal((L, T, H)).astype(np.float32)
+    w = rng.uniform(-0.5, 0.5, (L, C, 4)).astype(np.float32)
+    ring = rng.standard_normal((L, 3, C)).astype(np.float32)
+    return {"x": x, "a": a, "b": b, "w": w, "ring": ring}
 
 
 def warmup_rows(seed: int, n_rows: int, L: int, H: int, d: int = D) -> dict:

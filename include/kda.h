@@ -52,7 +52,7 @@ extern "C" {
 #define KDA_HEAD_DIM 128   /* d_k = d_v; glm5_spec_ppn_gate.rs fixture head_dim */
 #define KDA_T_MAX 15       /* verify rows per round: K + 1 <= 15 (glm_spec.rs, WALK-REUSE) */
 #define KDA_B_MAX 15       /* batched-decode sessions per step (same knee) */
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 #define KDA_ACCEPT_WORK_BYTES 12288   /* workspace of kda_accept_greedy */
 #define KDA_NO_TOKEN 0xFFFFFFFFu      /* argmax slot of a logits row holding a NaN */
 #define KDA_CONV_RING_ROWS 3          /* short-conv history: kernel size 4 keeps 3 raw rows */
@@ -204,6 +204,36 @@ int kda_verify_round(const float* snap_prev, float* snap_out, const void* pk, co
 int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dtype,
                       const uint32_t* drafts, uint32_t* vam, uint32_t* out2, void* work,
                       void* stream);
+
+/*
+ * Pre-scan row ops: one layer-set's projections to scan inputs, all t rows.
+ *   glm_spec.rs (0.123.0), module doc VERIFY-ROW BATCHING: a KDA layer's
+ *   gates and short conv run batched over the t = K+1 verify rows ahead of the
+ *   scan; glm5_spec_ppn_gate.rs fixture: short_conv_kernel_size 4,
+ *   gate_lower_bound -5.0.  Per row t, channel c, head h (d = 128):
+ *     y_t[c] = SiLU(w[c][0] x_{t-3}[c] + w[c][1] x_{t-2}[c] + w[c][2] x_{t-1}[c]
+ *                   + w[c][3] x_t[c])          x_{-3..-1} = the ring rows
+ *     q, k   = the q, k blocks of y, each L2-normalised per (t, h):
+ *              y / sqrt(sum y^2 + 1e-6);  v = the v block of y
+ *     g      = max(-softplus(a_t), -5);  beta = sigmoid(b_t)
+ *   (The pages fix the kernel size, the bound and the order of these ops;
+ *   SiLU after the conv, no conv bias, the norm epsilon and -softplus as the
+ *   gate's log-decay are this library's reading.)
+ *   x        : [L][T][3*H*128] in in_dtype, the raw q | k | v projections
+ *              (channel c = block*H*128 + h*128 + j).  Element alignment.
+ *   a        : [L][T][H*128] gate pre-activations; b : [L][T][H].
+ *   conv_w   : [L][3*H*128][4] f32 taps, oldest first, 16-byte aligned.
+ *   ring_in  : [L][3][3*H*128] f32, the conv ring before row 0 (row 0 oldest).
+ *   ring_out : [L][3][3*H*128] f32 or NULL: the ring after all T rows (the
+ *              full-accept ring; kda_conv_reroll gives it for a partial
+ *              accept).  May be ring_in itself.
+ *   q, k, v, g : [L][T][H][128] f32, beta : [L][T][H] f32 -- the scan's
+ *              inputs, 16-byte aligned (beta: 4 bytes).
+ *   1 <= T <= KDA_T_MAX, L, H >= 1.
+ */
+int kda_row_ops(const void* x, const void* a, const void* b, const float* conv_w,
+                const float* ring_in, float* ring_out, float* q, float* k, float* v, float* g,
+                float* beta, int L, int T, int H, int in_dtype, void* stream);
 
 /*
  * Conv-ring rollback.

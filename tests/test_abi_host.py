@@ -42,7 +42,7 @@ def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"kda_scan_rows", "kda_snapshot", "kda_replay", "kda_scan_batched",
                           "kda_verify_round", "kda_accept_greedy", "kda_conv_reroll",
-                          "kda_copy_batch", "kda_last_error", "kda_abi_version"}
+                          "kda_copy_batch", "kda_row_ops", "kda_last_error", "kda_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -313,6 +313,43 @@ def test_copy_batch_refusals(lib, b):
     assert lib.kda_copy_batch(b["ptrs"], 2, 0, None) == ERR_RANGE and "words=0" in _msg(lib)
     assert lib.kda_copy_batch(None, 2, 100, None) == ERR_ARG and "table is NULL" in _msg(lib)
     assert lib.kda_copy_batch(ctypes.c_void_p(b.addr["ptrs"] + 4), 2, 100, None) == ERR_ALIGN
+
+
+def _ops(lib, b, **kw):
+    a = dict(x=b["q"], a=b["k"], bb=b["beta"], w=b["ptrs"], ring=b["snap"], ring_out=None,
+             q=b["o"], k=b["s_out"], v=b["v"], g=b["g"], beta=b["s_in"], L=2, T=8, H=2, dt=0)
+    a.update(kw)
+    return lib.kda_row_ops(a["x"], a["a"], a["bb"], a["w"], a["ring"], a["ring_out"], a["q"],
+                           a["k"], a["v"], a["g"], a["beta"], a["L"], a["T"], a["H"], a["dt"],
+                           None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(T=0), ERR_RANGE, "T=0"),
+    (dict(T=16), ERR_RANGE, "T=16"),
+    (dict(L=0), ERR_RANGE, "L=0"),
+    (dict(H=0), ERR_RANGE, "H=0"),
+    (dict(dt=4), ERR_ARG, "in_dtype"),
+    (dict(x=None), ERR_ARG, "x is NULL"),
+    (dict(w=None), ERR_ARG, "conv_w is NULL"),
+    (dict(ring=None), ERR_ARG, "ring_in is NULL"),
+    (dict(g=None), ERR_ARG, "g is NULL"),
+    (dict(beta=None), ERR_ARG, "beta is NULL"),
+])
+def test_row_ops_refusals(lib, b, kw, code, needle):
+    assert _ops(lib, b, **kw) == code
+    assert needle in _msg(lib)
+
+
+def test_row_ops_alignment_and_alias(lib, b):
+    off = lambda n, k: ctypes.c_void_p(b.addr[n] + k)
+    assert _ops(lib, b, w=off("ptrs", 4)) == ERR_ALIGN and "conv_w is not 16" in _msg(lib)
+    assert _ops(lib, b, q=off("o", 4)) == ERR_ALIGN and "q is not 16" in _msg(lib)
+    assert _ops(lib, b, x=off("q", 1), dt=1) == ERR_ALIGN and "x is not 2" in _msg(lib)
+    assert _ops(lib, b, v=b["q"]) == ERR_ALIAS and "v overlaps x" in _msg(lib)
+    assert _ops(lib, b, g=b["o"]) == ERR_ALIAS and "q overlaps g" in _msg(lib)
+    # the ring may be updated in place, but not partially over itself
+    assert _ops(lib, b, ring_out=off("snap", 64)) == ERR_ALIAS and "partially" in _msg(lib)
 
 
 def test_snapshot_refusals(lib, b):
