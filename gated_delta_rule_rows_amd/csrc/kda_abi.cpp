@@ -356,7 +356,7 @@ int kda_row_ops(const void* x, const void* a, const void* b, const float* conv_w
         {"beta", beta, LH * T * 4, 4, false},
     };
     if ((rc = check_spans(fn, in, 5)) || (rc = check_spans(fn, out, 6)) ||
-        (rc = check_alias(fn, out, 6, in, 5, &out[0], &in[4])))
+        (rc = check_alias(fn, out, 6, in, 5)))
         return rc;
     kda::RowOpsArgs r{};
     r.x = x; r.a = a; r.b = b; r.w = conv_w; r.ring_in = ring_in; r.ring_out = ring_out;

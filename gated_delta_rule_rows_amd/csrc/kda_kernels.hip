@@ -562,107 +562,103 @@ __global__ void __launch_bounds__(kRerollThreads) kda_reroll_kernel(RerollArgs a
 //             taps w[c][0..3] oldest first, then SiLU; q and k L2-normalised
 //             per (row, head) with 1e-6 under the square root;
 //   g       : max(-softplus(a), -5);     beta : sigmoid(b).
-// One workgroup per (layer, head), one lane per head channel (q, k, v and g
-// of that channel); every row's loads are issued before any arithmetic.
+// Given the raw rows, every row's conv window x_{t-3..t} is known, so rows
+// are independent: one workgroup of 128 lanes per (layer, row, head), a lane
+// per head channel (q, k, v and g of that channel), 16 loads per lane issued
+// before any arithmetic.  The 15 rows of a (layer, head) re-read each raw row
+// up to four times; the blockIdx -> work mapping keeps them on one XCD (the
+// dispatcher deals workgroups round-robin over the 8 XCDs), so the re-reads
+// hit that XCD's L2.  The row T-1 workgroup also writes the ring after the
+// round: it is that row's conv window minus its oldest entry.
 constexpr int kOpsThreads = kD;   // 2 waves
+constexpr int kXcds = 8;
 constexpr float kNormEps = 1e-6f;
 
-__device__ __forceinline__ float silu_f(float y) { return y / (1.0f + __expf(-y)); }
-
+__device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float rcp_f(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float silu_f(float y) { return y * rcp_f(1.0f + exp_f(-y)); }
 __device__ __forceinline__ float softplus_f(float a) {
-    return a > 0.0f ? a + log1pf(__expf(-a)) : log1pf(__expf(a));
+    // max(a, 0) + ln(1 + e^-|a|), the log on the hardware log2
+    return fmaxf(a, 0.0f) + __builtin_amdgcn_logf(1.0f + exp_f(-fabsf(a))) * 0.69314718055994531f;
 }
 
 template <bool BF16>
 __global__ void __launch_bounds__(kOpsThreads) kda_row_ops_kernel(RowOpsArgs a) {
     const int j = threadIdx.x;
     const int wave = j >> 6;
-    const long long l = blockIdx.x / a.H;
-    const long long h = blockIdx.x % a.H;
+    // XCD-aware work index: consecutive work items share an XCD
+    const long long nwork = a.nwork;
+    const long long per_xcd = (nwork + kXcds - 1) / kXcds;
+    const long long bid = blockIdx.x;
+    const long long work = (bid % kXcds) * per_xcd + bid / kXcds;
+    if (work >= nwork) return;   // whole workgroup: no barrier is skipped by part of it
+    const int T = a.T;
+    const long long lh = work / T;
+    const int t = static_cast<int>(work % T);
+    const long long l = lh / a.H;
+    const long long h = lh % a.H;
     const long long HD = static_cast<long long>(a.H) * kD;
     const long long C = 3 * HD;
-    const int T = a.T;
-    // this lane's q, k, v channels
-    const long long cq = h * kD + j, ck = HD + cq, cv = 2 * HD + cq;
+    const long long c0 = h * kD + j;   // this lane's q channel; k at +HD, v at +2HD
 
-    float xq[kTMax], xk[kTMax], xv[kTMax], xa[kTMax];
+    // conv window rows t-3..t per block: ring rows for t-3+m < 0, raw rows after
+    float xw[3][4];
 #pragma unroll
-    for (int t = 0; t < kTMax; ++t) {
-        if (t < T) {
-            const size_t r = static_cast<size_t>((l * T + t) * C);
-            const size_t ra = static_cast<size_t>((l * T + t) * HD);
-            xq[t] = load1<BF16>(a.x, r + cq);
-            xk[t] = load1<BF16>(a.x, r + ck);
-            xv[t] = load1<BF16>(a.x, r + cv);
-            xa[t] = load1<BF16>(a.a, ra + cq);
+    for (int m = 0; m < 4; ++m) {
+        const int r = t - 3 + m;
+#pragma unroll
+        for (int blk = 0; blk < 3; ++blk) {
+            const long long c = c0 + blk * HD;
+            if (r < 0)
+                xw[blk][m] = a.ring_in[(l * kRingRows + (r + kRingRows)) * C + c];
+            else
+                xw[blk][m] = load1<BF16>(a.x, static_cast<size_t>((l * T + r) * C + c));
         }
     }
-    const float4 wq = *reinterpret_cast<const float4*>(a.w + (l * C + cq) * 4);
-    const float4 wk = *reinterpret_cast<const float4*>(a.w + (l * C + ck) * 4);
-    const float4 wv = *reinterpret_cast<const float4*>(a.w + (l * C + cv) * 4);
-    const float* ring = a.ring_in + l * kRingRows * C;
-    float rq0 = ring[cq], rq1 = ring[C + cq], rq2 = ring[2 * C + cq];
-    float rk0 = ring[ck], rk1 = ring[C + ck], rk2 = ring[2 * C + ck];
-    float rv0 = ring[cv], rv1 = ring[C + cv], rv2 = ring[2 * C + cv];
+    const float xa = load1<BF16>(a.a, static_cast<size_t>((l * T + t) * HD + c0));
+    float4 w[3];
+#pragma unroll
+    for (int blk = 0; blk < 3; ++blk)
+        w[blk] = *reinterpret_cast<const float4*>(a.w + (l * C + c0 + blk * HD) * 4);
     float bt = 0.0f;
-    if (j < T) bt = load1<BF16>(a.b, static_cast<size_t>((l * T + j) * a.H + h));
+    if (j == 0) bt = load1<BF16>(a.b, static_cast<size_t>((l * T + t) * a.H + h));
 
-    // conv + SiLU per row; the ring rolls in registers
-    __shared__ float part[kTMax][2][2];   // [row][wave][q, k] partial sums of squares
-    float yq[kTMax], yk[kTMax];
+    float y[3];
 #pragma unroll
-    for (int t = 0; t < kTMax; ++t) {
-        if (t < T) {
-            float cqv = wq.x * rq0;
-            cqv = fmaf(wq.y, rq1, cqv);
-            cqv = fmaf(wq.z, rq2, cqv);
-            cqv = fmaf(wq.w, xq[t], cqv);
-            float ckv = wk.x * rk0;
-            ckv = fmaf(wk.y, rk1, ckv);
-            ckv = fmaf(wk.z, rk2, ckv);
-            ckv = fmaf(wk.w, xk[t], ckv);
-            float cvv = wv.x * rv0;
-            cvv = fmaf(wv.y, rv1, cvv);
-            cvv = fmaf(wv.z, rv2, cvv);
-            cvv = fmaf(wv.w, xv[t], cvv);
-            rq0 = rq1; rq1 = rq2; rq2 = xq[t];
-            rk0 = rk1; rk1 = rk2; rk2 = xk[t];
-            rv0 = rv1; rv1 = rv2; rv2 = xv[t];
-            yq[t] = silu_f(cqv);
-            yk[t] = silu_f(ckv);
-            const size_t o = static_cast<size_t>(((l * T + t) * a.H + h) * kD + j);
-            a.v[o] = silu_f(cvv);
-            a.g[o] = fmaxf(-softplus_f(xa[t]), kGateLo);
-            float sq = yq[t] * yq[t];
-            float sk = yk[t] * yk[t];
+    for (int blk = 0; blk < 3; ++blk) {
+        float acc = w[blk].x * xw[blk][0];
+        acc = fmaf(w[blk].y, xw[blk][1], acc);
+        acc = fmaf(w[blk].z, xw[blk][2], acc);
+        acc = fmaf(w[blk].w, xw[blk][3], acc);
+        y[blk] = silu_f(acc);
+    }
+    const size_t o = static_cast<size_t>(((l * T + t) * a.H + h) * kD + j);
+    a.v[o] = y[2];
+    a.g[o] = fmaxf(-softplus_f(xa), kGateLo);
+    if (j == 0) a.beta[(l * T + t) * a.H + h] = rcp_f(1.0f + exp_f(-bt));
+
+    float sq = y[0] * y[0];
+    float sk = y[1] * y[1];
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                sq += __shfl_xor(sq, off);
-                sk += __shfl_xor(sk, off);
-            }
-            if ((j & 63) == 0) {
-                part[t][wave][0] = sq;
-                part[t][wave][1] = sk;
-            }
-        }
+    for (int off = 32; off >= 1; off >>= 1) {
+        sq += __shfl_xor(sq, off);
+        sk += __shfl_xor(sk, off);
+    }
+    __shared__ float part[2][2];   // [wave][q, k]
+    if ((j & 63) == 0) {
+        part[wave][0] = sq;
+        part[wave][1] = sk;
     }
     __syncthreads();
+    a.q[o] = y[0] * __builtin_amdgcn_rsqf(part[0][0] + part[1][0] + kNormEps);
+    a.k[o] = y[1] * __builtin_amdgcn_rsqf(part[0][1] + part[1][1] + kNormEps);
+
+    if (a.ring_out && t == T - 1) {
 #pragma unroll
-    for (int t = 0; t < kTMax; ++t) {
-        if (t < T) {
-            const float nq = 1.0f / sqrtf(part[t][0][0] + part[t][1][0] + kNormEps);
-            const float nk = 1.0f / sqrtf(part[t][0][1] + part[t][1][1] + kNormEps);
-            const size_t o = static_cast<size_t>(((l * T + t) * a.H + h) * kD + j);
-            a.q[o] = yq[t] * nq;
-            a.k[o] = yk[t] * nk;
-        }
-    }
-    if (j < T) a.beta[(l * T + j) * a.H + h] = 1.0f / (1.0f + __expf(-bt));
-    if (a.ring_out) {
-        float* ro = a.ring_out + l * kRingRows * C;
-        ro[cq] = rq0; ro[C + cq] = rq1; ro[2 * C + cq] = rq2;
-        ro[ck] = rk0; ro[C + ck] = rk1; ro[2 * C + ck] = rk2;
-        ro[cv] = rv0; ro[C + cv] = rv1; ro[2 * C + cv] = rv2;
+        for (int m = 0; m < kRingRows; ++m)
+#pragma unroll
+            for (int blk = 0; blk < 3; ++blk)
+                a.ring_out[(l * kRingRows + m) * C + c0 + blk * HD] = xw[blk][m + 1];
     }
 }
 
@@ -935,8 +931,11 @@ hipError_t launch_reroll(const RerollArgs& a0, bool bf16, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_row_ops(const RowOpsArgs& a, bool bf16, hipStream_t stream) {
-    const unsigned long long blocks = static_cast<unsigned long long>(a.L) * a.H;
+hipError_t launch_row_ops(const RowOpsArgs& a0, bool bf16, hipStream_t stream) {
+    RowOpsArgs a = a0;
+    a.nwork = static_cast<long long>(a.L) * a.H * a.T;
+    const long long per_xcd = (a.nwork + kXcds - 1) / kXcds;
+    const unsigned long long blocks = static_cast<unsigned long long>(per_xcd) * kXcds;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
     if (bf16)
         kda_row_ops_kernel<true><<<dim3(static_cast<unsigned>(blocks)), kOpsThreads, 0, stream>>>(a);

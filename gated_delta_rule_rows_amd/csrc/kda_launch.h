@@ -86,6 +86,7 @@ struct RowOpsArgs {
     float* v;
     float* g;
     float* beta;            // [L][T][H]
+    long long nwork;        // L*H*T, set by launch_row_ops
     int L;
     int T;
     int H;

@@ -226,7 +226,8 @@ int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dty
  *   ring_in  : [L][3][3*H*128] f32, the conv ring before row 0 (row 0 oldest).
  *   ring_out : [L][3][3*H*128] f32 or NULL: the ring after all T rows (the
  *              full-accept ring; kda_conv_reroll gives it for a partial
- *              accept).  May be ring_in itself.
+ *              accept).  Must not overlap ring_in: rows are computed in
+ *              parallel, and the early rows read ring_in.
  *   q, k, v, g : [L][T][H][128] f32, beta : [L][T][H] f32 -- the scan's
  *              inputs, 16-byte aligned (beta: 4 bytes).
  *   1 <= T <= KDA_T_MAX, L, H >= 1.

@@ -348,8 +348,9 @@ def test_row_ops_alignment_and_alias(lib, b):
     assert _ops(lib, b, x=off("q", 1), dt=1) == ERR_ALIGN and "x is not 2" in _msg(lib)
     assert _ops(lib, b, v=b["q"]) == ERR_ALIAS and "v overlaps x" in _msg(lib)
     assert _ops(lib, b, g=b["o"]) == ERR_ALIAS and "q overlaps g" in _msg(lib)
-    # the ring may be updated in place, but not partially over itself
-    assert _ops(lib, b, ring_out=off("snap", 64)) == ERR_ALIAS and "partially" in _msg(lib)
+    # rows run in parallel and the early ones read ring_in: no in-place ring
+    assert _ops(lib, b, ring_out=b["snap"]) == ERR_ALIAS and "ring_out overlaps ring_in" in _msg(lib)
+    assert _ops(lib, b, ring_out=off("snap", 64)) == ERR_ALIAS
 
 
 def test_snapshot_refusals(lib, b):

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-5
 
 
-def _run(inp, L, T, H, bf16=False, in_place_ring=False):
+def _run(inp, L, T, H, bf16=False):
     dev = {}
     for n in ("x", "a", "b"):
         if bf16:
@@ -33,7 +33,7 @@ def _run(inp, L, T, H, bf16=False, in_place_ring=False):
     ring = torch.from_numpy(inp["ring"]).cuda()
     out = {n: torch.full((L, T, H, 128), 9.0, device="cuda") for n in ("q", "k", "v", "g")}
     out["beta"] = torch.full((L, T, H), 9.0, device="cuda")
-    ring_out = ring if in_place_ring else torch.empty_like(ring)
+    ring_out = torch.full_like(ring, 9.0)
     kda.kda_row_ops(dev["x"], dev["a"], dev["b"], w, ring, out["q"], out["k"], out["v"],
                     out["g"], out["beta"], ring_out=ring_out)
     torch.cuda.synchronize()
@@ -71,17 +71,26 @@ def test_row_ops_match_oracle_bf16(L, T, H):
     _close(got, _ref(inp, H, bf16=True))
 
 
-def test_row_ops_in_place_ring_and_full_accept_reroll():
-    L, T, H = 2, 7, 4
-    inp = synth.row_op_inputs(7, 0, L, T, H)
-    got, dev = _run(inp, L, T, H, in_place_ring=True)
+@pytest.mark.parametrize("T", [1, 2, 3, 7])
+def test_row_ops_ring_is_the_full_accept_reroll(T):
+    # the ring after all T rows (written by the last row's workgroup, from ring
+    # rows when T < 3) is the re-roll of the snapshot at keep = T
+    L, H = 2, 4
+    inp = synth.row_op_inputs(7, T, L, T, H)
+    got, dev = _run(inp, L, T, H)
     _close(got, _ref(inp, H))
-    # the ring after all T rows is the full-accept re-roll of the snapshot
     snap = torch.from_numpy(inp["ring"]).cuda()
     out = torch.empty_like(snap)
     kda.kda_conv_reroll(snap, dev["x"], T, out)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(out.cpu().numpy(), got["ring"])
+    # rows run in parallel, so an in-place ring is refused
+    q = torch.empty(L, T, H, 128, device="cuda")
+    beta = torch.empty(L, T, H, device="cuda")
+    with pytest.raises(kda.KdaError, match="ring_out overlaps ring_in"):
+        kda.kda_row_ops(dev["x"], dev["a"], dev["b"], torch.from_numpy(inp["w"]).cuda(), snap,
+                        q, torch.empty_like(q), torch.empty_like(q), torch.empty_like(q), beta,
+                        ring_out=snap)
 
 
 def test_row_ops_feed_the_scan_end_to_end():
