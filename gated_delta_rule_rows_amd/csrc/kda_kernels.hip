@@ -375,6 +375,10 @@ __device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], in
 #pragma unroll
             for (int c = 0; c < C; ++c) e[c] = fmaf(nbt, u[c], ve[c]);
             if constexpr (M == Rows::kFull) {
+                // finish w's butterfly on every lane: sunk into the writer's
+                // branch, its last DPP step would become mov 0, mov_dpp, add
+#pragma unroll
+                for (int c = 0; c < C; ++c) asm volatile("" : "+v"(w[c]));
                 const float qk = L.qk[t];
                 float ov[C];
 #pragma unroll
