@@ -16,7 +16,9 @@ Two pipelines of the same round are timed in one run:
   split: kda_scan_rows out of place (the untouched input is the snapshot),
       then kda_replay of the kept rows when j < 14.
 
-Also timed: kda_accept_greedy over one round's logits (t = 15, V = 150,000,
+Also timed: the batched-decode arm (15 sessions x 34 layers at t = 1); the
+bf16 serving mix as fused rounds with forced full accept, forced j = 0 and K
+drawn per round from {1, 3, 5, 7, 14}; kda_accept_greedy over one round's logits (t = 15, V = 150,000,
 f32), the greedy accept that decides j on the device; kda_conv_reroll of the
 34 layers' short-conv rings; kda_copy_batch of 34 separately allocated layer
 states in one launch; kda_row_ops turning one round's projections into scan
@@ -151,6 +153,10 @@ def main() -> int:
                     help="extra round launches timed after a 512 MiB write, for the MALL-cold figure")
     ap.add_argument("--copy-launches", type=int, default=8,
                     help="kda_snapshot launches of the full state, timed for the copy ceiling")
+    ap.add_argument("--batched-steps", type=int, default=8,
+                    help="batched-decode steps (B=15, t=1, 34 layers) timed back to back")
+    ap.add_argument("--serving-steps", type=int, default=32,
+                    help="bf16 serving-mix rounds per accept pattern (0 skips the figure)")
     ap.add_argument("--accept-launches", type=int, default=32,
                     help="kda_accept_greedy launches at t=15, V=150,000 (0 skips the figure)")
     ap.add_argument("--no-split", action="store_true", help="skip the split scan + replay pipeline")
@@ -321,6 +327,87 @@ def main() -> int:
         copy_gbps = 2 * src.numel() * 4 / (float(np.median(cu)) * 1e-6) / 1e9
         del dst
 
+    # batched-decode arm: 15 sessions x 34 layers x 64 heads, one row each, in place
+    batched = None
+    if args.batched_steps > 0:
+        wb = synth.WORKLOADS["batched_b15"]
+        B = wb.B
+        b_states = torch.zeros(L, B, H, D, D, device="cuda")
+        b_table = kda.state_table(b_states)
+        b_pool = [[torch.from_numpy(r[n]).cuda() for n in names]
+                  for r in (synth.rows(wb.seed, i, L, B, H) for i in range(4))]
+        b_o = torch.empty(L, B, H, D, device="cuda")
+        for i in range(2):
+            kda.kda_scan_batched(b_table, *b_pool[i % 4], o=b_o)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for i in range(args.batched_steps):
+            kda.kda_scan_batched(b_table, *b_pool[i % 4], o=b_o)
+        b.record(stream)
+        torch.cuda.synchronize()
+        b_us = a.elapsed_time(b) * 1e3 / args.batched_steps
+        # per (session, layer, head): state read + write, q/k/v/g, beta, o
+        b_bytes = L * B * H * (2 * STATE_BYTES + 4 * ROW_BYTES + 4 + ROW_BYTES)
+        batched = {"workload": "batched_b15", "B": B, "steps": args.batched_steps,
+                   "us_per_step": b_us, "rows_heads_per_s": L * B * H / (b_us * 1e-6),
+                   "bytes_per_step": b_bytes, "gbps": b_bytes / (b_us * 1e-6) / 1e9}
+        del b_states, b_pool, b_o
+
+    # serving mix: bf16 rows, f32 state, fused rounds; forced full accept, forced
+    # j = 0, and K drawn per round from {1, 3, 5, 7, 14} with j ~ U{0..K}
+    serving = None
+    if args.serving_steps > 0:
+        wsv = synth.WORKLOADS["serving_mix_bf16"]
+        ks = [int(x) for x in synth.serving_ks(wsv.seed, args.serving_steps)]
+        by_t = {}
+        for kk in sorted(set(ks) | {T - 1}):
+            r = synth.rows_bf16(wsv.seed, kk, L, kk + 1, H)
+            by_t[kk + 1] = [torch.from_numpy(r[n].view(np.int16)).cuda().view(torch.bfloat16)
+                            for n in names]
+        sv_state = [torch.zeros(L, H, D, D, device="cuda") for _ in range(2)]
+        sv_e = [torch.zeros(L * T * H * D, device="cuda") for _ in range(2)]
+        sv_o = torch.empty(L * T * H * D, device="cuda")
+
+        def serve(seq):
+            """seq: list of (T_round, keep of this round); returns (us, rows)."""
+            prev = None
+            for warm in (True, False):
+                torch.cuda.synchronize()
+                a, b = ev(), ev()
+                a.record(stream)
+                for i, (tr, keep) in enumerate(seq):
+                    rows = by_t[tr]
+                    e_cur = sv_e[i % 2][:L * tr * H * D].view(L, tr, H, D)
+                    o_cur = sv_o[:L * tr * H * D].view(L, tr, H, D)
+                    snap, nxt = sv_state[i % 2], sv_state[(i + 1) % 2]
+                    if prev is None:
+                        kda.kda_verify_round(snap, nxt, None, 0, *rows, o_cur, e=e_cur)
+                    else:
+                        p_rows, p_e, p_keep = prev
+                        kda.kda_verify_round(snap, nxt, (p_rows[1], None, p_rows[3], None, p_e),
+                                             p_keep, *rows, o_cur, e=e_cur)
+                    prev = (rows, e_cur, keep)
+                b.record(stream)
+                torch.cuda.synchronize()
+                if not warm:
+                    return a.elapsed_time(b) * 1e3, sum(tr for tr, _ in seq)
+                prev = None
+
+        n = args.serving_steps
+        rng = np.random.default_rng(wsv.seed)
+        seqs = {
+            "full_accept_k14": [(T, T)] * n,
+            "j0_k14": [(T, 1)] * n,
+            "mix": [(kk + 1, int(rng.integers(0, kk + 1)) + 1) for kk in ks],
+        }
+        serving = {"workload": "serving_mix_bf16", "rounds": n, "dtype_rows": "bf16"}
+        for name, seq in seqs.items():
+            us, nrows = serve(seq)
+            serving[name] = {"us_per_round": us / n,
+                             "rows_heads_per_s": nrows * H * L / (us * 1e-6)}
+        del by_t, sv_state, sv_e, sv_o
+
     # greedy accept of one K=14 round over a 150,000-entry vocabulary (f32 logits)
     accept = None
     if args.accept_launches > 0:
@@ -452,6 +539,8 @@ def main() -> int:
         "split": split,
         "accept": accept,
         "rollback_extras": rollback_extras,
+        "batched": batched,
+        "serving_mix": serving,
         "copy_ceiling_gbps": copy_gbps,
         "frac_of_copy_ceiling": (achieved / copy_gbps) if copy_gbps else None,
         "wall_s_timed": f_wall,
