@@ -227,14 +227,15 @@ struct Src {
 // Load one phase's rows, run `between` (the state loads, when this is the
 // first phase), then stage everything in LDS.  All loads are in flight before
 // the first wait.  Ends with the staged rows visible to every wave.
-template <int R, int C, bool BF16, Rows M, typename F>
+template <int R, int C, bool BF16, Rows M, int TMAX = kTMax, typename F>
 __device__ __forceinline__ void stage(Stage<R>& L, const Src& src, int tid, F&& between) {
     using TL = Tile<R, C>;
     using KR = KeyRow<R>;
     float* sd = reinterpret_cast<float*>(L.d);
     float* sk = reinterpret_cast<float*>(L.k);
     float* sq = reinterpret_cast<float*>(L.q);
-    constexpr int kPer = (kTMax * (kD / 4) + TL::THREADS - 1) / TL::THREADS;
+    // float4 loads per lane per input: enough for TMAX rows of 32 float4
+    constexpr int kPer = (TMAX * (kD / 4) + TL::THREADS - 1) / TL::THREADS;
     const int T = src.T;
     float4 in_k[kPer], in_v[kPer], in_g[kPer], in_q[kPer];
     float in_b[kPer];
@@ -454,8 +455,21 @@ kda_scan_kernel(ScanArgs a) {
         for (int r = 0; r < R; ++r) load_gcols<C>(st_in + (lane_off + r * kD), s[r]);
     };
     auto store_state = [&] {
+        if constexpr (TABLE) {
+            // rows past the 4 KiB immediate-offset range get one shared base
+            // pair: left to itself the compiler builds a 64-bit address per
+            // row there, and those pairs spill
+            constexpr int kNear = 4096 / (kD * 4);
+            gfloat* near = st_out + lane_off;
+            gfloat* far = near + kNear * kD;
+            asm volatile("" : "+v"(far));
 #pragma unroll
-        for (int r = 0; r < R; ++r) store_gcols<C>(st_out + (lane_off + r * kD), s[r]);
+            for (int r = 0; r < R; ++r)
+                store_gcols<C>(r < kNear ? near + r * kD : far + (r - kNear) * kD, s[r]);
+        } else {
+#pragma unroll
+            for (int r = 0; r < R; ++r) store_gcols<C>(st_out + (lane_off + r * kD), s[r]);
+        }
     };
 
     if constexpr (FUSED) {
@@ -475,7 +489,8 @@ kda_scan_kernel(ScanArgs a) {
         store_state();         // the committed state: this round's snapshot
         stage<R, C, BF16, MB>(L, b, tid, [] {});
     } else {
-        stage<R, C, BF16, MB>(L, b, tid, load_state);
+        // the batched arm always scans one row per session
+        stage<R, C, BF16, MB, TABLE ? 1 : kTMax>(L, b, tid, load_state);
     }
     run_rows<R, C, MB>(L, s, b.T, a.o, TABLE ? nullptr : a.e_out, o0, ostride, ig, i0, j0);
     if constexpr (!FUSED) store_state();
