@@ -42,6 +42,11 @@
 // No MFMA: each row is two matrix-vector products and a rank-1 update with a
 // sequential dependency from row to row -- there is no dense contraction to
 // feed the matrix cores.
+//
+// Beside the scan, all HBM- or latency-bound: the pre-scan row ops (short
+// conv, norms, gate, beta) that produce the scan's inputs; the conv-ring
+// rollback; a plain copy (snapshots) and a pointer-table batched copy; and the
+// greedy accept (split-row argmax, then a one-workgroup prefix walk).
 
 #include <hip/hip_runtime.h>
 
