@@ -16,7 +16,8 @@ Two pipelines of the same round are timed in one run:
   split: kda_scan_rows out of place (the untouched input is the snapshot),
       then kda_replay of the kept rows when j < 14.
 
-Also timed: the batched-decode arm (15 sessions x 34 layers at t = 1); the
+Also timed: the same fused round issued per layer (34 launches of 64 heads
+replayed from one HIP graph); the batched-decode arm (15 sessions x 34 layers at t = 1); the
 bf16 serving mix as fused rounds with forced full accept, forced j = 0 and K
 drawn per round from {1, 3, 5, 7, 14}; kda_accept_greedy over one round's logits (t = 15, V = 150,000,
 f32), the greedy accept that decides j on the device; kda_conv_reroll of the
@@ -153,6 +154,8 @@ def main() -> int:
                     help="extra round launches timed after a 512 MiB write, for the MALL-cold figure")
     ap.add_argument("--copy-launches", type=int, default=8,
                     help="kda_snapshot launches of the full state, timed for the copy ceiling")
+    ap.add_argument("--per-layer-rounds", type=int, default=16,
+                    help="rounds of 34 per-layer fused launches replayed from a HIP graph")
     ap.add_argument("--batched-steps", type=int, default=8,
                     help="batched-decode steps (B=15, t=1, 34 layers) timed back to back")
     ap.add_argument("--serving-steps", type=int, default=32,
@@ -326,6 +329,51 @@ def main() -> int:
             cu.append(a.elapsed_time(b) * 1e3)
         copy_gbps = 2 * src.numel() * 4 / (float(np.median(cu)) * 1e-6) / 1e9
         del dst
+
+    # the same fused round issued one layer at a time (34 launches of 64 heads,
+    # as a model's layer loop issues it), captured once in a HIP graph; the
+    # graph fixes keep_prev at 8, the mean of j + 1 for j ~ U{0..14}
+    per_layer = None
+    if args.per_layer_rounds > 0:
+        snap, nxt = bufs[0]
+        rows = dev_rounds[0]
+        e_prev, e_cur = stash[0]
+
+        def lay(x, l):
+            return x[l:l + 1]
+
+        def layer_loop():
+            for l in range(L):
+                rr = [lay(x, l) for x in rows]
+                kda.kda_verify_round(lay(snap, l), lay(nxt, l),
+                                     (rr[1], None, rr[3], None, lay(e_prev, l)), 8, *rr,
+                                     lay(o, l), e=lay(e_cur, l))
+
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            layer_loop()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            layer_loop()
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(args.per_layer_rounds):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        pl_us = a.elapsed_time(b) * 1e3 / args.per_layer_rounds
+        per_layer = {"launches_per_round": L, "keep_prev": 8, "rounds": args.per_layer_rounds,
+                     "us_per_round": pl_us, "us_per_layer": pl_us / L,
+                     "rows_heads_per_s": T * H * L / (pl_us * 1e-6),
+                     "note": "one kda_verify_round per layer (64 heads, 4 workgroups per "
+                             "head), 34 launches replayed from one HIP graph"}
+        del graph
 
     # batched-decode arm: 15 sessions x 34 layers x 64 heads, one row each, in place
     batched = None
@@ -539,6 +587,7 @@ def main() -> int:
         "split": split,
         "accept": accept,
         "rollback_extras": rollback_extras,
+        "per_layer_graph": per_layer,
         "batched": batched,
         "serving_mix": serving,
         "copy_ceiling_gbps": copy_gbps,

@@ -65,19 +65,25 @@ constexpr float kInvSqrtD = 0.0883883476483184405501055452631f;
 
 template <int R, int C>
 struct Tile {
-    static constexpr int NI = kD / R;         // lanes reducing one column group
-    static constexpr int NJG = 64 / NI;       // column groups per wave
-    static constexpr int WCOLS = NJG * C;     // value columns per wave
-    static constexpr int WAVES = kD / WCOLS;  // waves per head
+    static constexpr int NI = kD / R;          // lanes reducing one column group
+    static constexpr int NJG = 64 / NI;        // column groups per wave
+    static constexpr int WCOLS = NJG * C;      // value columns per wave
+    static constexpr int WAVES = 4;            // waves per workgroup
     static constexpr int THREADS = 64 * WAVES;
+    static constexpr int BCOLS = WAVES * WCOLS;   // value columns per workgroup
+    static constexpr int BLOCKS = kD / BCOLS;     // workgroups per head
     static_assert(NI == 4 || NI == 8 || NI == 16, "the reduction must stay in one DPP row");
-    static_assert(kD % WCOLS == 0, "waves must tile the head");
-    static_assert(C == 2 || C == 4, "column vector width");
+    static_assert(kD % BCOLS == 0, "workgroups must tile the head");
+    static_assert(C == 1 || C == 2 || C == 4, "column vector width");
 };
 
-// The library's one tiling.  Changing it changes the canonical rounding of
-// every entry point together, so identity between them is kept.
-using TileT = Tile<16, 4>;
+// The key split R = 16 (8 lanes per column group) fixes the rounding: each
+// value column is an in-lane chain over its lane's 16 keys, in order, then
+// the same 3-step butterfly, whatever C is.  C (value columns per lane) only
+// sets how many workgroups share a head -- 1 at C = 4, 2 at C = 2, 4 at C = 1
+// -- so launches with few chains can spread over the chip and still give the
+// bits of every other launch.
+constexpr int kKeysPerLane = 16;
 
 // ------------------------------------------------------------------ lane ops
 
@@ -153,9 +159,11 @@ __device__ __forceinline__ void load_gcols(const gfloat* p, float (&x)[C]) {
     if constexpr (C == 4) {
         const vf4 v = *(const gvf4*)p;
         x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-    } else {
+    } else if constexpr (C == 2) {
         const vf2 v = *(const gvf2*)p;
         x[0] = v.x; x[1] = v.y;
+    } else {
+        x[0] = *p;
     }
 }
 
@@ -163,8 +171,10 @@ template <int C>
 __device__ __forceinline__ void store_gcols(gfloat* p, const float (&x)[C]) {
     if constexpr (C == 4) {
         *(gvf4*)p = vf4{x[0], x[1], x[2], x[3]};
-    } else {
+    } else if constexpr (C == 2) {
         *(gvf2*)p = vf2{x[0], x[1]};
+    } else {
+        *p = x[0];
     }
 }
 
@@ -173,9 +183,11 @@ __device__ __forceinline__ void load_cols(const float* p, float (&x)[C]) {
     if constexpr (C == 4) {
         const float4 v = *reinterpret_cast<const float4*>(p);
         x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-    } else {
+    } else if constexpr (C == 2) {
         const float2 v = *reinterpret_cast<const float2*>(p);
         x[0] = v.x; x[1] = v.y;
+    } else {
+        x[0] = *p;
     }
 }
 
@@ -183,8 +195,10 @@ template <int C>
 __device__ __forceinline__ void store_cols(float* p, const float (&x)[C]) {
     if constexpr (C == 4) {
         *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
-    } else {
+    } else if constexpr (C == 2) {
         *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+    } else {
+        *p = x[0];
     }
 }
 
@@ -419,13 +433,14 @@ kda_scan_kernel(ScanArgs a) {
     const int ig = lane % TL::NI;
     const int jg = lane / TL::NI;
     const int i0 = ig * R;
-    const int j0 = wave * TL::WCOLS + jg * C;
+    // --- where this chain lives: workgroup blk of the head's TL::BLOCKS
+    const size_t chain = blockIdx.x / TL::BLOCKS;
+    const int blk = static_cast<int>(blockIdx.x % TL::BLOCKS);
+    const int j0 = blk * TL::BCOLS + wave * TL::WCOLS + jg * C;
     // this lane's element offset inside a head's state; the per-head base
     // pointers are wave-uniform, so addresses are SGPR base + 32-bit offset
     const uint32_t lane_off = static_cast<uint32_t>(i0 * kD + j0);
 
-    // --- where this chain lives
-    const size_t chain = blockIdx.x;
     const gfloat* st_in;
     gfloat* st_out;
     Src b;   // this launch's rows
@@ -876,12 +891,28 @@ __global__ void __launch_bounds__(64 * kTMax) kda_accept_finish_kernel(AcceptArg
     }
 }
 
+template <int C, bool BF16, Rows MA, Rows MB, bool TABLE>
+hipError_t launch_tiled(const ScanArgs& a, hipStream_t stream) {
+    using TL = Tile<kKeysPerLane, C>;
+    const unsigned long long blocks = static_cast<unsigned long long>(a.n_chains) * TL::BLOCKS;
+    if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    kda_scan_kernel<kKeysPerLane, C, BF16, MA, MB, TABLE>
+        <<<dim3(static_cast<unsigned>(blocks)), dim3(TL::THREADS), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+// Chains below which a head is split over more workgroups: a launch should
+// reach every CU (256) with at least two workgroups where it can.
+constexpr long long kSplitBy4Below = 256;   // C = 1: 4 workgroups per head
+constexpr long long kSplitBy2Below = 512;   // C = 2: 2 workgroups per head
+
 template <bool BF16, Rows MA, Rows MB, bool TABLE>
 hipError_t launch_one(const ScanArgs& a, hipStream_t stream) {
-    using TL = TileT;
-    kda_scan_kernel<16, 4, BF16, MA, MB, TABLE>
-        <<<dim3(static_cast<unsigned>(a.n_chains)), dim3(TL::THREADS), 0, stream>>>(a);
-    return hipGetLastError();
+    if constexpr (!TABLE) {
+        if (a.n_chains < kSplitBy4Below) return launch_tiled<1, BF16, MA, MB, TABLE>(a, stream);
+        if (a.n_chains < kSplitBy2Below) return launch_tiled<2, BF16, MA, MB, TABLE>(a, stream);
+    }
+    return launch_tiled<4, BF16, MA, MB, TABLE>(a, stream);
 }
 
 template <bool BF16>

@@ -461,3 +461,55 @@ def test_fused_pipeline_serving_mix_bf16_sampled_vs_oracle():
     w = synth.WORKLOADS["serving_mix_bf16"]
     Ks = synth.serving_ks(w.seed, 3)
     _fused_pipeline(w, 3, SAMPLE_HEADS, bf16=True, stash=False, Ts=[int(k) + 1 for k in Ks])
+
+
+# ----------------------------------------------------------------- tilings
+
+def _per_layers(fn, L, chunk):
+    """Run fn(l0, l1) on layer chunks [l0, l1) and return the pieces in order."""
+    return [fn(l0, min(l0 + chunk, L)) for l0 in range(0, L, chunk)]
+
+
+@pytest.mark.parametrize("chunk", [1, 4, 8])
+def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk):
+    # 1 layer = 64 chains (4 workgroups per head), 4 layers = 256 chains
+    # (2 per head), 8 layers = 512 chains (1 per head): every tiling must
+    # give the bits of the 34-layer launch, for the scan, both replays and
+    # the fused round
+    L, T, H = 34, 15, 64
+    r = rand_rows(91, L, T, H)
+    rows = rows_dev(r)
+    s0 = dev(rand_state(92, L, H, 0.5))
+    s_full, o_full = scan(s0, rows)
+    e_full = torch.empty(L, T, H, D, device="cuda")
+    kda.kda_scan_rows(s0, torch.empty_like(s0), *rows, o=torch.empty_like(o_full), e=e_full)
+    rep_full = torch.empty_like(s0)
+    kda.kda_replay(s0, rep_full, *rows[1:], keep=6)
+    reps_full = torch.empty_like(s0)
+    kda.kda_replay(s0, reps_full, rows[1], None, rows[3], None, keep=9, e=e_full)
+    snap_full, o2_full = torch.empty_like(s0), torch.empty_like(o_full)
+    kda.kda_verify_round(s0, snap_full, (rows[1], None, rows[3], None, e_full), 11, *rows, o2_full)
+    torch.cuda.synchronize()
+
+    def lay(x, l0, l1):
+        return x[l0:l1].contiguous()
+
+    def piece(l0, l1):
+        rr = [lay(x, l0, l1) for x in rows]
+        si = lay(s0, l0, l1)
+        so, oo = scan(si, rr)
+        rp = torch.empty_like(si)
+        kda.kda_replay(si, rp, *rr[1:], keep=6)
+        el = lay(e_full, l0, l1)
+        rps = torch.empty_like(si)
+        kda.kda_replay(si, rps, rr[1], None, rr[3], None, keep=9, e=el)
+        sn, o2 = torch.empty_like(si), torch.empty_like(oo)
+        kda.kda_verify_round(si, sn, (rr[1], None, rr[3], None, el), 11, *rr, o2)
+        return so, oo, rp, rps, sn, o2
+
+    parts = _per_layers(piece, L, chunk)
+    torch.cuda.synchronize()
+    got = [torch.cat([p[i] for p in parts]) for i in range(6)]
+    for name, a, b in zip(("state", "o", "replay", "stash replay", "round snap", "round o"),
+                          got, (s_full, o_full, rep_full, reps_full, snap_full, o2_full)):
+        assert bits_equal(a, b), f"{name} differs at chunk {chunk}"
