@@ -246,68 +246,85 @@ struct Src {
 // Load one phase's rows, run `between` (the state loads, when this is the
 // first phase), then stage everything in LDS.  All loads are in flight before
 // the first wait.  Ends with the staged rows visible to every wave.
-template <int R, int C, bool BF16, Rows M, int TMAX = kTMax, typename F>
-__device__ __forceinline__ void stage(Stage<R>& L, const Src& src, int tid, F&& between) {
+// One phase's row inputs in flight: float4 loads per lane per input, enough
+// for TMAX rows of 32 float4.
+template <int R, int C, Rows M, int TMAX>
+struct Staged {
+    static constexpr int kPer = (TMAX * (kD / 4) + Tile<R, C>::THREADS - 1) / Tile<R, C>::THREADS;
+    float4 k[kPer], v[kPer], g[kPer], q[kPer];
+    float b[kPer];
+};
+
+// Issue every global load of a phase's rows (nothing waits on them here).
+template <int R, int C, bool BF16, Rows M, int TMAX>
+__device__ __forceinline__ void stage_issue(Staged<R, C, M, TMAX>& in, const Src& src, int tid) {
     using TL = Tile<R, C>;
-    using KR = KeyRow<R>;
-    float* sd = reinterpret_cast<float*>(L.d);
-    float* sk = reinterpret_cast<float*>(L.k);
-    float* sq = reinterpret_cast<float*>(L.q);
-    // float4 loads per lane per input: enough for TMAX rows of 32 float4
-    constexpr int kPer = (TMAX * (kD / 4) + TL::THREADS - 1) / TL::THREADS;
     const int T = src.T;
-    float4 in_k[kPer], in_v[kPer], in_g[kPer], in_q[kPer];
-    float in_b[kPer];
 #pragma unroll
-    for (int p = 0; p < kPer; ++p) {
+    for (int p = 0; p < Staged<R, C, M, TMAX>::kPer; ++p) {
         // unconditional (row clamped into range, surplus values unused): a
         // branch here would make the merge copies wait on the loads
         const int idx = tid + p * TL::THREADS;
         const int t = min(idx >> 5, T - 1);
         const size_t off = src.row0 + t * src.rstride + (idx & 31) * 4;
-        in_k[p] = load4<BF16>(src.k, off);
-        in_g[p] = load4<BF16>(src.g, off);
+        in.k[p] = load4<BF16>(src.k, off);
+        in.g[p] = load4<BF16>(src.g, off);
         if constexpr (M == Rows::kStash) {
-            in_v[p] = *reinterpret_cast<const float4*>(src.e + off);
+            in.v[p] = *reinterpret_cast<const float4*>(src.e + off);
         } else {
-            in_v[p] = load4<BF16>(src.v, off);
-            in_b[p] = load1<BF16>(src.beta, src.b0 + t * src.bstride);
+            in.v[p] = load4<BF16>(src.v, off);
+            in.b[p] = load1<BF16>(src.beta, src.b0 + t * src.bstride);
         }
-        if constexpr (M == Rows::kFull) in_q[p] = load4<BF16>(src.q, off);
+        if constexpr (M == Rows::kFull) in.q[p] = load4<BF16>(src.q, off);
     }
-    between();
-    // keep the staging arithmetic below from being hoisted between the loads
-    // (it would wait on the first input load before the state loads are
-    // issued): the staged values pass through an empty asm placed here
+}
+
+// Keep the staging arithmetic from being hoisted between the loads (it would
+// wait on the first input load before later loads are issued): the staged
+// values pass through an empty asm placed after every load of the launch.
+template <int R, int C, Rows M, int TMAX>
+__device__ __forceinline__ void stage_fence(Staged<R, C, M, TMAX>& in) {
 #pragma unroll
-    for (int p = 0; p < kPer; ++p) {
-        opaque(in_k[p]);
-        opaque(in_v[p]);
-        opaque(in_g[p]);
-        if constexpr (M == Rows::kFull) opaque(in_q[p]);
-        if constexpr (M != Rows::kStash) asm volatile("" : "+v"(in_b[p])::"memory");
+    for (int p = 0; p < Staged<R, C, M, TMAX>::kPer; ++p) {
+        opaque(in.k[p]);
+        opaque(in.v[p]);
+        opaque(in.g[p]);
+        if constexpr (M == Rows::kFull) opaque(in.q[p]);
+        if constexpr (M != Rows::kStash) asm volatile("" : "+v"(in.b[p])::"memory");
     }
+}
+
+// Write a phase's rows to LDS in the scan's layout (decay, q/sqrt(128), beta v
+// or e), then (q/sqrt(128)).k per row.  Ends with every lane past a barrier.
+template <int R, int C, Rows M, int TMAX>
+__device__ __forceinline__ void stage_commit(Stage<R>& L, const Staged<R, C, M, TMAX>& in, int T,
+                                             int tid) {
+    using TL = Tile<R, C>;
+    using KR = KeyRow<R>;
+    float* sd = reinterpret_cast<float*>(L.d);
+    float* sk = reinterpret_cast<float*>(L.k);
+    float* sq = reinterpret_cast<float*>(L.q);
 #pragma unroll
-    for (int p = 0; p < kPer; ++p) {
+    for (int p = 0; p < Staged<R, C, M, TMAX>::kPer; ++p) {
         const int idx = tid + p * TL::THREADS;
         if (idx < T * (kD / 4)) {
             const int t = idx >> 5;
             const int c4 = idx & 31;
             const int kp = t * KR::kStride + KR::at(c4 * 4);   // 4 keys never straddle a group
-            const float4 gg = in_g[p];
-            *reinterpret_cast<float4*>(sk + kp) = in_k[p];
+            const float4 gg = in.g[p];
+            *reinterpret_cast<float4*>(sk + kp) = in.k[p];
             *reinterpret_cast<float4*>(sd + kp) =
                 make_float4(decay_of(gg.x), decay_of(gg.y), decay_of(gg.z), decay_of(gg.w));
             if constexpr (M == Rows::kStash) {
-                L.ve[t * 32 + c4] = in_v[p];
+                L.ve[t * 32 + c4] = in.v[p];
             } else {
-                const float bt = in_b[p];
-                const float4 gv = in_v[p];
+                const float bt = in.b[p];
+                const float4 gv = in.v[p];
                 L.ve[t * 32 + c4] = make_float4(bt * gv.x, bt * gv.y, bt * gv.z, bt * gv.w);
                 if (c4 == 0) L.b[t] = bt;
             }
             if constexpr (M == Rows::kFull) {
-                const float4 gq = in_q[p];
+                const float4 gq = in.q[p];
                 *reinterpret_cast<float4*>(sq + kp) = make_float4(
                     gq.x * kInvSqrtD, gq.y * kInvSqrtD, gq.z * kInvSqrtD, gq.w * kInvSqrtD);
             }
@@ -334,9 +351,17 @@ __device__ __forceinline__ void stage(Stage<R>& L, const Src& src, int tid, F&& 
     }
 }
 
-// The sequential row loop over register state.  o_row(t) / e_row(t) give the
-// (wave-uniform) start of row t's output vectors; e rows are written only
-// when `e_out` is set.
+// A phase's rows from HBM into LDS; `between` runs after the row loads are
+// issued and before anything waits on them (the state loads go there).
+template <int R, int C, bool BF16, Rows M, int TMAX = kTMax, typename F>
+__device__ __forceinline__ void stage(Stage<R>& L, const Src& src, int tid, F&& between) {
+    Staged<R, C, M, TMAX> in;
+    stage_issue<R, C, BF16, M, TMAX>(in, src, tid);
+    between();
+    stage_fence<R, C, M, TMAX>(in);
+    stage_commit<R, C, M, TMAX>(L, in, src.T, tid);
+}
+
 template <int R, int C, Rows M>
 __device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], int T,
                                          float* o, float* e_out, size_t o0, size_t ostride,
@@ -420,12 +445,17 @@ __device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], in
 // previous round from the snapshot, then that committed state is stored),
 // then phase B (this launch's rows).  Without FUSED the state after phase B
 // is stored.
-template <int R, int C, bool BF16, Rows MA, Rows MB, bool TABLE>
-__global__ void __launch_bounds__((Tile<R, C>::THREADS)) __attribute__((amdgpu_waves_per_eu(4)))
+template <int R, int C, bool BF16, Rows MA, Rows MB, bool TABLE, bool DUAL>
+__global__ void __launch_bounds__((Tile<R, C>::THREADS))
+__attribute__((amdgpu_waves_per_eu(DUAL ? 2 : 4)))   // DUAL: LDS allows 2 workgroups per CU
 kda_scan_kernel(ScanArgs a) {
     using TL = Tile<R, C>;
     constexpr bool FUSED = MA != Rows::kNone;
-    __shared__ Stage<R> L;
+    static_assert(!DUAL || FUSED, "two stage areas serve the fused round only");
+    // DUAL: phase A and phase B rows each get an LDS area, so both are loaded
+    // up front (one memory round trip fewer per launch, twice the LDS)
+    __shared__ Stage<R> Ls[DUAL ? 2 : 1];
+    Stage<R>& L = Ls[0];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -492,14 +522,34 @@ kda_scan_kernel(ScanArgs a) {
         }
     };
 
+    Src p;   // the previous round's kept rows (fused round)
     if constexpr (FUSED) {
+        const size_t l = chain / a.H, h = chain % a.H;
+        p.q = nullptr; p.k = a.pk; p.v = a.pv; p.g = a.pg; p.beta = a.pbeta; p.e = a.pe;
+        p.row0 = (l * a.T_prev * a.H + h) * kD; p.rstride = static_cast<size_t>(a.H) * kD;
+        p.b0 = l * a.T_prev * a.H + h;           p.bstride = a.H;
+        p.T = a.keep;
+    }
+
+    if constexpr (DUAL) {
+        Stage<R>& LB = Ls[DUAL ? 1 : 0];
+        Staged<R, C, MA, kTMax> inA;
+        Staged<R, C, MB, kTMax> inB;
+        if (a.keep > 0) stage_issue<R, C, BF16, MA, kTMax>(inA, p, tid);
+        stage_issue<R, C, BF16, MB, kTMax>(inB, b, tid);
+        load_state();
+        if (a.keep > 0) stage_fence<R, C, MA, kTMax>(inA);
+        stage_fence<R, C, MB, kTMax>(inB);
         if (a.keep > 0) {
-            const size_t l = chain / a.H, h = chain % a.H;
-            Src p;
-            p.q = nullptr; p.k = a.pk; p.v = a.pv; p.g = a.pg; p.beta = a.pbeta; p.e = a.pe;
-            p.row0 = (l * a.T_prev * a.H + h) * kD; p.rstride = static_cast<size_t>(a.H) * kD;
-            p.b0 = l * a.T_prev * a.H + h;           p.bstride = a.H;
-            p.T = a.keep;
+            stage_commit<R, C, MA, kTMax>(L, inA, a.keep, tid);
+            run_rows<R, C, MA>(L, s, a.keep, nullptr, nullptr, 0, 0, ig, i0, j0);
+        }
+        store_state();         // the committed state: this round's snapshot
+        stage_commit<R, C, MB, kTMax>(LB, inB, b.T, tid);
+        run_rows<R, C, MB>(LB, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0);
+        return;
+    } else if constexpr (FUSED) {
+        if (a.keep > 0) {
             stage<R, C, BF16, MA>(L, p, tid, load_state);
             run_rows<R, C, MA>(L, s, a.keep, nullptr, nullptr, 0, 0, ig, i0, j0);
             __syncthreads();   // every wave is done with phase A's staged rows
@@ -891,13 +941,25 @@ __global__ void __launch_bounds__(64 * kTMax) kda_accept_finish_kernel(AcceptArg
     }
 }
 
+// Fused rounds of at most this many workgroups take two stage areas (about
+// 74 KB of LDS each, so two workgroups per CU): they fit in one pass.
+constexpr unsigned long long kDualStageMaxBlocks = 512;
+
 template <int C, bool BF16, Rows MA, Rows MB, bool TABLE>
 hipError_t launch_tiled(const ScanArgs& a, hipStream_t stream) {
     using TL = Tile<kKeysPerLane, C>;
     const unsigned long long blocks = static_cast<unsigned long long>(a.n_chains) * TL::BLOCKS;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    kda_scan_kernel<kKeysPerLane, C, BF16, MA, MB, TABLE>
-        <<<dim3(static_cast<unsigned>(blocks)), dim3(TL::THREADS), 0, stream>>>(a);
+    const dim3 grid(static_cast<unsigned>(blocks));
+    if constexpr (MA != Rows::kNone && C != 4) {
+        if (blocks <= kDualStageMaxBlocks) {
+            kda_scan_kernel<kKeysPerLane, C, BF16, MA, MB, TABLE, true>
+                <<<grid, dim3(TL::THREADS), 0, stream>>>(a);
+            return hipGetLastError();
+        }
+    }
+    kda_scan_kernel<kKeysPerLane, C, BF16, MA, MB, TABLE, false>
+        <<<grid, dim3(TL::THREADS), 0, stream>>>(a);
     return hipGetLastError();
 }
 
