@@ -470,14 +470,14 @@ def _per_layers(fn, L, chunk):
     return [fn(l0, min(l0 + chunk, L)) for l0 in range(0, L, chunk)]
 
 
-@pytest.mark.parametrize("chunk", [1, 4, 8])
-def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk):
+@pytest.mark.parametrize("chunk,bf16", [(1, False), (4, False), (8, False), (1, True), (4, True)])
+def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16):
     # 1 layer = 64 chains (4 workgroups per head), 4 layers = 256 chains
     # (2 per head), 8 layers = 512 chains (1 per head): every tiling must
     # give the bits of the 34-layer launch, for the scan, both replays and
     # the fused round
     L, T, H = 34, 15, 64
-    r = rand_rows(91, L, T, H)
+    r = rand_rows(91, L, T, H, bf16=bf16)
     rows = rows_dev(r)
     s0 = dev(rand_state(92, L, H, 0.5))
     s_full, o_full = scan(s0, rows)
