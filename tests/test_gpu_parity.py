@@ -419,9 +419,21 @@ def test_verify_round_equals_replay_then_scan(bf16, stash):
     assert bits_equal(x, ref_snap)
 
 
-def _fused_pipeline(w, rounds, heads, bf16=False, stash=True, Ts=None):
+def max_ulp(a, ref):
+    """Largest |a - ref| in units of ref's f32 spacing, over the elements at
+    least 1/256 of the largest magnitude (near zero the spacing is so fine that
+    any rounding reads as millions of ulp)."""
+    ref = np.asarray(ref, np.float32)
+    big = np.abs(ref) >= np.abs(ref).max() / 256
+    d = np.abs(np.asarray(a, np.float64) - ref.astype(np.float64))[big]
+    return float((d / np.spacing(np.abs(ref[big])).astype(np.float64)).max())
+
+
+def _fused_pipeline(w, rounds, heads, bf16=False, stash=True, Ts=None, log=None):
     """Run `rounds` fused verify rounds of workload w on the GPU and the matching
-    scan/replay chain on the oracle (sampled heads); compare every round."""
+    scan/replay chain on the oracle (sampled heads); compare every round.  With
+    `log` (a list), append (round, max |d| state, max ulp state, max |d| o,
+    max ulp o) per round."""
     js = synth.accepts(w.seed, max(rounds, 1), w.T - 1)
     snap = torch.zeros(w.L, w.H, D, D, device="cuda")
     ref = np.zeros((w.L, len(heads), D, D), np.float32)
@@ -441,8 +453,12 @@ def _fused_pipeline(w, rounds, heads, bf16=False, stash=True, Ts=None):
         snap = nxt
         sub = [x[:, :, heads] for x in rows_np(rw)]
         _, o_ref = oracle.scan_rows(ref, *sub, threads=oracle.max_threads())
-        assert maxerr(host(snap)[:, heads], ref) <= TOL, f"round {r} snapshot"
-        assert maxerr(host(o)[:, :, heads], o_ref) <= TOL, f"round {r} outputs"
+        got_s, got_o = host(snap)[:, heads], host(o)[:, :, heads]
+        if log is not None:
+            log.append((r, maxerr(got_s, ref), max_ulp(got_s, ref), maxerr(got_o, o_ref),
+                        max_ulp(got_o, o_ref)))
+        assert maxerr(got_s, ref) <= TOL, f"round {r} snapshot"
+        assert maxerr(got_o, o_ref) <= TOL, f"round {r} outputs"
         keep = int(js[r] % T) + 1
         ref = oracle.replay(ref, *sub, keep=keep, threads=oracle.max_threads())
         prev = (cur, e, keep)
@@ -455,6 +471,22 @@ def test_fused_pipeline_tiny_vs_oracle():
 
 def test_fused_pipeline_verify_k14_sampled_vs_oracle():
     _fused_pipeline(synth.WORKLOADS["verify_k14"], 3, SAMPLE_HEADS)
+
+
+def test_long_chain_drift_verify_k14_all_rounds():
+    # all 32 rounds of the headline workload, 480 rows per chain: the error
+    # against the oracle is logged per round so a drift over long chains shows
+    w = synth.WORKLOADS["verify_k14"]
+    log = []
+    _fused_pipeline(w, w.rounds, SAMPLE_HEADS, log=log)
+    print("\nround  max|d| state  max ulp state  max|d| o  max ulp o   (ulp over |ref| >= max/256)")
+    for r, ds, us, do, uo in log:
+        print(f"{r:5d}  {ds:12.3e}  {us:13.1f}  {do:8.3e}  {uo:9.1f}")
+    # a steady error, not one that grows with the chain: the last 8 rounds may
+    # not be worse than 4x the first 8
+    first = max(x[1] for x in log[:8])
+    last = max(x[1] for x in log[-8:])
+    assert last <= 4 * first + 1e-7, f"state error grows along the chain: {first} -> {last}"
 
 
 def test_fused_pipeline_serving_mix_bf16_sampled_vs_oracle():
