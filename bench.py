@@ -16,7 +16,8 @@ Two pipelines of the same round are timed in one run:
   split: kda_scan_rows out of place (the untouched input is the snapshot),
       then kda_replay of the kept rows when j < 14.
 
-Also timed: the same fused round issued per layer (34 launches of 64 heads
+Also timed: one TP=8 rank's share of the round (8 heads x 34 layers per
+launch); the same fused round issued per layer (34 launches of 64 heads
 replayed from one HIP graph); the batched-decode arm (15 sessions x 34 layers at t = 1); the
 bf16 serving mix as fused rounds with forced full accept, forced j = 0 and K
 drawn per round from {1, 3, 5, 7, 14}; kda_accept_greedy over one round's logits (t = 15, V = 150,000,
@@ -156,6 +157,8 @@ def main() -> int:
                     help="kda_snapshot launches of the full state, timed for the copy ceiling")
     ap.add_argument("--per-layer-rounds", type=int, default=16,
                     help="rounds of 34 per-layer fused launches replayed from a HIP graph")
+    ap.add_argument("--tp-share-rounds", type=int, default=32,
+                    help="fused rounds of one TP=8 rank's share (8 heads x 34 layers)")
     ap.add_argument("--batched-steps", type=int, default=8,
                     help="batched-decode steps (B=15, t=1, 34 layers) timed back to back")
     ap.add_argument("--serving-steps", type=int, default=32,
@@ -375,6 +378,37 @@ def main() -> int:
                              "head), 34 launches replayed from one HIP graph"}
         del graph
 
+    # one tensor-parallel rank's share at TP = 8: 8 heads x 34 layers per launch
+    tp_share = None
+    if args.tp_share_rounds > 0:
+        Ht = H // 8
+        r_tp = synth.rows(w.seed, 0, L, T, Ht)
+        tp_rows = [torch.from_numpy(r_tp[n]).cuda() for n in names]
+        tp_snap = torch.zeros(L, Ht, D, D, device="cuda")
+        tp_nxt = torch.empty_like(tp_snap)
+        tp_o = torch.empty(L, T, Ht, D, device="cuda")
+        tp_e = [torch.zeros(L, T, Ht, D, device="cuda") for _ in range(2)]
+
+        def tp_round():
+            kda.kda_verify_round(tp_snap, tp_nxt, (tp_rows[1], None, tp_rows[3], None, tp_e[0]),
+                                 8, *tp_rows, tp_o, e=tp_e[1])
+
+        for _ in range(3):
+            tp_round()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record(stream)
+        for _ in range(args.tp_share_rounds):
+            tp_round()
+        b.record(stream)
+        torch.cuda.synchronize()
+        tp_us = a.elapsed_time(b) * 1e3 / args.tp_share_rounds
+        tp_bytes = L * Ht * round_bytes_per_head(8, T)
+        tp_share = {"heads": Ht, "layers": L, "chains": L * Ht, "keep_prev": 8,
+                    "us_per_round": tp_us, "rows_heads_per_s": T * Ht * L / (tp_us * 1e-6),
+                    "gbps": tp_bytes / (tp_us * 1e-6) / 1e9}
+        del tp_rows, tp_snap, tp_nxt, tp_o, tp_e
+
     # batched-decode arm: 15 sessions x 34 layers x 64 heads, one row each, in place
     batched = None
     if args.batched_steps > 0:
@@ -588,6 +622,7 @@ def main() -> int:
         "accept": accept,
         "rollback_extras": rollback_extras,
         "per_layer_graph": per_layer,
+        "tp8_share": tp_share,
         "batched": batched,
         "serving_mix": serving,
         "copy_ceiling_gbps": copy_gbps,
