@@ -364,15 +364,20 @@ def main() -> int:
         for _ in range(2):
             graph.replay()
         torch.cuda.synchronize()
+        marks = [(ev(), ev()) for _ in range(args.per_layer_rounds)]
         a, b = ev(), ev()
         a.record(stream)
-        for _ in range(args.per_layer_rounds):
+        for m0, m1 in marks:
+            m0.record(stream)
             graph.replay()
+            m1.record(stream)
         b.record(stream)
         torch.cuda.synchronize()
         pl_us = a.elapsed_time(b) * 1e3 / args.per_layer_rounds
+        per_round = [m0.elapsed_time(m1) * 1e3 for m0, m1 in marks]
         per_layer = {"launches_per_round": L, "keep_prev": 8, "rounds": args.per_layer_rounds,
                      "us_per_round": pl_us, "us_per_layer": pl_us / L,
+                     "round_us": stats_us(per_round),
                      "rows_heads_per_s": T * H * L / (pl_us * 1e-6),
                      "note": "one kda_verify_round per layer (64 heads, 4 workgroups per "
                              "head), 34 launches replayed from one HIP graph"}
