@@ -453,33 +453,45 @@ def main() -> int:
             by_t[kk + 1] = [torch.from_numpy(r[n].view(np.int16)).cuda().view(torch.bfloat16)
                             for n in names]
         sv_state = [torch.zeros(L, H, D, D, device="cuda") for _ in range(2)]
-        sv_e = [torch.zeros(L * T * H * D, device="cuda") for _ in range(2)]
+        sv_e = [torch.zeros(L * T * H * D, device="cuda") for _ in range(6)]
         sv_o = torch.empty(L * T * H * D, device="cuda")
 
-        def serve(seq):
-            """seq: list of (T_round, keep of this round); returns (us, rows)."""
-            prev = None
+        def serve(seq, store_every=1):
+            """seq: list of (T_round, keep of this round); returns (us, rows).
+
+            store_every = n stores the committed state on every n-th round only;
+            the rounds in between are replayed from the last stored state by
+            kda_verify_round_multi (their stash planes stay alive until then)."""
             for warm in (True, False):
+                pending = []          # rounds replayed since the last stored state
+                base, other = sv_state
                 torch.cuda.synchronize()
                 a, b = ev(), ev()
                 a.record(stream)
                 for i, (tr, keep) in enumerate(seq):
                     rows = by_t[tr]
-                    e_cur = sv_e[i % 2][:L * tr * H * D].view(L, tr, H, D)
+                    e_cur = sv_e[i % 6][:L * tr * H * D].view(L, tr, H, D)
                     o_cur = sv_o[:L * tr * H * D].view(L, tr, H, D)
-                    snap, nxt = sv_state[i % 2], sv_state[(i + 1) % 2]
-                    if prev is None:
-                        kda.kda_verify_round(snap, nxt, None, 0, *rows, o_cur, e=e_cur)
+                    prevs = [(r[1], None, r[3], None, pe, kp) for r, pe, kp in pending]
+                    if store_every == 1:
+                        if prevs:
+                            kda.kda_verify_round(base, other, prevs[0][:5], prevs[0][5], *rows,
+                                                 o_cur, e=e_cur)
+                        else:
+                            kda.kda_verify_round(base, other, None, 0, *rows, o_cur, e=e_cur)
+                        store = True
                     else:
-                        p_rows, p_e, p_keep = prev
-                        kda.kda_verify_round(snap, nxt, (p_rows[1], None, p_rows[3], None, p_e),
-                                             p_keep, *rows, o_cur, e=e_cur)
-                    prev = (rows, e_cur, keep)
+                        store = i % store_every == store_every - 1
+                        kda.kda_verify_round_multi(base, other if store else None, prevs, *rows,
+                                                   o_cur, e=e_cur)
+                    if store:
+                        base, other = other, base
+                        pending = []
+                    pending.append((rows, e_cur, keep))
                 b.record(stream)
                 torch.cuda.synchronize()
                 if not warm:
                     return a.elapsed_time(b) * 1e3, sum(tr for tr, _ in seq)
-                prev = None
 
         n = args.serving_steps
         rng = np.random.default_rng(wsv.seed)
@@ -493,6 +505,11 @@ def main() -> int:
             us, nrows = serve(seq)
             serving[name] = {"us_per_round": us / n,
                              "rows_heads_per_s": nrows * H * L / (us * 1e-6)}
+        # the K mix with the committed state stored every second / fourth round only
+        for every in (2, 4):
+            us, nrows = serve(seqs["mix"], store_every=every)
+            serving[f"mix_store_every_{every}"] = {
+                "us_per_round": us / n, "rows_heads_per_s": nrows * H * L / (us * 1e-6)}
         del by_t, sv_state, sv_e, sv_o
 
     # greedy accept of one K=14 round over a 150,000-entry vocabulary (f32 logits)

@@ -39,6 +39,13 @@ KDA_IN_BF16 = 1
 ACCEPT_WORK_BYTES = 12288
 NO_TOKEN = 0xFFFFFFFF
 RING_ROWS = 3
+MAX_PREV_ROUNDS = 4
+
+
+class _PrevRound(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("g", ctypes.c_void_p),
+                ("beta", ctypes.c_void_p), ("e", ctypes.c_void_p), ("T", ctypes.c_int),
+                ("keep", ctypes.c_int)]
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 _lib = None
@@ -76,9 +83,12 @@ def load():
     lib.kda_conv_reroll.argtypes = [p, p, p, i, i, i, ctypes.c_longlong, i, p]
     lib.kda_copy_batch.argtypes = [p, i, ctypes.c_longlong, p]
     lib.kda_row_ops.argtypes = [p] * 11 + [i, i, i, i, p]
+    lib.kda_verify_round_multi.argtypes = [p, p, ctypes.POINTER(_PrevRound), i, p, p, p, p, p,
+                                           p, p, i, i, i, i, p]
     for fn in (lib.kda_scan_rows, lib.kda_snapshot, lib.kda_replay, lib.kda_scan_batched,
                lib.kda_verify_round, lib.kda_accept_greedy, lib.kda_conv_reroll,
-               lib.kda_copy_batch, lib.kda_row_ops, lib.kda_abi_version):
+               lib.kda_copy_batch, lib.kda_row_ops, lib.kda_verify_round_multi,
+               lib.kda_abi_version):
         fn.restype = i
     lib.kda_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -242,6 +252,40 @@ def kda_verify_round(snap_prev, snap_out, prev, keep: int, q, k, v, g, beta, o, 
     _check(lib.kda_verify_round(
         _dev(snap_prev, "snap_prev"), _dev(snap_out, "snap_out"), _dev(pk, "pk"), _dev(pv, "pv"),
         _dev(pg, "pg"), _dev(pb, "pbeta"), _dev(pe, "pe"), int(T_prev), int(keep), _dev(q, "q"),
+        _dev(k, "k"), _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"),
+        _dev(e, "e"), L, T, H, dt, _stream(stream)))
+
+
+def kda_verify_round_multi(snap_base, snap_out, prevs, q, k, v, g, beta, o, e=None,
+                           stream=None) -> None:
+    """A fused round replaying several earlier rounds.
+
+    prevs: up to 4 tuples (k, v, g, beta, e, keep), oldest first, each an earlier
+    round's retained rows ([L][T_i][H][D]; v/beta may be None when its stash e is
+    given) and how many of them to replay.  snap_base is the committed state
+    before prevs[0].  snap_out (or None to skip the store) receives the
+    committed state after all of them; o (and e) this round's outputs.
+    """
+    lib = load()
+    L, T, H = _rows_shape(q, k, v, g, beta)
+    dt = _in_dtype((q, k, v, g, beta))
+    _state(snap_base, (L, H, D, D), "snap_base")
+    if snap_out is not None:
+        _state(snap_out, (L, H, D, D), "snap_out")
+    _plane(o, (L, T, H, D), "o")
+    _plane(e, (L, T, H, D), "e")
+    if len(prevs) > MAX_PREV_ROUNDS:
+        raise ValueError(f"at most {MAX_PREV_ROUNDS} earlier rounds")
+    arr = (_PrevRound * max(1, len(prevs)))()
+    for n, (pk, pv, pg, pb, pe, keep) in enumerate(prevs):
+        Lp, Tp, Hp, pdt = _kept_rows(pk, pv, pg, pb, pe, f"prevs[{n}]")
+        if (Lp, Hp) != (L, H) or pdt != dt:
+            raise ValueError(f"prevs[{n}] does not match this round's L, H, dtype")
+        ptr = lambda t, nm: None if t is None else _dev(t, f"prevs[{n}] {nm}").value
+        arr[n] = _PrevRound(ptr(pk, "k"), ptr(pv, "v"), ptr(pg, "g"), ptr(pb, "beta"),
+                            ptr(pe, "e"), Tp, int(keep))
+    _check(lib.kda_verify_round_multi(
+        _dev(snap_base, "snap_base"), _dev(snap_out, "snap_out"), arr, len(prevs), _dev(q, "q"),
         _dev(k, "k"), _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"),
         _dev(e, "e"), L, T, H, dt, _stream(stream)))
 
@@ -419,4 +463,5 @@ __all__ = [
     "kda_replay", "kda_scan_batched", "kda_verify_round", "state_table", "kda_abi_version",
     "kda_last_error", "kda_accept_greedy", "accept_workspace", "ACCEPT_WORK_BYTES", "NO_TOKEN",
     "kda_conv_reroll", "copy_table", "kda_copy_batch", "RING_ROWS", "kda_row_ops",
+    "kda_verify_round_multi", "MAX_PREV_ROUNDS",
 ]

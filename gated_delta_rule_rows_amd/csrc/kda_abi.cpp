@@ -114,6 +114,88 @@ static_assert(sizeof(kda::AcceptScratch) <= KDA_ACCEPT_WORK_BYTES, "accept works
 static_assert(kda::kNoToken == KDA_NO_TOKEN, "one sentinel");
 static_assert(kda::kRingRows == KDA_CONV_RING_ROWS, "one ring depth");
 
+// The fused round behind kda_verify_round and kda_verify_round_multi.
+int verify_round(const char* fn, bool one_round, const float* snap_base, float* snap_out,
+                 const kda_prev_round* prev, int n_prev, const void* q, const void* k,
+                 const void* v, const void* g, const void* beta, float* o, float* e, int L,
+                 int T, int H, int in_dtype, void* stream) {
+    int rc;
+    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H)) ||
+        (rc = check_rows(fn, "T", T)))
+        return rc;
+    if (n_prev < 0 || n_prev > KDA_MAX_PREV_ROUNDS)
+        return refuse(KDA_ERR_RANGE, "%s: n_prev=%d outside 0..%d", fn, n_prev,
+                      KDA_MAX_PREV_ROUNDS);
+    if (n_prev > 0 && !prev) return refuse(KDA_ERR_ARG, "%s: prev is NULL", fn);
+    const unsigned long long chains = static_cast<unsigned long long>(L) * H;
+    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
+    const unsigned long long rows = chains * T;
+    // earlier rounds: validate each, keep those with rows to replay
+    kda::ScanArgs a{};
+    int stash = -1;   // all replayed rounds read the stash plane (1) or none does (0)
+    Span in[6 + 5 * KDA_MAX_PREV_ROUNDS];
+    int n_in = 0;
+    in[n_in++] = {one_round ? "snap_prev" : "snap_base", snap_base, chains * kStateBytes, 16,
+                  false};
+    in[n_in++] = {"q", q, rows * kRowElems * es, 16, false};
+    in[n_in++] = {"k", k, rows * kRowElems * es, 16, false};
+    in[n_in++] = {"v", v, rows * kRowElems * es, 16, false};
+    in[n_in++] = {"g", g, rows * kRowElems * es, 16, false};
+    in[n_in++] = {"beta", beta, rows * es, es, false};
+    static const char* const one[5] = {"pk", "pg", "pv", "pbeta", "pe"};
+    static const char* const names[KDA_MAX_PREV_ROUNDS][5] = {
+        {"prev[0].k", "prev[0].g", "prev[0].v", "prev[0].beta", "prev[0].e"},
+        {"prev[1].k", "prev[1].g", "prev[1].v", "prev[1].beta", "prev[1].e"},
+        {"prev[2].k", "prev[2].g", "prev[2].v", "prev[2].beta", "prev[2].e"},
+        {"prev[3].k", "prev[3].g", "prev[3].v", "prev[3].beta", "prev[3].e"},
+    };
+    for (int i = 0; i < n_prev; ++i) {
+        const kda_prev_round& pr = prev[i];
+        if (pr.T < 1 || pr.T > KDA_T_MAX)
+            return refuse(KDA_ERR_RANGE, "%s: prev[%d].T=%d outside 1..%d", fn, i, pr.T, KDA_T_MAX);
+        if (pr.keep < 0 || pr.keep > pr.T)
+            return refuse(KDA_ERR_RANGE, "%s: prev[%d].keep=%d outside 0..=%d", fn, i, pr.keep,
+                          pr.T);
+        if (pr.keep == 0) continue;   // nothing of that round is replayed
+        const int st = pr.e != nullptr ? 1 : 0;
+        if (stash >= 0 && st != stash)
+            return refuse(KDA_ERR_ARG,
+                          st ? "%s: prev[%d] brings the stash plane e and an earlier replayed "
+                               "round does not (all or none)"
+                             : "%s: prev[%d] has no stash plane e and an earlier replayed round "
+                               "has one (all or none)",
+                          fn, i);
+        stash = st;
+        const unsigned long long prow = chains * pr.T;
+        const char* const* nm = one_round ? one : names[i];
+        in[n_in++] = {nm[0], pr.k, prow * kRowElems * es, 16, false};
+        in[n_in++] = {nm[1], pr.g, prow * kRowElems * es, 16, false};
+        if (st) {
+            in[n_in++] = {nm[4], pr.e, prow * kRowElems * 4, 16, false};
+        } else {
+            in[n_in++] = {nm[2], pr.v, prow * kRowElems * es, 16, false};
+            in[n_in++] = {nm[3], pr.beta, prow * es, es, false};
+        }
+        kda::PrevRows& d = a.prev[a.n_prev++];
+        d.k = pr.k; d.g = pr.g; d.T = pr.T; d.keep = pr.keep;
+        if (st) d.e = pr.e; else { d.v = pr.v; d.beta = pr.beta; }
+    }
+    const Span out[] = {
+        {"snap_out", snap_out, chains * kStateBytes, 16, true},
+        {"o", o, rows * kRowElems * 4, 16, false},
+        {"e", e, rows * kRowElems * 4, 16, true},
+    };
+    if ((rc = check_spans(fn, in, n_in)) || (rc = check_spans(fn, out, 3)) ||
+        (rc = check_alias(fn, out, 3, in, n_in, &out[0], &in[0])))
+        return rc;
+    a.s_in = snap_base; a.s_out = snap_out;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.e_out = e;
+    a.n_chains = static_cast<long long>(chains); a.H = H; a.T = T; a.T_stride = T;
+    const kda::Launch kind = stash == 1 ? kda::Launch::kRoundStash : kda::Launch::kRound;
+    return launched(fn, kda::launch_scan(a, kind, in_dtype == KDA_IN_BF16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -248,51 +330,23 @@ int kda_verify_round(const float* snap_prev, float* snap_out, const void* pk, co
                      const void* q, const void* k, const void* v, const void* g, const void* beta,
                      float* o, float* e, int L, int T, int H, int in_dtype, void* stream) {
     const char* fn = "kda_verify_round";
-    int rc;
-    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H)) ||
-        (rc = check_rows(fn, "T", T)))
-        return rc;
     if (T_prev < 0 || T_prev > KDA_T_MAX)
         return refuse(KDA_ERR_RANGE, "%s: T_prev=%d outside 0..%d", fn, T_prev, KDA_T_MAX);
     if (keep < 0 || keep > T_prev)
         return refuse(KDA_ERR_RANGE, "%s: keep=%d outside 0..=%d (previous-round rows to replay)",
                       fn, keep, T_prev);
-    const unsigned long long chains = static_cast<unsigned long long>(L) * H;
-    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
-    const unsigned long long prow = chains * T_prev;
-    const unsigned long long rows = chains * T;
-    const bool replay = keep > 0;
-    const bool stash = replay && pe != nullptr;
-    const Span in[] = {
-        {"snap_prev", snap_prev, chains * kStateBytes, 16, false},
-        {"pk", replay ? pk : nullptr, prow * kRowElems * es, 16, !replay},
-        {"pg", replay ? pg : nullptr, prow * kRowElems * es, 16, !replay},
-        {"pv", replay && !stash ? pv : nullptr, prow * kRowElems * es, 16, !replay || stash},
-        {"pbeta", replay && !stash ? pbeta : nullptr, prow * es, es, !replay || stash},
-        {"pe", stash ? pe : nullptr, prow * kRowElems * 4, 16, true},
-        {"q", q, rows * kRowElems * es, 16, false},
-        {"k", k, rows * kRowElems * es, 16, false},
-        {"v", v, rows * kRowElems * es, 16, false},
-        {"g", g, rows * kRowElems * es, 16, false},
-        {"beta", beta, rows * es, es, false},
-    };
-    const Span out[] = {
-        {"snap_out", snap_out, chains * kStateBytes, 16, false},
-        {"o", o, rows * kRowElems * 4, 16, false},
-        {"e", e, rows * kRowElems * 4, 16, true},
-    };
-    if ((rc = check_spans(fn, in, 11)) || (rc = check_spans(fn, out, 3)) ||
-        (rc = check_alias(fn, out, 3, in, 11, &out[0], &in[0])))
-        return rc;
-    kda::ScanArgs a{};
-    a.s_in = snap_prev; a.s_out = snap_out;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.e_out = e;
-    a.pk = pk; a.pv = pv; a.pg = pg; a.pbeta = pbeta; a.pe = stash ? pe : nullptr;
-    a.T_prev = T_prev; a.keep = keep;
-    a.n_chains = static_cast<long long>(chains); a.H = H; a.T = T; a.T_stride = T;
-    const kda::Launch kind = stash ? kda::Launch::kRoundStash : kda::Launch::kRound;
-    return launched(fn, kda::launch_scan(a, kind, in_dtype == KDA_IN_BF16,
-                                         static_cast<hipStream_t>(stream)));
+    if (!snap_out) return refuse(KDA_ERR_ARG, "%s: snap_out is NULL", fn);
+    const kda_prev_round pr = {pk, pv, pg, pbeta, pe, T_prev, keep};
+    return verify_round(fn, true, snap_prev, snap_out, &pr, keep > 0 ? 1 : 0, q, k, v, g, beta,
+                        o, e, L, T, H, in_dtype, stream);
+}
+
+int kda_verify_round_multi(const float* snap_base, float* snap_out, const kda_prev_round* prev,
+                           int n_prev, const void* q, const void* k, const void* v,
+                           const void* g, const void* beta, float* o, float* e, int L, int T,
+                           int H, int in_dtype, void* stream) {
+    return verify_round("kda_verify_round_multi", false, snap_base, snap_out, prev, n_prev, q, k,
+                        v, g, beta, o, e, L, T, H, in_dtype, stream);
 }
 
 int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dtype,

@@ -522,41 +522,57 @@ kda_scan_kernel(ScanArgs a) {
         }
     };
 
-    Src p;   // the previous round's kept rows (fused round)
-    if constexpr (FUSED) {
+    // an earlier round's kept rows (fused round), in that round's layout
+    auto prev_src = [&](int i) {
+        const PrevRows& pr = a.prev[i];
         const size_t l = chain / a.H, h = chain % a.H;
-        p.q = nullptr; p.k = a.pk; p.v = a.pv; p.g = a.pg; p.beta = a.pbeta; p.e = a.pe;
-        p.row0 = (l * a.T_prev * a.H + h) * kD; p.rstride = static_cast<size_t>(a.H) * kD;
-        p.b0 = l * a.T_prev * a.H + h;           p.bstride = a.H;
-        p.T = a.keep;
-    }
+        Src p;
+        p.q = nullptr; p.k = pr.k; p.v = pr.v; p.g = pr.g; p.beta = pr.beta; p.e = pr.e;
+        p.row0 = (l * pr.T * a.H + h) * kD; p.rstride = static_cast<size_t>(a.H) * kD;
+        p.b0 = l * pr.T * a.H + h;           p.bstride = a.H;
+        p.T = pr.keep;
+        return p;
+    };
 
     if constexpr (DUAL) {
+        // at most one earlier round (the launcher's rule)
         Stage<R>& LB = Ls[DUAL ? 1 : 0];
         Staged<R, C, MA, kTMax> inA;
         Staged<R, C, MB, kTMax> inB;
-        if (a.keep > 0) stage_issue<R, C, BF16, MA, kTMax>(inA, p, tid);
+        const bool replay = a.n_prev > 0;
+        Src p;
+        if (replay) {
+            p = prev_src(0);
+            stage_issue<R, C, BF16, MA, kTMax>(inA, p, tid);
+        }
         stage_issue<R, C, BF16, MB, kTMax>(inB, b, tid);
         load_state();
-        if (a.keep > 0) stage_fence<R, C, MA, kTMax>(inA);
+        if (replay) stage_fence<R, C, MA, kTMax>(inA);
         stage_fence<R, C, MB, kTMax>(inB);
-        if (a.keep > 0) {
-            stage_commit<R, C, MA, kTMax>(L, inA, a.keep, tid);
-            run_rows<R, C, MA>(L, s, a.keep, nullptr, nullptr, 0, 0, ig, i0, j0);
+        if (replay) {
+            stage_commit<R, C, MA, kTMax>(L, inA, p.T, tid);
+            run_rows<R, C, MA>(L, s, p.T, nullptr, nullptr, 0, 0, ig, i0, j0);
         }
-        store_state();         // the committed state: this round's snapshot
+        if (a.s_out) store_state();   // the committed state: this round's snapshot
         stage_commit<R, C, MB, kTMax>(LB, inB, b.T, tid);
         run_rows<R, C, MB>(LB, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0);
         return;
     } else if constexpr (FUSED) {
-        if (a.keep > 0) {
-            stage<R, C, BF16, MA>(L, p, tid, load_state);
-            run_rows<R, C, MA>(L, s, a.keep, nullptr, nullptr, 0, 0, ig, i0, j0);
-            __syncthreads();   // every wave is done with phase A's staged rows
+        if (a.n_prev > 0) {
+            const Src p0 = prev_src(0);
+            stage<R, C, BF16, MA>(L, p0, tid, load_state);
+            run_rows<R, C, MA>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+            __syncthreads();   // every wave is done with these staged rows
+            for (int i = 1; i < a.n_prev; ++i) {
+                const Src pi = prev_src(i);
+                stage<R, C, BF16, MA>(L, pi, tid, [] {});
+                run_rows<R, C, MA>(L, s, pi.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+                __syncthreads();
+            }
         } else {
             load_state();
         }
-        store_state();         // the committed state: this round's snapshot
+        if (a.s_out) store_state();   // the committed state: this round's snapshot
         stage<R, C, BF16, MB>(L, b, tid, [] {});
     } else {
         // the batched arm always scans one row per session
@@ -952,7 +968,7 @@ hipError_t launch_tiled(const ScanArgs& a, hipStream_t stream) {
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blocks));
     if constexpr (MA != Rows::kNone && C != 4) {
-        if (blocks <= kDualStageMaxBlocks) {
+        if (blocks <= kDualStageMaxBlocks && a.n_prev <= 1) {
             kda_scan_kernel<kKeysPerLane, C, BF16, MA, MB, TABLE, true>
                 <<<grid, dim3(TL::THREADS), 0, stream>>>(a);
             return hipGetLastError();

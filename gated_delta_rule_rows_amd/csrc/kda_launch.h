@@ -13,6 +13,20 @@ constexpr int kD = 128;        // head dim: d_k = d_v
 constexpr int kTMax = 15;      // verify rows per launch
 constexpr int kBMax = 15;      // batched-decode sessions
 
+constexpr int kMaxPrev = 4;   // earlier rounds one fused launch can replay
+
+// The retained rows of an earlier round: k, g and either e (the stash plane)
+// or v and beta, in that round's layout [L][T][H][128].
+struct PrevRows {
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* e;
+    int T;      // rows per layer in that round's layout
+    int keep;   // rows to replay, 1..T
+};
+
 // One launch of the row kernel.  Either the contiguous layout
 //   state [chain][128][128], chain = l*H + h, rows [L][T_stride][H][128]
 // or (batched) the table layout
@@ -30,14 +44,10 @@ struct ScanArgs {
     const float* e_in;   // stash plane read by a stash replay
     float* o;            // per-row outputs (full rows)
     float* e_out;        // stash plane written by a scan, or nullptr
-    // the previous round's rows (fused verify round only)
-    const void* pk;
-    const void* pv;
-    const void* pg;
-    const void* pbeta;
-    const float* pe;
-    int T_prev;          // rows per layer in the previous round's layout
-    int keep;            // previous-round rows to replay (0 = none)
+    // fused verify round only: earlier rounds' kept rows, replayed in order
+    // from s_in before this launch's rows (entries with keep = 0 left out)
+    PrevRows prev[kMaxPrev];
+    int n_prev;
     long long n_chains;  // (layer, head) or (layer, session, head) chains
     int H;
     int T;               // rows this launch runs
@@ -51,8 +61,8 @@ enum class Launch {
     kReplayStash,   // keep rows from the stash plane e, state stored
     kBatchedOut,    // batched arm, one row per session, o
     kBatchedState,  // batched arm, state only
-    kRound,         // fused verify round: replay (recomputed), store, scan for o
-    kRoundStash,    // fused verify round: replay from the stash, store, scan for o
+    kRound,         // fused verify round: replay (recomputed), store (if s_out), scan for o
+    kRoundStash,    // fused verify round: replay from the stash, store (if s_out), scan for o
 };
 
 hipError_t launch_scan(const ScanArgs& a, Launch kind, bool bf16, hipStream_t stream);

@@ -52,10 +52,11 @@ extern "C" {
 #define KDA_HEAD_DIM 128   /* d_k = d_v; glm5_spec_ppn_gate.rs fixture head_dim */
 #define KDA_T_MAX 15       /* verify rows per round: K + 1 <= 15 (glm_spec.rs, WALK-REUSE) */
 #define KDA_B_MAX 15       /* batched-decode sessions per step (same knee) */
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 #define KDA_ACCEPT_WORK_BYTES 12288   /* workspace of kda_accept_greedy */
 #define KDA_NO_TOKEN 0xFFFFFFFFu      /* argmax slot of a logits row holding a NaN */
 #define KDA_CONV_RING_ROWS 3          /* short-conv history: kernel size 4 keeps 3 raw rows */
+#define KDA_MAX_PREV_ROUNDS 4         /* earlier rounds one kda_verify_round_multi can replay */
 
 enum { KDA_IN_F32 = 0, KDA_IN_BF16 = 1 };
 
@@ -175,6 +176,43 @@ int kda_verify_round(const float* snap_prev, float* snap_out, const void* pk, co
                      const void* q, const void* k, const void* v, const void* g,
                      const void* beta, float* o, float* e, int L, int T, int H, int in_dtype,
                      void* stream);
+
+/*
+ * The retained rows of an earlier verify round, for kda_verify_round_multi:
+ * k, g and either its stash plane e or v and beta, all in that round's
+ * layout [L][T][H][128] ([L][T][H] for beta), in the launch's in_dtype.
+ */
+typedef struct {
+    const void* k;
+    const void* v;      /* may be NULL when e is given */
+    const void* g;
+    const void* beta;   /* may be NULL when e is given */
+    const float* e;     /* that round's stash plane, or NULL */
+    int T;              /* that round's rows per layer, 1..KDA_T_MAX */
+    int keep;           /* its rows to replay, 0..T (0: nothing of that round) */
+} kda_prev_round;
+
+/*
+ * A fused verify round that replays several earlier rounds.
+ *   glm_spec.rs (0.123.0), ROLLBACK: a rolled-back state is rebuilt by
+ *   replaying kept rows from a snapshot, and the replay is the scan's own row
+ *   program.  Extending kda_verify_round, the snapshot may be older than the
+ *   previous round: snap_base is the committed state before prev[0], and the
+ *   kept rows of prev[0], prev[1], ... are replayed in that order before this
+ *   round's rows are scanned.  A caller can so store the committed state only
+ *   every few rounds (snap_out = NULL in between) and save that write, which
+ *   dominates the HBM bytes of a round at small K.
+ *   snap_out : the committed state after all n_prev rounds (this round's
+ *              snapshot), or NULL to not store it.  May be snap_base.
+ *   prev     : HOST array of n_prev descriptors, 0 <= n_prev <= 4; either
+ *              every replayed round (keep > 0) brings e or none does.
+ *   The rest as for kda_verify_round.  Bit for bit, the result equals
+ *   kda_replay of each round in turn, then kda_scan_rows of this round.
+ */
+int kda_verify_round_multi(const float* snap_base, float* snap_out, const kda_prev_round* prev,
+                           int n_prev, const void* q, const void* k, const void* v,
+                           const void* g, const void* beta, float* o, float* e, int L, int T,
+                           int H, int in_dtype, void* stream);
 
 /*
  * Greedy accept of one verify round.

@@ -42,7 +42,8 @@ def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"kda_scan_rows", "kda_snapshot", "kda_replay", "kda_scan_batched",
                           "kda_verify_round", "kda_accept_greedy", "kda_conv_reroll",
-                          "kda_copy_batch", "kda_row_ops", "kda_last_error", "kda_abi_version"}
+                          "kda_copy_batch", "kda_row_ops", "kda_verify_round_multi",
+                          "kda_last_error", "kda_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -56,6 +57,7 @@ def test_abi_version_matches_header(lib):
     assert re.search(r"#define\s+KDA_NO_TOKEN\s+0xFFFFFFFFu", open(HEADER).read())
     assert kda.NO_TOKEN == 0xFFFFFFFF
     assert _header_constant("KDA_CONV_RING_ROWS") == kda.RING_ROWS == 3
+    assert _header_constant("KDA_MAX_PREV_ROUNDS") == kda.MAX_PREV_ROUNDS == 4
 
 
 class Bufs:
@@ -351,6 +353,38 @@ def test_row_ops_alignment_and_alias(lib, b):
     # rows run in parallel and the early ones read ring_in: no in-place ring
     assert _ops(lib, b, ring_out=b["snap"]) == ERR_ALIAS and "ring_out overlaps ring_in" in _msg(lib)
     assert _ops(lib, b, ring_out=off("snap", 64)) == ERR_ALIAS
+
+
+def _multi(lib, b, prevs, **kw):
+    arr = (kda._PrevRound * max(1, len(prevs)))(*prevs)
+    a = dict(base=b["snap"], out=b["s_out"], n=len(prevs), q=b["q"], k=b["k"], v=b["v"],
+             g=b["g"], beta=b["beta"], o=b["o"], e=None, L=2, T=8, H=2, dt=0)
+    a.update(kw)
+    return lib.kda_verify_round_multi(a["base"], a["out"], arr, a["n"], a["q"], a["k"], a["v"],
+                                      a["g"], a["beta"], a["o"], a["e"], a["L"], a["T"], a["H"],
+                                      a["dt"], None)
+
+
+def _pr(b, T=8, keep=3, stash=True):
+    return kda._PrevRound(b.addr["k"], None if stash else b.addr["v"], b.addr["g"],
+                          None if stash else b.addr["beta"], b.addr["ptrs"] if stash else None,
+                          T, keep)
+
+
+def test_verify_round_multi_refusals(lib, b):
+    assert _multi(lib, b, [_pr(b)] * 4, n=5) == ERR_RANGE and "n_prev=5" in _msg(lib)
+    assert _multi(lib, b, [], n=-1) == ERR_RANGE
+    assert _multi(lib, b, [_pr(b, T=16)]) == ERR_RANGE and "prev[0].T=16" in _msg(lib)
+    assert _multi(lib, b, [_pr(b), _pr(b, T=4, keep=5)]) == ERR_RANGE and "prev[1].keep=5" in _msg(lib)
+    assert _multi(lib, b, [_pr(b), _pr(b, stash=False)]) == ERR_ARG and "all or none" in _msg(lib)
+    # a round with nothing kept is not read: its mismatch does not matter, the alias does
+    assert _multi(lib, b, [_pr(b), _pr(b, keep=0, stash=False)], o=b["k"]) == ERR_ALIAS
+    assert _multi(lib, b, [_pr(b)], out=ctypes.c_void_p(b.addr["snap"] + 64)) == ERR_ALIAS
+    bad = kda._PrevRound(None, None, b.addr["g"], None, b.addr["ptrs"], 8, 2)
+    assert _multi(lib, b, [bad]) == ERR_ARG and "prev[0].k is NULL" in _msg(lib)
+    arr_null = lib.kda_verify_round_multi(b["snap"], b["s_out"], None, 1, b["q"], b["k"], b["v"],
+                                          b["g"], b["beta"], b["o"], None, 2, 8, 2, 0, None)
+    assert arr_null == ERR_ARG and "prev is NULL" in _msg(lib)
 
 
 def test_snapshot_refusals(lib, b):

@@ -545,3 +545,66 @@ def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16):
     for name, a, b in zip(("state", "o", "replay", "stash replay", "round snap", "round o"),
                           got, (s_full, o_full, rep_full, reps_full, snap_full, o2_full)):
         assert bits_equal(a, b), f"{name} differs at chunk {chunk}"
+
+
+# ----------------------------------------------------------------- multi-round replay
+
+@pytest.mark.parametrize("L,keeps,store,stash,bf16", [
+    (2, [], True, True, False),              # no earlier round: a plain scan from snap_base
+    (2, [5], True, True, False),             # one round, two stage areas
+    (2, [3, 0, 8], False, True, False),      # a round with nothing kept is skipped
+    (2, [2, 7], True, False, True),          # recomputed replay, bf16
+    (12, [4, 1, 12, 9], True, True, False),  # 768 chains, one workgroup per head
+    (12, [6, 6], False, False, False),
+])
+def test_verify_round_multi_equals_replays_then_scan(L, keeps, store, stash, bf16):
+    H, T = 64, 15
+    s0 = dev(rand_state(71, L, H, 0.5))
+    prevs, ref = [], s0.clone()
+    for n, keep in enumerate(keeps):
+        Tn = [15, 9, 12, 15][n]
+        r = rows_dev(rand_rows(72 + n, L, Tn, H, bf16=bf16))
+        e_n = torch.empty(L, Tn, H, D, device="cuda")
+        kda.kda_scan_rows(ref, torch.empty_like(ref), *r, o=None, e=e_n)
+        if keep:
+            nxt = torch.empty_like(ref)
+            if stash:
+                kda.kda_replay(ref, nxt, r[1], None, r[3], None, keep=keep, e=e_n)
+            else:
+                kda.kda_replay(ref, nxt, *r[1:], keep=keep)
+            ref = nxt
+        if stash:
+            prevs.append((r[1], None, r[3], None, e_n, keep))
+        else:
+            prevs.append((r[1], r[2], r[3], r[4], None, keep))
+    cur = rows_dev(rand_rows(80, L, T, H, bf16=bf16))
+    _, o_ref, e_ref = scan_e(ref, cur)
+    snap_out = torch.empty_like(s0) if store else None
+    o = torch.empty(L, T, H, D, device="cuda")
+    e = torch.empty(L, T, H, D, device="cuda")
+    kda.kda_verify_round_multi(s0, snap_out, prevs, *cur, o, e=e)
+    torch.cuda.synchronize()
+    if store:
+        assert bits_equal(snap_out, ref)
+    assert bits_equal(o, o_ref) and bits_equal(e, e_ref)
+
+
+def test_verify_round_multi_in_place_and_refusals():
+    L, H, T = 2, 8, 6
+    s0 = dev(rand_state(81, L, H, 0.5))
+    r1 = rows_dev(rand_rows(82, L, 10, H))
+    e1 = torch.empty(L, 10, H, D, device="cuda")
+    kda.kda_scan_rows(s0, torch.empty_like(s0), *r1, o=None, e=e1)
+    cur = rows_dev(rand_rows(83, L, T, H))
+    ref = torch.empty_like(s0)
+    kda.kda_replay(s0, ref, r1[1], None, r1[3], None, keep=4, e=e1)
+    x = s0.clone()
+    o = torch.empty(L, T, H, D, device="cuda")
+    kda.kda_verify_round_multi(x, x, [(r1[1], None, r1[3], None, e1, 4)], *cur, o)
+    torch.cuda.synchronize()
+    assert bits_equal(x, ref)
+    with pytest.raises(kda.KdaError, match="all or none"):
+        kda.kda_verify_round_multi(s0, None, [(r1[1], None, r1[3], None, e1, 4),
+                                              (r1[1], r1[2], r1[3], r1[4], None, 2)], *cur, o)
+    with pytest.raises(ValueError, match="at most 4"):
+        kda.kda_verify_round_multi(s0, None, [(r1[1], None, r1[3], None, e1, 1)] * 5, *cur, o)
