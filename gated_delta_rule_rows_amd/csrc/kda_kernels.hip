@@ -446,15 +446,11 @@ __device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], in
 // then phase B (this launch's rows).  Without FUSED the state after phase B
 // is stored.
 template <int R, int C, bool BF16, Rows MA, Rows MB, bool TABLE, bool DUAL>
-__global__ void __launch_bounds__((Tile<R, C>::THREADS))
-__attribute__((amdgpu_waves_per_eu(DUAL ? 2 : 4)))   // DUAL: LDS allows 2 workgroups per CU
-kda_scan_kernel(ScanArgs a) {
+__device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R>* Ls, size_t chain,
+                                           int blk) {
     using TL = Tile<R, C>;
     constexpr bool FUSED = MA != Rows::kNone;
     static_assert(!DUAL || FUSED, "two stage areas serve the fused round only");
-    // DUAL: phase A and phase B rows each get an LDS area, so both are loaded
-    // up front (one memory round trip fewer per launch, twice the LDS)
-    __shared__ Stage<R> Ls[DUAL ? 2 : 1];
     Stage<R>& L = Ls[0];
 
     const int tid = threadIdx.x;
@@ -463,9 +459,7 @@ kda_scan_kernel(ScanArgs a) {
     const int ig = lane % TL::NI;
     const int jg = lane / TL::NI;
     const int i0 = ig * R;
-    // --- where this chain lives: workgroup blk of the head's TL::BLOCKS
-    const size_t chain = blockIdx.x / TL::BLOCKS;
-    const int blk = static_cast<int>(blockIdx.x % TL::BLOCKS);
+    // --- this workgroup: column block blk of chain `chain`
     const int j0 = blk * TL::BCOLS + wave * TL::WCOLS + jg * C;
     // this lane's element offset inside a head's state; the per-head base
     // pointers are wave-uniform, so addresses are SGPR base + 32-bit offset
@@ -580,6 +574,35 @@ kda_scan_kernel(ScanArgs a) {
     }
     run_rows<R, C, MB>(L, s, b.T, a.o, TABLE ? nullptr : a.e_out, o0, ostride, ig, i0, j0);
     if constexpr (!FUSED) store_state();
+}
+
+// DUAL: phase A and phase B rows each get an LDS area, so both are loaded up
+// front (one memory round trip fewer per launch, twice the LDS).
+// TAILC (0, 1 or 2): the chains past a.n_head_chains -- the last, sparse fill
+// of the chip -- run with TAILC value columns per lane, so over 4 or 2
+// workgroups each (the same bits); that fill then spreads over the CUs and
+// ends sooner.
+template <int R, int C, bool BF16, Rows MA, Rows MB, bool TABLE, bool DUAL, int TAILC>
+__global__ void __launch_bounds__((Tile<R, C>::THREADS))
+__attribute__((amdgpu_waves_per_eu(DUAL ? 2 : 4)))   // DUAL: LDS allows 2 workgroups per CU
+kda_scan_kernel(ScanArgs a) {
+    using TL = Tile<R, C>;
+    __shared__ Stage<R> Ls[DUAL ? 2 : 1];
+    if constexpr (TAILC != 0) {
+        static_assert(C == 4 && !DUAL && !TABLE, "the tail split serves whole-head launches");
+        const unsigned long long head_blocks =
+            static_cast<unsigned long long>(a.n_head_chains) * TL::BLOCKS;
+        if (blockIdx.x >= head_blocks) {
+            const unsigned long long t = blockIdx.x - head_blocks;
+            constexpr int kSplit = Tile<R, TAILC>::BLOCKS;
+            scan_chain<R, TAILC, BF16, MA, MB, TABLE, DUAL>(
+                a, Ls, static_cast<size_t>(a.n_head_chains + t / kSplit),
+                static_cast<int>(t % kSplit));
+            return;
+        }
+    }
+    scan_chain<R, C, BF16, MA, MB, TABLE, DUAL>(a, Ls, blockIdx.x / TL::BLOCKS,
+                                                static_cast<int>(blockIdx.x % TL::BLOCKS));
 }
 
 // ------------------------------------------------------------------ copy
@@ -961,20 +984,59 @@ __global__ void __launch_bounds__(64 * kTMax) kda_accept_finish_kernel(AcceptArg
 // 74 KB of LDS each, so two workgroups per CU): they fit in one pass.
 constexpr unsigned long long kDualStageMaxBlocks = 512;
 
+// The chip's CUs; whole-head workgroups resident at once are 4 per CU (128
+// VGPRs, 4 waves per SIMD).  A launch of more chains than that runs in fills;
+// when its last fill is sparse, its chains are split so that the fill has
+// about one workgroup per CU: 4 ways up to CUs/4 chains, 2 ways up to CUs/2.
+int chip_cus() {
+    static int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        return n;
+    }();
+    return cus;
+}
+
+template <int TAILC, bool BF16, Rows MA, Rows MB>
+hipError_t launch_split_tail(const ScanArgs& a, long long tail, hipStream_t stream) {
+    using TL = Tile<kKeysPerLane, 4>;
+    const unsigned long long tb = static_cast<unsigned long long>(a.n_head_chains) +
+                                  static_cast<unsigned long long>(tail) *
+                                      Tile<kKeysPerLane, TAILC>::BLOCKS;
+    if (tb > 0x7FFFFFFFull) return hipErrorInvalidValue;
+    kda_scan_kernel<kKeysPerLane, 4, BF16, MA, MB, false, false, TAILC>
+        <<<dim3(static_cast<unsigned>(tb)), dim3(TL::THREADS), 0, stream>>>(a);
+    return hipGetLastError();
+}
+
 template <int C, bool BF16, Rows MA, Rows MB, bool TABLE>
-hipError_t launch_tiled(const ScanArgs& a, hipStream_t stream) {
+hipError_t launch_tiled(const ScanArgs& a0, hipStream_t stream) {
     using TL = Tile<kKeysPerLane, C>;
+    ScanArgs a = a0;
     const unsigned long long blocks = static_cast<unsigned long long>(a.n_chains) * TL::BLOCKS;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blocks));
     if constexpr (MA != Rows::kNone && C != 4) {
         if (blocks <= kDualStageMaxBlocks && a.n_prev <= 1) {
-            kda_scan_kernel<kKeysPerLane, C, BF16, MA, MB, TABLE, true>
+            kda_scan_kernel<kKeysPerLane, C, BF16, MA, MB, TABLE, true, 0>
                 <<<grid, dim3(TL::THREADS), 0, stream>>>(a);
             return hipGetLastError();
         }
     }
-    kda_scan_kernel<kKeysPerLane, C, BF16, MA, MB, TABLE, false>
+    if constexpr (C == 4 && !TABLE) {
+        const long long cus = chip_cus();
+        const long long slots = 4 * cus;
+        const long long tail = a.n_chains % slots;
+        if (a.n_chains > slots && tail > 0 && tail <= cus / 2) {
+            a.n_head_chains = a.n_chains - tail;
+            return tail <= cus / 4 ? launch_split_tail<1, BF16, MA, MB>(a, tail, stream)
+                                   : launch_split_tail<2, BF16, MA, MB>(a, tail, stream);
+        }
+    }
+    kda_scan_kernel<kKeysPerLane, C, BF16, MA, MB, TABLE, false, 0>
         <<<grid, dim3(TL::THREADS), 0, stream>>>(a);
     return hipGetLastError();
 }

@@ -49,6 +49,7 @@ struct ScanArgs {
     PrevRows prev[kMaxPrev];
     int n_prev;
     long long n_chains;  // (layer, head) or (layer, session, head) chains
+    long long n_head_chains;   // chains run whole-head before a split tail (launcher)
     int H;
     int T;               // rows this launch runs
     int T_stride;        // rows per layer in this launch's input layout

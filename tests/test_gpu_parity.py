@@ -502,13 +502,16 @@ def _per_layers(fn, L, chunk):
     return [fn(l0, min(l0 + chunk, L)) for l0 in range(0, L, chunk)]
 
 
-@pytest.mark.parametrize("chunk,bf16", [(1, False), (4, False), (8, False), (1, True), (4, True)])
-def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16):
+@pytest.mark.parametrize("chunk,bf16,L", [(1, False, 34), (4, False, 34), (8, False, 34),
+                                          (1, True, 34), (4, True, 34), (1, False, 17)])
+def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L):
     # 1 layer = 64 chains (4 workgroups per head), 4 layers = 256 chains
     # (2 per head), 8 layers = 512 chains (1 per head): every tiling must
-    # give the bits of the 34-layer launch, for the scan, both replays and
-    # the fused round
-    L, T, H = 34, 15, 64
+    # give the bits of the full launch, for the scan, both replays and the
+    # fused round.  The full launch itself ends in a split tail: at 34 layers
+    # its last 128 chains run 2 workgroups per head, at 17 layers its last 64
+    # chains 4 per head.
+    T, H = 15, 64
     r = rand_rows(91, L, T, H, bf16=bf16)
     rows = rows_dev(r)
     s0 = dev(rand_state(92, L, H, 0.5))
