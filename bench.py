@@ -64,6 +64,11 @@ def replay_bytes_per_head(keep: int, es: int = 4) -> int:
     return 2 * STATE_BYTES + keep * (3 * D * es + es)
 
 
+def columns_bytes_per_head(T: int, es: int = 4) -> int:
+    """State-column scan: the state read once, written after every row, rows and o."""
+    return STATE_BYTES * (1 + T) + T * (4 * D * es + es) + T * ROW_BYTES
+
+
 def round_bytes_per_head(keep_prev: int, T: int, es: int = 4) -> int:
     """Fused round: snapshot in + committed state out, keep_prev rows of k, g and
     the stash e in, T rows of q,k,v,g,beta in, T rows of o and e out."""
@@ -166,6 +171,8 @@ def main() -> int:
     ap.add_argument("--accept-launches", type=int, default=32,
                     help="kda_accept_greedy launches at t=15, V=150,000 (0 skips the figure)")
     ap.add_argument("--no-split", action="store_true", help="skip the split scan + replay pipeline")
+    ap.add_argument("--columns-rounds", type=int, default=16,
+                    help="rounds of the state-column rollback arm (0 skips it)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -300,6 +307,41 @@ def main() -> int:
                         "gbps": sum(rep_bytes) / (sum(rep_us) * 1e-6) / 1e9} if rep_us else None),
             "round_gbps": (args.steps * scan_bytes + sum(rep_bytes)) / (s_ms * 1e-3) / 1e9,
         }
+
+    # the state-column arm: every round writes the state after each of its T
+    # rows and the next round continues from column keep-1 (a view, no copy)
+    columns = None
+    if args.columns_rounds > 0:
+        cols = [torch.empty(T, L, H, D, D, device="cuda") for _ in range(2)]
+        col_state = [bufs[0][0]]
+
+        def columns_round(i, m):
+            r = i % w.rounds
+            rows = dev_rounds[r % n_pool]
+            out = cols[i % 2]
+            if m is not None:
+                m[0].record(stream)
+            kda.kda_scan_rows_columns(col_state[0], out, *rows, o)
+            if m is not None:
+                m[1].record(stream)
+            col_state[0] = out[int(js[r])]
+            return None
+
+        cm, _, c_ms, _ = timed(columns_round, args.warmup, args.columns_rounds, 2)
+        c_us = [cm[s][0].elapsed_time(cm[s][1]) * 1e3 for s in range(args.columns_rounds)]
+        c_bytes = chains * columns_bytes_per_head(T)
+        columns = {
+            "rounds": args.columns_rounds,
+            "value": args.columns_rounds * T * H * L / (c_ms * 1e-3),
+            "round_us": stats_us(c_us),
+            "gbps": c_bytes / (float(np.mean(c_us)) * 1e-6) / 1e9,
+            "bytes_per_round": c_bytes,
+            "column_bytes": T * chains * D * D * 4,
+            "vs_fused": (args.columns_rounds * T * H * L / (c_ms * 1e-3)) / value,
+            "note": "kda_scan_rows_columns: the state after every row written (T columns), "
+                    "the next round continues from column keep-1 by pointer; no replay",
+        }
+        del cols, col_state
 
     # MALL-cold round launches: write 512 MiB between launches, time the launch alone
     cold_us = []
@@ -641,6 +683,7 @@ def main() -> int:
         "committed_rows_heads_per_s": sum(int(js[(args.warmup + s) % w.rounds]) + 1
                                           for s in range(args.steps)) * H * L / (f_ms * 1e-3),
         "split": split,
+        "state_columns": columns,
         "accept": accept,
         "rollback_extras": rollback_extras,
         "per_layer_graph": per_layer,

@@ -74,6 +74,7 @@ def load():
     lib = ctypes.CDLL(_LIB_PATH)
     p, i = ctypes.c_void_p, ctypes.c_int
     lib.kda_scan_rows.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, p]
+    lib.kda_scan_rows_columns.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, p]
     lib.kda_snapshot.argtypes = [p, p, i, i, p]
     lib.kda_replay.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, p]
     lib.kda_scan_batched.argtypes = [p, p, p, p, p, p, p, i, i, i, i, p]
@@ -88,7 +89,7 @@ def load():
     for fn in (lib.kda_scan_rows, lib.kda_snapshot, lib.kda_replay, lib.kda_scan_batched,
                lib.kda_verify_round, lib.kda_accept_greedy, lib.kda_conv_reroll,
                lib.kda_copy_batch, lib.kda_row_ops, lib.kda_verify_round_multi,
-               lib.kda_abi_version):
+               lib.kda_scan_rows_columns, lib.kda_abi_version):
         fn.restype = i
     lib.kda_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -177,6 +178,28 @@ def kda_scan_rows(s_in, s_out, q, k, v, g, beta, o=None, e=None, stream=None) ->
     _check(lib.kda_scan_rows(_dev(s_in, "s_in"), _dev(s_out, "s_out"), _dev(q, "q"), _dev(k, "k"),
                              _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"),
                              _dev(e, "e"), L, T, H, dt, _stream(stream)))
+
+
+def kda_scan_rows_columns(s_in, s_cols, q, k, v, g, beta, o, e=None, stream=None) -> None:
+    """The state-column variant: scan T rows and keep the state after every row.
+
+    s_cols is [T][L][H][D][D]; s_cols[t] is the state after rows 0..t, so a
+    round that accepts keep rows continues from s_cols[keep - 1].  s_in is
+    left untouched; o is required.
+    """
+    lib = load()
+    L, T, H = _rows_shape(q, k, v, g, beta)
+    _state(s_in, (L, H, D, D), "s_in")
+    _state(s_cols, (T, L, H, D, D), "s_cols")
+    if o is None:
+        raise ValueError("o is required")
+    _plane(o, (L, T, H, D), "o")
+    _plane(e, (L, T, H, D), "e")
+    dt = _in_dtype((q, k, v, g, beta))
+    _check(lib.kda_scan_rows_columns(_dev(s_in, "s_in"), _dev(s_cols, "s_cols"), _dev(q, "q"),
+                                     _dev(k, "k"), _dev(v, "v"), _dev(g, "g"),
+                                     _dev(beta, "beta"), _dev(o, "o"), _dev(e, "e"), L, T, H, dt,
+                                     _stream(stream)))
 
 
 def kda_snapshot(s, snap, stream=None) -> None:

@@ -240,6 +240,41 @@ int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k,
                                          static_cast<hipStream_t>(stream)));
 }
 
+int kda_scan_rows_columns(const float* s_in, float* s_cols, const void* q, const void* k,
+                          const void* v, const void* g, const void* beta, float* o, float* e,
+                          int L, int T, int H, int in_dtype, void* stream) {
+    const char* fn = "kda_scan_rows_columns";
+    int rc;
+    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H)) ||
+        (rc = check_rows(fn, "T", T)))
+        return rc;
+    const unsigned long long chains = static_cast<unsigned long long>(L) * H;
+    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
+    const unsigned long long rows = chains * T;
+    const Span in[] = {
+        {"s_in", s_in, chains * kStateBytes, 16, false},
+        {"q", q, rows * kRowElems * es, 16, false},
+        {"k", k, rows * kRowElems * es, 16, false},
+        {"v", v, rows * kRowElems * es, 16, false},
+        {"g", g, rows * kRowElems * es, 16, false},
+        {"beta", beta, rows * es, es, false},
+    };
+    const Span out[] = {
+        {"s_cols", s_cols, rows * kStateBytes, 16, false},
+        {"o", o, rows * kRowElems * 4, 16, false},
+        {"e", e, rows * kRowElems * 4, 16, true},
+    };
+    if ((rc = check_spans(fn, in, 6)) || (rc = check_spans(fn, out, 3)) ||
+        (rc = check_alias(fn, out, 3, in, 6)))
+        return rc;
+    kda::ScanArgs a{};
+    a.s_in = s_in; a.s_cols = s_cols; a.col_stride = chains * kda::kD * kda::kD;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.e_out = e;
+    a.n_chains = static_cast<long long>(chains); a.H = H; a.T = T; a.T_stride = T;
+    return launched(fn, kda::launch_scan(a, kda::Launch::kScanColumns, in_dtype == KDA_IN_BF16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 int kda_snapshot(const float* s, float* snap, int L, int H, void* stream) {
     const char* fn = "kda_snapshot";
     int rc;

@@ -1,7 +1,8 @@
 // gfx950 kernels of the KDA verify-row scan.
 //
-// One workgroup owns one (layer, head) chain -- or, in the batched arm, one
-// (layer, session, head) chain -- and keeps that head's 128 x 128 f32 state in
+// A workgroup owns one (layer, head) chain -- or, in the batched arm, one
+// (layer, session, head) chain; in launches with few chains, a 32- or 64-column
+// block of one -- and keeps that part of the head's 128 x 128 f32 state in
 // VGPRs for the whole row loop: the state is read from HBM once and written
 // once per launch, whatever the row count T.  This is what the source page
 // (memra-engine 0.123.0 glm_spec.rs, module doc VERIFY-ROW BATCHING) means by
@@ -22,22 +23,25 @@
 // A lane owns R consecutive key rows x C consecutive value columns; the NI =
 // 128/R lanes that share a column group sit next to each other inside one
 // 16-lane DPP row, so the reduction over i is an in-lane chain followed by a
-// log2(NI)-step butterfly with no LDS traffic and no barrier.  A wave covers
-// (64/NI)*C columns and a head takes 128 / that many waves.
+// log2(NI)-step butterfly with no LDS traffic and no barrier.  R = 16 (NI = 8)
+// throughout; a workgroup has 4 waves covering 4*(64/NI)*C columns, so a head
+// takes 1, 2 or 4 workgroups for C = 4, 2, 1.
 //
 // Bit identity.  Every entry point (T-row scan, replay, batched t=1) runs the
-// same row code with the same tiling, explicit fmaf, -ffp-contract=off, one
-// decay routine, and a reduction tree that does not depend on T, B, L, H or
-// the entry point.  The state crosses HBM as exact f32 words, so a T-row launch equals
-// T chained one-row launches bit for bit.
+// same row code with the same key split, explicit fmaf, -ffp-contract=off,
+// one decay routine, and a reduction tree that does not depend on T, B, L, H,
+// C or the entry point.  The state crosses HBM as exact f32 words, so a T-row
+// launch equals T chained one-row launches bit for bit, and every tiling gives
+// the same bits.
 //
 // Rollback.  A scan can also write each row's delta vector e (the "stash"
 // plane beside the row inputs).  A replay that reads e skips both reductions:
 // per element it is the decay multiply and the rank-1 FMA, with the very e
 // bits the scan used, so it rebuilds the same state bits.  The fused verify
-// round replays the previous round's kept rows from its snapshot, stores that
-// committed state (this round's snapshot) and then scans the new rows for o,
-// so the state crosses HBM once per round.
+// round replays the previous round's kept rows from its snapshot (or several
+// earlier rounds' from an older one), stores that committed state (this
+// round's snapshot) and then scans the new rows for o, so the state crosses
+// HBM once per round.
 //
 // No MFMA: each row is two matrix-vector products and a rank-1 update with a
 // sequential dependency from row to row -- there is no dense contraction to
@@ -221,7 +225,11 @@ enum class Rows {
     kFull,    // u and w reductions: state, o and (optionally) e -- the verify scan
     kState,   // u reduction only: state and (optionally) e
     kStash,   // e read from the stash: decay and rank-1 update only
+    kFullCols,   // kFull, and the state after every row stored (state columns)
 };
+
+// Modes that reduce S'^T q and write o.
+constexpr bool has_q(Rows m) { return m == Rows::kFull || m == Rows::kFullCols; }
 
 // All T rows of one phase, staged in LDS.
 template <int R>
@@ -275,7 +283,7 @@ __device__ __forceinline__ void stage_issue(Staged<R, C, M, TMAX>& in, const Src
             in.v[p] = load4<BF16>(src.v, off);
             in.b[p] = load1<BF16>(src.beta, src.b0 + t * src.bstride);
         }
-        if constexpr (M == Rows::kFull) in.q[p] = load4<BF16>(src.q, off);
+        if constexpr (has_q(M)) in.q[p] = load4<BF16>(src.q, off);
     }
 }
 
@@ -289,7 +297,7 @@ __device__ __forceinline__ void stage_fence(Staged<R, C, M, TMAX>& in) {
         opaque(in.k[p]);
         opaque(in.v[p]);
         opaque(in.g[p]);
-        if constexpr (M == Rows::kFull) opaque(in.q[p]);
+        if constexpr (has_q(M)) opaque(in.q[p]);
         if constexpr (M != Rows::kStash) asm volatile("" : "+v"(in.b[p])::"memory");
     }
 }
@@ -323,7 +331,7 @@ __device__ __forceinline__ void stage_commit(Stage<R>& L, const Staged<R, C, M, 
                 L.ve[t * 32 + c4] = make_float4(bt * gv.x, bt * gv.y, bt * gv.z, bt * gv.w);
                 if (c4 == 0) L.b[t] = bt;
             }
-            if constexpr (M == Rows::kFull) {
+            if constexpr (has_q(M)) {
                 const float4 gq = in.q[p];
                 *reinterpret_cast<float4*>(sq + kp) = make_float4(
                     gq.x * kInvSqrtD, gq.y * kInvSqrtD, gq.z * kInvSqrtD, gq.w * kInvSqrtD);
@@ -334,7 +342,7 @@ __device__ __forceinline__ void stage_commit(Stage<R>& L, const Staged<R, C, M, 
 
     // (q/sqrt(128)).k per row: one 16-lane DPP row per verify row, 8 keys per
     // lane in ascending order, then a fixed butterfly
-    if constexpr (M == Rows::kFull) {
+    if constexpr (has_q(M)) {
         const int wave = tid >> 6;
         const int l16 = tid & 15;
         for (int t = wave * 4 + ((tid & 63) >> 4); t < T; t += TL::WAVES * 4) {
@@ -362,10 +370,13 @@ __device__ __forceinline__ void stage(Stage<R>& L, const Src& src, int tid, F&& 
     stage_commit<R, C, M, TMAX>(L, in, src.T, tid);
 }
 
+// kFullCols: `cols` addresses this chain's state in column 0, and row t's
+// state goes to cols + t * col_stride.
 template <int R, int C, Rows M>
 __device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], int T,
                                          float* o, float* e_out, size_t o0, size_t ostride,
-                                         int ig, int i0, int j0) {
+                                         int ig, int i0, int j0, gfloat* cols = nullptr,
+                                         size_t col_stride = 0) {
     using TL = Tile<R, C>;
     using KR = KeyRow<R>;
     const float* sve = reinterpret_cast<const float*>(L.ve);
@@ -379,7 +390,7 @@ __device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], in
             const float4 y = L.d[kb / 4 + r4];
             kk[4 * r4 + 0] = x.x; kk[4 * r4 + 1] = x.y; kk[4 * r4 + 2] = x.z; kk[4 * r4 + 3] = x.w;
             dk[4 * r4 + 0] = y.x; dk[4 * r4 + 1] = y.y; dk[4 * r4 + 2] = y.z; dk[4 * r4 + 3] = y.w;
-            if constexpr (M == Rows::kFull) {
+            if constexpr (has_q(M)) {
                 const float4 z = L.q[kb / 4 + r4];
                 qq[4 * r4 + 0] = z.x; qq[4 * r4 + 1] = z.y; qq[4 * r4 + 2] = z.z; qq[4 * r4 + 3] = z.w;
             }
@@ -408,18 +419,18 @@ __device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], in
                 for (int c = 0; c < C; ++c) {
                     s[r][c] = s[r][c] * dk[r];
                     u[c] = fmaf(kk[r], s[r][c], u[c]);
-                    if constexpr (M == Rows::kFull) w[c] = fmaf(qq[r], s[r][c], w[c]);
+                    if constexpr (has_q(M)) w[c] = fmaf(qq[r], s[r][c], w[c]);
                 }
             }
 #pragma unroll
             for (int c = 0; c < C; ++c) {
                 u[c] = group_sum<TL::NI>(u[c]);
-                if constexpr (M == Rows::kFull) w[c] = group_sum<TL::NI>(w[c]);
+                if constexpr (has_q(M)) w[c] = group_sum<TL::NI>(w[c]);
             }
             // e = beta v - beta u
 #pragma unroll
             for (int c = 0; c < C; ++c) e[c] = fmaf(nbt, u[c], ve[c]);
-            if constexpr (M == Rows::kFull) {
+            if constexpr (has_q(M)) {
                 // finish w's butterfly on every lane: sunk into the writer's
                 // branch, its last DPP step would become mov 0, mov_dpp, add
 #pragma unroll
@@ -438,13 +449,18 @@ __device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], in
 #pragma unroll
             for (int c = 0; c < C; ++c) s[r][c] = fmaf(kk[r], e[c], s[r][c]);
         }
+        if constexpr (M == Rows::kFullCols) {
+            gfloat* col = cols + t * col_stride + (i0 * kD + j0);
+#pragma unroll
+            for (int r = 0; r < R; ++r) store_gcols<C>(col + r * kD, s[r]);
+        }
     }
 }
 
-// One launch: optionally a replay phase A (FUSED: rows 0..keep-1 of the
-// previous round from the snapshot, then that committed state is stored),
-// then phase B (this launch's rows).  Without FUSED the state after phase B
-// is stored.
+// One launch: optionally a replay phase A (FUSED: the kept rows of up to
+// kMaxPrev earlier rounds, oldest first, from the snapshot, then -- when
+// a.s_out is set -- that committed state is stored), then phase B (this
+// launch's rows).  Without FUSED the state after phase B is stored.
 template <int R, int C, bool BF16, Rows MA, Rows MB, bool TABLE, bool DUAL>
 __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R>* Ls, size_t chain,
                                            int blk) {
@@ -571,6 +587,13 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R>* Ls, size
     } else {
         // the batched arm always scans one row per session
         stage<R, C, BF16, MB, TABLE ? 1 : kTMax>(L, b, tid, load_state);
+    }
+    if constexpr (MB == Rows::kFullCols) {
+        // the last column is the state after all rows: no separate store
+        static_assert(!FUSED && !TABLE, "state columns serve the plain scan");
+        run_rows<R, C, MB>(L, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0,
+                           (gfloat*)a.s_cols + chain * kDD, a.col_stride);
+        return;
     }
     run_rows<R, C, MB>(L, s, b.T, a.o, TABLE ? nullptr : a.e_out, o0, ostride, ig, i0, j0);
     if constexpr (!FUSED) store_state();
@@ -1066,6 +1089,7 @@ hipError_t launch_dtype(const ScanArgs& a, Launch kind, hipStream_t stream) {
         case Launch::kBatchedState: return launch_one<BF16, Rows::kNone, Rows::kState, true>(a, stream);
         case Launch::kRound:        return launch_one<BF16, Rows::kState, Rows::kFull, false>(a, stream);
         case Launch::kRoundStash:   return launch_one<BF16, Rows::kStash, Rows::kFull, false>(a, stream);
+        case Launch::kScanColumns:  return launch_one<BF16, Rows::kNone, Rows::kFullCols, false>(a, stream);
     }
     return hipErrorInvalidValue;
 }

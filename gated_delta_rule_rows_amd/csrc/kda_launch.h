@@ -48,6 +48,10 @@ struct ScanArgs {
     // from s_in before this launch's rows (entries with keep = 0 left out)
     PrevRows prev[kMaxPrev];
     int n_prev;
+    // state columns (kScanColumns): the state after row t of chain c at
+    // s_cols + t * col_stride + c * 128 * 128
+    float* s_cols;
+    size_t col_stride;
     long long n_chains;  // (layer, head) or (layer, session, head) chains
     long long n_head_chains;   // chains run whole-head before a split tail (launcher)
     int H;
@@ -64,6 +68,7 @@ enum class Launch {
     kBatchedState,  // batched arm, state only
     kRound,         // fused verify round: replay (recomputed), store (if s_out), scan for o
     kRoundStash,    // fused verify round: replay from the stash, store (if s_out), scan for o
+    kScanColumns,   // T rows, outputs o (and e), the state after every row stored
 };
 
 hipError_t launch_scan(const ScanArgs& a, Launch kind, bool bf16, hipStream_t stream);

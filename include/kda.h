@@ -52,7 +52,7 @@ extern "C" {
 #define KDA_HEAD_DIM 128   /* d_k = d_v; glm5_spec_ppn_gate.rs fixture head_dim */
 #define KDA_T_MAX 15       /* verify rows per round: K + 1 <= 15 (glm_spec.rs, WALK-REUSE) */
 #define KDA_B_MAX 15       /* batched-decode sessions per step (same knee) */
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 #define KDA_ACCEPT_WORK_BYTES 12288   /* workspace of kda_accept_greedy */
 #define KDA_NO_TOKEN 0xFFFFFFFFu      /* argmax slot of a logits row holding a NaN */
 #define KDA_CONV_RING_ROWS 3          /* short-conv history: kernel size 4 keeps 3 raw rows */
@@ -92,6 +92,28 @@ enum {
 int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k,
                   const void* v, const void* g, const void* beta, float* o, float* e, int L,
                   int T, int H, int in_dtype, void* stream);
+
+/*
+ * The per-row state-column variant of a verify scan: T rows as kda_scan_rows,
+ * keeping the state after every row, so that accepting keep rows commits
+ * column keep-1 by pointer, with no replay.
+ *   glm_spec.rs (0.123.0), module doc ROLLBACK and the Glm5VerifyCkpt doc:
+ *   the column clones per row (restore column keep-1) that the pages later
+ *   retired for snapshot plus replay.  It serves as the comparison arm of
+ *   kda_replay / kda_verify_round: it writes T states per round instead of
+ *   one.
+ *   s_in        : [L][H][128][128] f32, left untouched.
+ *   s_cols      : [T][L][H][128][128] f32.  Column t, the L x H states at
+ *                 s_cols + t*L*H*128*128, is the state after rows 0..t: the
+ *                 bits of kda_scan_rows over rows 0..t and of kda_replay with
+ *                 keep = t + 1.  Column T-1 is the state after the round.
+ *   q..beta, e  : as kda_scan_rows.
+ *   o           : [L][T][H][128] f32, required.
+ *   No output may overlap an input.  L, H >= 1;  1 <= T <= KDA_T_MAX.
+ */
+int kda_scan_rows_columns(const float* s_in, float* s_cols, const void* q, const void* k,
+                          const void* v, const void* g, const void* beta, float* o, float* e,
+                          int L, int T, int H, int in_dtype, void* stream);
 
 /*
  * snap = s, a device copy of L x H states [L][H][128][128] f32.

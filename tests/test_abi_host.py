@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) >= {"kda_scan_rows", "kda_snapshot", "kda_replay", "kda_scan_batched",
                           "kda_verify_round", "kda_accept_greedy", "kda_conv_reroll",
                           "kda_copy_batch", "kda_row_ops", "kda_verify_round_multi",
-                          "kda_last_error", "kda_abi_version"}
+                          "kda_scan_rows_columns", "kda_last_error", "kda_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -97,6 +97,15 @@ def _scan(lib, b, **kw):
     a.update(kw)
     return lib.kda_scan_rows(a["s_in"], a["s_out"], a["q"], a["k"], a["v"], a["g"], a["beta"],
                              a["o"], a["e"], a["L"], a["T"], a["H"], a["dt"], None)
+
+
+def _columns(lib, b, **kw):
+    a = dict(s_in=b["s_in"], s_cols=b["s_out"], q=b["q"], k=b["k"], v=b["v"], g=b["g"],
+             beta=b["beta"], o=b["o"], e=None, L=2, T=8, H=2, dt=0)
+    a.update(kw)
+    return lib.kda_scan_rows_columns(a["s_in"], a["s_cols"], a["q"], a["k"], a["v"], a["g"],
+                                     a["beta"], a["o"], a["e"], a["L"], a["T"], a["H"], a["dt"],
+                                     None)
 
 
 def _replay(lib, b, **kw):
@@ -184,6 +193,36 @@ def test_scan_rows_alignment_and_alias(lib, b):
 def test_replay_refusals(lib, b, kw, code, needle):
     assert _replay(lib, b, **kw) == code
     assert needle in _msg(lib)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(T=0), ERR_RANGE, "T=0"),
+    (dict(T=16), ERR_RANGE, "T=16"),
+    (dict(L=0), ERR_RANGE, "L=0"),
+    (dict(dt=3), ERR_ARG, "in_dtype"),
+    (dict(o=None), ERR_ARG, "o is NULL"),
+    (dict(s_cols=None), ERR_ARG, "s_cols is NULL"),
+    (dict(s_in=None), ERR_ARG, "s_in is NULL"),
+    (dict(g=None), ERR_ARG, "g is NULL"),
+])
+def test_scan_rows_columns_refusals(lib, b, kw, code, needle):
+    assert _columns(lib, b, **kw) == code
+    assert needle in _msg(lib)
+
+
+def test_scan_rows_columns_alignment_and_alias(lib, b):
+    off = lambda n, k: ctypes.c_void_p(b.addr[n] + k)
+    assert _columns(lib, b, s_cols=off("s_out", 4)) == ERR_ALIGN
+    assert "s_cols is not 16-byte aligned" in _msg(lib)
+    # no in-place form: the columns may not even be s_in itself
+    assert _columns(lib, b, s_cols=b["s_in"]) == ERR_ALIAS and "s_cols overlaps s_in" in _msg(lib)
+    # T columns of L*H states reach past the first state: a row input there is refused
+    cols_bytes = 8 * 2 * 2 * 128 * 128 * 4
+    assert _columns(lib, b, s_cols=off("q", -(cols_bytes - 16))) == ERR_ALIAS
+    assert "s_cols overlaps q" in _msg(lib)
+    assert _columns(lib, b, e=off("s_out", cols_bytes - 16)) == ERR_ALIAS
+    assert "s_cols overlaps e" in _msg(lib)
+    assert _columns(lib, b, o=b["k"]) == ERR_ALIAS and "o overlaps k" in _msg(lib)
 
 
 def test_replay_alias(lib, b):
