@@ -486,5 +486,5 @@ __all__ = [
     "kda_replay", "kda_scan_batched", "kda_verify_round", "state_table", "kda_abi_version",
     "kda_last_error", "kda_accept_greedy", "accept_workspace", "ACCEPT_WORK_BYTES", "NO_TOKEN",
     "kda_conv_reroll", "copy_table", "kda_copy_batch", "RING_ROWS", "kda_row_ops",
-    "kda_verify_round_multi", "MAX_PREV_ROUNDS",
+    "kda_verify_round_multi", "MAX_PREV_ROUNDS", "kda_scan_rows_columns",
 ]
