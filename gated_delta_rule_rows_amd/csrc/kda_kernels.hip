@@ -158,27 +158,33 @@ typedef float vf4 __attribute__((ext_vector_type(4)));
 using gvf2 = __attribute__((address_space(1))) vf2;
 using gvf4 = __attribute__((address_space(1))) vf4;
 
-template <int C>
+// State words.  NT: nontemporal (streaming) access.  A launch reads each state
+// word once and writes it once, and the next reader is a later launch, so
+// keeping them out of the caches costs nothing; it measured 7-9% faster fused
+// rounds and 14% faster batched steps.
+template <int C, bool NT>
 __device__ __forceinline__ void load_gcols(const gfloat* p, float (&x)[C]) {
     if constexpr (C == 4) {
-        const vf4 v = *(const gvf4*)p;
+        const vf4 v = NT ? __builtin_nontemporal_load((const gvf4*)p) : *(const gvf4*)p;
         x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
     } else if constexpr (C == 2) {
-        const vf2 v = *(const gvf2*)p;
+        const vf2 v = NT ? __builtin_nontemporal_load((const gvf2*)p) : *(const gvf2*)p;
         x[0] = v.x; x[1] = v.y;
     } else {
-        x[0] = *p;
+        x[0] = NT ? __builtin_nontemporal_load(p) : *p;
     }
 }
 
-template <int C>
+template <int C, bool NT>
 __device__ __forceinline__ void store_gcols(gfloat* p, const float (&x)[C]) {
     if constexpr (C == 4) {
-        *(gvf4*)p = vf4{x[0], x[1], x[2], x[3]};
+        const vf4 v{x[0], x[1], x[2], x[3]};
+        if constexpr (NT) __builtin_nontemporal_store(v, (gvf4*)p); else *(gvf4*)p = v;
     } else if constexpr (C == 2) {
-        *(gvf2*)p = vf2{x[0], x[1]};
+        const vf2 v{x[0], x[1]};
+        if constexpr (NT) __builtin_nontemporal_store(v, (gvf2*)p); else *(gvf2*)p = v;
     } else {
-        *p = x[0];
+        if constexpr (NT) __builtin_nontemporal_store(x[0], p); else *p = x[0];
     }
 }
 
@@ -452,7 +458,7 @@ __device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], in
         if constexpr (M == Rows::kFullCols) {
             gfloat* col = cols + t * col_stride + (i0 * kD + j0);
 #pragma unroll
-            for (int r = 0; r < R; ++r) store_gcols<C>(col + r * kD, s[r]);
+            for (int r = 0; r < R; ++r) store_gcols<C, false>(col + r * kD, s[r]);
         }
     }
 }
@@ -509,10 +515,13 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R>* Ls, size
         o0 = (l * a.T * a.H + h) * kD;              ostride = static_cast<size_t>(a.H) * kD;
     }
 
+    // the state streams (see load_gcols), except in the state-column arm,
+    // whose 2 GB of column writes measured faster through the caches
+    constexpr bool kNT = MB != Rows::kFullCols;
     float s[R][C];
     auto load_state = [&] {
 #pragma unroll
-        for (int r = 0; r < R; ++r) load_gcols<C>(st_in + (lane_off + r * kD), s[r]);
+        for (int r = 0; r < R; ++r) load_gcols<C, kNT>(st_in + (lane_off + r * kD), s[r]);
     };
     auto store_state = [&] {
         if constexpr (TABLE) {
@@ -525,10 +534,10 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R>* Ls, size
             asm volatile("" : "+v"(far));
 #pragma unroll
             for (int r = 0; r < R; ++r)
-                store_gcols<C>(r < kNear ? near + r * kD : far + (r - kNear) * kD, s[r]);
+                store_gcols<C, kNT>(r < kNear ? near + r * kD : far + (r - kNear) * kD, s[r]);
         } else {
 #pragma unroll
-            for (int r = 0; r < R; ++r) store_gcols<C>(st_out + (lane_off + r * kD), s[r]);
+            for (int r = 0; r < R; ++r) store_gcols<C, kNT>(st_out + (lane_off + r * kD), s[r]);
         }
     };
 
