@@ -237,15 +237,15 @@ enum class Rows {
 // Modes that reduce S'^T q and write o.
 constexpr bool has_q(Rows m) { return m == Rows::kFull || m == Rows::kFullCols; }
 
-// All T rows of one phase, staged in LDS.
-template <int R>
+// Up to TM rows of one phase, staged in LDS (the batched arm stages one).
+template <int R, int TM = kTMax>
 struct Stage {
-    float4 d[kTMax * KeyRow<R>::kStride / 4];   // exp(clamp(g)), key layout
-    float4 k[kTMax * KeyRow<R>::kStride / 4];   // k, key layout
-    float4 q[kTMax * KeyRow<R>::kStride / 4];   // q / sqrt(128), key layout (kFull)
-    float4 ve[kTMax * kD / 4];                  // beta * v, or e for kStash; [t][j]
-    float b[kTMax];                             // beta
-    float qk[kTMax];                            // (q / sqrt(128)) . k
+    float4 d[TM * KeyRow<R>::kStride / 4];   // exp(clamp(g)), key layout
+    float4 k[TM * KeyRow<R>::kStride / 4];   // k, key layout
+    float4 q[TM * KeyRow<R>::kStride / 4];   // q / sqrt(128), key layout (kFull)
+    float4 ve[TM * kD / 4];                  // beta * v, or e for kStash; [t][j]
+    float b[TM];                             // beta
+    float qk[TM];                            // (q / sqrt(128)) . k
 };
 
 // One phase's row inputs, located for one chain.
@@ -311,7 +311,7 @@ __device__ __forceinline__ void stage_fence(Staged<R, C, M, TMAX>& in) {
 // Write a phase's rows to LDS in the scan's layout (decay, q/sqrt(128), beta v
 // or e), then (q/sqrt(128)).k per row.  Ends with every lane past a barrier.
 template <int R, int C, Rows M, int TMAX>
-__device__ __forceinline__ void stage_commit(Stage<R>& L, const Staged<R, C, M, TMAX>& in, int T,
+__device__ __forceinline__ void stage_commit(Stage<R, TMAX>& L, const Staged<R, C, M, TMAX>& in, int T,
                                              int tid) {
     using TL = Tile<R, C>;
     using KR = KeyRow<R>;
@@ -368,7 +368,7 @@ __device__ __forceinline__ void stage_commit(Stage<R>& L, const Staged<R, C, M, 
 // A phase's rows from HBM into LDS; `between` runs after the row loads are
 // issued and before anything waits on them (the state loads go there).
 template <int R, int C, bool BF16, Rows M, int TMAX = kTMax, typename F>
-__device__ __forceinline__ void stage(Stage<R>& L, const Src& src, int tid, F&& between) {
+__device__ __forceinline__ void stage(Stage<R, TMAX>& L, const Src& src, int tid, F&& between) {
     Staged<R, C, M, TMAX> in;
     stage_issue<R, C, BF16, M, TMAX>(in, src, tid);
     between();
@@ -378,8 +378,8 @@ __device__ __forceinline__ void stage(Stage<R>& L, const Src& src, int tid, F&& 
 
 // kFullCols: `cols` addresses this chain's state in column 0, and row t's
 // state goes to cols + t * col_stride.
-template <int R, int C, Rows M>
-__device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], int T,
+template <int R, int C, Rows M, int TM>
+__device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C], int T,
                                          float* o, float* e_out, size_t o0, size_t ostride,
                                          int ig, int i0, int j0, gfloat* cols = nullptr,
                                          size_t col_stride = 0) {
@@ -468,12 +468,12 @@ __device__ __forceinline__ void run_rows(const Stage<R>& L, float (&s)[R][C], in
 // a.s_out is set -- that committed state is stored), then phase B (this
 // launch's rows).  Without FUSED the state after phase B is stored.
 template <int R, int C, bool BF16, Rows MA, Rows MB, bool TABLE, bool DUAL>
-__device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R>* Ls, size_t chain,
-                                           int blk) {
+__device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1 : kTMax>* Ls,
+                                           size_t chain, int blk) {
     using TL = Tile<R, C>;
     constexpr bool FUSED = MA != Rows::kNone;
     static_assert(!DUAL || FUSED, "two stage areas serve the fused round only");
-    Stage<R>& L = Ls[0];
+    auto& L = Ls[0];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -555,7 +555,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R>* Ls, size
 
     if constexpr (DUAL) {
         // at most one earlier round (the launcher's rule)
-        Stage<R>& LB = Ls[DUAL ? 1 : 0];
+        auto& LB = Ls[DUAL ? 1 : 0];
         Staged<R, C, MA, kTMax> inA;
         Staged<R, C, MB, kTMax> inB;
         const bool replay = a.n_prev > 0;
@@ -619,7 +619,8 @@ __global__ void __launch_bounds__((Tile<R, C>::THREADS))
 __attribute__((amdgpu_waves_per_eu(DUAL ? 2 : 4)))   // DUAL: LDS allows 2 workgroups per CU
 kda_scan_kernel(ScanArgs a) {
     using TL = Tile<R, C>;
-    __shared__ Stage<R> Ls[DUAL ? 2 : 1];
+    // the batched arm stages its one row: 2.4 KB of LDS instead of 36.6 KB
+    __shared__ Stage<R, TABLE ? 1 : kTMax> Ls[DUAL ? 2 : 1];
     if constexpr (TAILC != 0) {
         static_assert(C == 4 && !DUAL && !TABLE, "the tail split serves whole-head launches");
         const unsigned long long head_blocks =
