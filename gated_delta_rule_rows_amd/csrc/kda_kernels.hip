@@ -25,7 +25,10 @@
 // 16-lane DPP row, so the reduction over i is an in-lane chain followed by a
 // log2(NI)-step butterfly with no LDS traffic and no barrier.  R = 16 (NI = 8)
 // throughout; a workgroup has 4 waves covering 4*(64/NI)*C columns, so a head
-// takes 1, 2 or 4 workgroups for C = 4, 2, 1.
+// takes 1, 2 or 4 workgroups for C = 4, 2, 1.  The whole-head verify scan and
+// fused round place the 8 lanes of a column group across the wave's 16-lane
+// rows instead and reduce with cross-row swaps (the swap layout, below): the
+// same pairs in the same order, fewer VALU ops.
 //
 // Bit identity.  Every entry point (T-row scan, replay, batched t=1) runs the
 // same row code with the same key split, explicit fmaf, -ffp-contract=off,
@@ -106,6 +109,47 @@ __device__ __forceinline__ float group_sum(float x) {
     if constexpr (NI >= 8) x = x + dpp<0x141>(x);  // row_half_mirror
     if constexpr (NI >= 16) x = x + dpp<0x140>(x); // row_mirror
     return x;
+}
+
+// The swap layout (whole-head launches that write o): the 8 key groups of a
+// column group sit on lane bits 4, 5 and 3 (key-group bits 0, 1 and 2) and
+// the column group on lane bits 0-2.  One 16-lane row then holds one value of
+// key-group bits 0-1, so gfx950's cross-row swaps pair key groups g and g^1
+// (v_permlane16_swap), then g^2 (v_permlane32_swap), and DPP row_ror:8 pairs
+// g and g^4: the pairs of group_sum<8>, in its order, so every sum keeps its
+// bits.  A reduce-scatter over the 4 columns of a lane costs 7 VALU ops
+// instead of group_sum's 12, and the column each lane ends with is all that
+// o needs.  (Written as asm: the compiler's swap builtins return the first
+// register for both results.  The s_nop covers the VALU-write to swap-read
+// wait states.)
+__device__ __forceinline__ void swap16(float& a, float& b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap32(float& a, float& b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Sum of x[0..3] over the 8 key groups; the lanes of row k (lane bits 4-5)
+// end with column k's sum.
+__device__ __forceinline__ float reduce_scatter4(const float (&x)[4]) {
+    float a = x[0], b = x[1], c = x[2], d = x[3];
+    swap16(a, b);   // even rows: column 0 of the row pair; odd rows: column 1
+    swap16(c, d);   // even rows: column 2; odd rows: column 3
+    float lo = a + b, hi = c + d;
+    swap32(lo, hi); // row k: column k over rows k and k^2
+    const float r = lo + hi;
+    return r + dpp<0x128>(r);   // row_ror:8 pairs lane bit 3
+}
+
+// Column k's value from row k, for k = 0..3, into every lane (the inverse
+// movement of reduce_scatter4).
+__device__ __forceinline__ void all_gather4(float x, float (&y)[4]) {
+    float a = x, b = x;
+    swap32(a, b);   // a: column (row & 1); b: column (row & 1) + 2
+    float a1 = a, b1 = b;
+    swap16(a, a1);  // a: column 0; a1: column 1
+    swap16(b, b1);  // b: column 2; b1: column 3
+    y[0] = a; y[1] = a1; y[2] = b; y[3] = b1;
 }
 
 // ------------------------------------------------------------------ input loads
@@ -378,7 +422,9 @@ __device__ __forceinline__ void stage(Stage<R, TMAX>& L, const Src& src, int tid
 
 // kFullCols: `cols` addresses this chain's state in column 0, and row t's
 // state goes to cols + t * col_stride.
-template <int R, int C, Rows M, int TM>
+// SW: the swap layout (above); the lane's 4 columns are reduced with
+// reduce_scatter4 and e is shared back with all_gather4.
+template <int R, int C, Rows M, bool SW, int TM>
 __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C], int T,
                                          float* o, float* e_out, size_t o0, size_t ostride,
                                          int ig, int i0, int j0, gfloat* cols = nullptr,
@@ -428,26 +474,42 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
                     if constexpr (has_q(M)) w[c] = fmaf(qq[r], s[r][c], w[c]);
                 }
             }
+            if constexpr (SW) {
+                static_assert(C == 4 && TL::NI == 8, "the swap layout is the whole-head tiling");
+                const int lane = threadIdx.x & 63;
+                const int kc = (lane >> 4) & 3;   // the column this lane reduces
+                const float uo = reduce_scatter4(u);
+                const float eo = fmaf(nbt, uo, sve[t * kD + j0 + kc]);
+                // each column's sum sits in two lanes (lane bit 3); bit 3 = 0 writes
+                const bool writer = (lane & 8) == 0;
+                if constexpr (has_q(M)) {
+                    const float ov = fmaf(eo, L.qk[t], reduce_scatter4(w));
+                    if (writer) o[o0 + t * ostride + j0 + kc] = ov;
+                }
+                if (e_out != nullptr && writer) e_out[o0 + t * ostride + j0 + kc] = eo;
+                all_gather4(eo, e);
+            } else {
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                u[c] = group_sum<TL::NI>(u[c]);
-                if constexpr (has_q(M)) w[c] = group_sum<TL::NI>(w[c]);
+                for (int c = 0; c < C; ++c) {
+                    u[c] = group_sum<TL::NI>(u[c]);
+                    if constexpr (has_q(M)) w[c] = group_sum<TL::NI>(w[c]);
+                }
+                // e = beta v - beta u
+#pragma unroll
+                for (int c = 0; c < C; ++c) e[c] = fmaf(nbt, u[c], ve[c]);
+                if constexpr (has_q(M)) {
+                    // finish w's butterfly on every lane: sunk into the writer's
+                    // branch, its last DPP step would become mov 0, mov_dpp, add
+#pragma unroll
+                    for (int c = 0; c < C; ++c) asm volatile("" : "+v"(w[c]));
+                    const float qk = L.qk[t];
+                    float ov[C];
+#pragma unroll
+                    for (int c = 0; c < C; ++c) ov[c] = fmaf(e[c], qk, w[c]);
+                    if (ig == 0) store_cols<C>(o + (o0 + t * ostride) + j0, ov);
+                }
+                if (e_out != nullptr && ig == 0) store_cols<C>(e_out + (o0 + t * ostride) + j0, e);
             }
-            // e = beta v - beta u
-#pragma unroll
-            for (int c = 0; c < C; ++c) e[c] = fmaf(nbt, u[c], ve[c]);
-            if constexpr (has_q(M)) {
-                // finish w's butterfly on every lane: sunk into the writer's
-                // branch, its last DPP step would become mov 0, mov_dpp, add
-#pragma unroll
-                for (int c = 0; c < C; ++c) asm volatile("" : "+v"(w[c]));
-                const float qk = L.qk[t];
-                float ov[C];
-#pragma unroll
-                for (int c = 0; c < C; ++c) ov[c] = fmaf(e[c], qk, w[c]);
-                if (ig == 0) store_cols<C>(o + (o0 + t * ostride) + j0, ov);
-            }
-            if (e_out != nullptr && ig == 0) store_cols<C>(e_out + (o0 + t * ostride) + j0, e);
         }
         // delta-rule write: S = S' + k e^T
 #pragma unroll
@@ -478,8 +540,12 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int ig = lane % TL::NI;
-    const int jg = lane / TL::NI;
+    // the swap layout serves the launches whose time is VALU-bound: the
+    // whole-head verify scan and fused round (batched and state-column
+    // launches measured faster with the plain layout)
+    constexpr bool SW = C == 4 && !TABLE && MB == Rows::kFull;
+    const int ig = SW ? (((lane >> 4) & 3) | ((lane >> 1) & 4)) : lane % TL::NI;
+    const int jg = SW ? (lane & 7) : lane / TL::NI;
     const int i0 = ig * R;
     // --- this workgroup: column block blk of chain `chain`
     const int j0 = blk * TL::BCOLS + wave * TL::WCOLS + jg * C;
@@ -570,22 +636,22 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         stage_fence<R, C, MB, kTMax>(inB);
         if (replay) {
             stage_commit<R, C, MA, kTMax>(L, inA, p.T, tid);
-            run_rows<R, C, MA>(L, s, p.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+            run_rows<R, C, MA, SW>(L, s, p.T, nullptr, nullptr, 0, 0, ig, i0, j0);
         }
         if (a.s_out) store_state();   // the committed state: this round's snapshot
         stage_commit<R, C, MB, kTMax>(LB, inB, b.T, tid);
-        run_rows<R, C, MB>(LB, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0);
+        run_rows<R, C, MB, SW>(LB, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0);
         return;
     } else if constexpr (FUSED) {
         if (a.n_prev > 0) {
             const Src p0 = prev_src(0);
             stage<R, C, BF16, MA>(L, p0, tid, load_state);
-            run_rows<R, C, MA>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+            run_rows<R, C, MA, SW>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
             __syncthreads();   // every wave is done with these staged rows
             for (int i = 1; i < a.n_prev; ++i) {
                 const Src pi = prev_src(i);
                 stage<R, C, BF16, MA>(L, pi, tid, [] {});
-                run_rows<R, C, MA>(L, s, pi.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+                run_rows<R, C, MA, SW>(L, s, pi.T, nullptr, nullptr, 0, 0, ig, i0, j0);
                 __syncthreads();
             }
         } else {
@@ -600,11 +666,11 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
     if constexpr (MB == Rows::kFullCols) {
         // the last column is the state after all rows: no separate store
         static_assert(!FUSED && !TABLE, "state columns serve the plain scan");
-        run_rows<R, C, MB>(L, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0,
+        run_rows<R, C, MB, SW>(L, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0,
                            (gfloat*)a.s_cols + chain * kDD, a.col_stride);
         return;
     }
-    run_rows<R, C, MB>(L, s, b.T, a.o, TABLE ? nullptr : a.e_out, o0, ostride, ig, i0, j0);
+    run_rows<R, C, MB, SW>(L, s, b.T, a.o, TABLE ? nullptr : a.e_out, o0, ostride, ig, i0, j0);
     if constexpr (!FUSED) store_state();
 }
 
