@@ -478,15 +478,22 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
                 static_assert(C == 4 && TL::NI == 8, "the swap layout is the whole-head tiling");
                 const int lane = threadIdx.x & 63;
                 const int kc = (lane >> 4) & 3;   // the column this lane reduces
+                const uint32_t col = static_cast<uint32_t>(j0 + kc);
                 const float uo = reduce_scatter4(u);
-                const float eo = fmaf(nbt, uo, sve[t * kD + j0 + kc]);
-                // each column's sum sits in two lanes (lane bit 3); bit 3 = 0 writes
+                const float eo = fmaf(nbt, uo, sve[t * kD + col]);
+                // each column's sum sits in two lanes (lane bit 3); bit 3 = 0
+                // writes, at a wave-uniform row base plus this lane's column
                 const bool writer = (lane & 8) == 0;
+                const size_t row = o0 + t * ostride;
                 if constexpr (has_q(M)) {
-                    const float ov = fmaf(eo, L.qk[t], reduce_scatter4(w));
-                    if (writer) o[o0 + t * ostride + j0 + kc] = ov;
+                    float wo = reduce_scatter4(w);
+                    // keep the last DPP add out of the writer's branch (sunk
+                    // there it becomes a DPP move and an add)
+                    asm volatile("" : "+v"(wo));
+                    const float ov = fmaf(eo, L.qk[t], wo);
+                    if (writer) ((gfloat*)(o + row))[col] = ov;
                 }
-                if (e_out != nullptr && writer) e_out[o0 + t * ostride + j0 + kc] = eo;
+                if (e_out != nullptr && writer) ((gfloat*)(e_out + row))[col] = eo;
                 all_gather4(eo, e);
             } else {
 #pragma unroll
