@@ -218,9 +218,11 @@ def main() -> int:
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    def timed(step_fn, n_warm, n_steps, n_marks):
+    def timed(step_fn, n_warm, n_steps, n_marks, first=0):
+        """n_warm untimed steps, then n_steps between two events.  With n_marks > 0
+        each step also gets n_marks events of its own."""
         for i in range(n_warm):
-            step_fn(i, None)
+            step_fn(first + i, None)
         torch.cuda.synchronize()
         marks = [[ev() for _ in range(n_marks)] for _ in range(n_steps)]
         start, end = ev(), ev()
@@ -229,7 +231,7 @@ def main() -> int:
         wall0 = time.perf_counter()
         start.record(stream)
         for s in range(n_steps):
-            info.append(step_fn(n_warm + s, marks[s]))
+            info.append(step_fn(first + n_warm + s, marks[s] if n_marks else None))
         end.record(stream)
         torch.cuda.synchronize()
         return marks, info, start.elapsed_time(end), time.perf_counter() - wall0
@@ -260,14 +262,20 @@ def main() -> int:
         pair[0], pair[1] = nxt, snap
         return keep_prev
 
-    fm, finfo, f_ms, f_wall = timed(fused_round, args.warmup, args.steps, 2)
-    f_us = [fm[s][0].elapsed_time(fm[s][1]) * 1e3 for s in range(args.steps)]
+    # the timed region holds the K launches back to back and nothing else (an
+    # event pair around every launch would add its own cost to each round), so
+    # a launch's mean duration is the region's event time over K
+    _, finfo, f_ms, f_wall = timed(fused_round, args.warmup, args.steps, 0)
     f_bytes = [chains * round_bytes_per_head(kp, T) for kp in finfo]
     f_flops = [chains * round_flops_per_head(kp, T) for kp in finfo]
-    achieved = sum(f_bytes) / (sum(f_us) * 1e-6) / 1e9
-    tflops = sum(f_flops) / (sum(f_us) * 1e-6) / 1e12
+    mean_launch_us = f_ms * 1e3 / args.steps
+    achieved = sum(f_bytes) / (f_ms * 1e-3) / 1e9
+    tflops = sum(f_flops) / (f_ms * 1e-3) / 1e12
     value = args.steps * T * H * L / (f_ms * 1e-3)
     ms_per_step = f_ms / args.steps
+    # the per-round spread: the next K rounds again, each between its own events
+    fm, _, _, _ = timed(fused_round, 0, args.steps, 2, first=args.warmup + args.steps)
+    f_us = [fm[s][0].elapsed_time(fm[s][1]) * 1e3 for s in range(args.steps)]
 
     # ---------------- split pipeline: scan, then replay when j < 14
     split = None
@@ -673,11 +681,13 @@ def main() -> int:
                       "2176 workgroups)",
             "flops_per_launch": sum(f_flops) / len(f_flops),
             "bytes_per_launch": sum(f_bytes) / len(f_bytes),
-            "mean_launch_us": float(np.mean(f_us)),
+            "mean_launch_us": mean_launch_us,
             "hbm": {"achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                     "frac": achieved / PEAK_HBM_GBPS},
         },
         "round_us": stats_us(f_us),
+        "round_us_note": "round_us: the K rounds after the timed ones, each launch between "
+                         "its own events (the event pairs add a few us per round)",
         "round_us_mall_cold": ({"mean": float(np.mean(cold_us)), "p50": pctl(cold_us, 50)}
                                if cold_us else None),
         "committed_rows_heads_per_s": sum(int(js[(args.warmup + s) % w.rounds]) + 1

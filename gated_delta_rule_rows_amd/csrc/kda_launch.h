@@ -54,6 +54,7 @@ struct ScanArgs {
     size_t col_stride;
     long long n_chains;  // (layer, head) or (layer, session, head) chains
     long long n_head_chains;   // chains run whole-head before a split tail (launcher)
+    unsigned long long entry_mul;  // batched arm: table entries run in order (i * entry_mul) mod n
     int H;
     int T;               // rows this launch runs
     int T_stride;        // rows per layer in this launch's input layout
