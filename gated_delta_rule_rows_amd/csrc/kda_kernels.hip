@@ -807,13 +807,14 @@ __global__ void __launch_bounds__(kRerollThreads) kda_reroll_kernel(RerollArgs a
 //             per (row, head) with 1e-6 under the square root;
 //   g       : max(-softplus(a), -5);     beta : sigmoid(b).
 // Given the raw rows, every row's conv window x_{t-3..t} is known, so rows
-// are independent: one workgroup of 128 lanes per (layer, row, head), a lane
-// per head channel (q, k, v and g of that channel), 16 loads per lane issued
-// before any arithmetic.  The 15 rows of a (layer, head) re-read each raw row
-// up to four times; the blockIdx -> work mapping keeps them on one XCD (the
-// dispatcher deals workgroups round-robin over the 8 XCDs), so the re-reads
-// hit that XCD's L2.  The row T-1 workgroup also writes the ring after the
-// round: it is that row's conv window minus its oldest entry.
+// are independent: one workgroup of 128 lanes per (layer, head, 3 rows), a
+// lane per head channel (q, k, v and g of that channel), the window's 6 raw
+// or ring rows loaded once and every load issued before any arithmetic.
+// Neighbouring row groups of a (layer, head) share 3 window rows; the
+// blockIdx -> work mapping keeps them on one XCD (the dispatcher deals
+// workgroups round-robin over the 8 XCDs), so those re-reads hit that XCD's
+// L2.  The workgroup holding row T-1 also writes the ring after the round:
+// the last three entries of the sequence.
 constexpr int kOpsThreads = kD;   // 2 waves
 constexpr int kXcds = 8;
 constexpr float kNormEps = 1e-6f;
@@ -826,83 +827,115 @@ __device__ __forceinline__ float softplus_f(float a) {
     return fmaxf(a, 0.0f) + __builtin_amdgcn_logf(1.0f + exp_f(-fabsf(a))) * 0.69314718055994531f;
 }
 
+// Rows per workgroup: 3 measured fastest (28-29 us for 34 layers x 64 heads
+// x 15 rows in f32, 35 us in bf16), against 29-30 and 30-34 us for 2, 4, 5
+// or 8 rows, and 34-37 / 48-53 us for one row per workgroup.
+constexpr int kRowsPerGroup = 3;
+
 template <bool BF16>
 __global__ void __launch_bounds__(kOpsThreads) kda_row_ops_kernel(RowOpsArgs a) {
     const int j = threadIdx.x;
     const int wave = j >> 6;
-    // XCD-aware work index: consecutive work items share an XCD
     const long long nwork = a.nwork;
     const long long per_xcd = (nwork + kXcds - 1) / kXcds;
     const long long bid = blockIdx.x;
     const long long work = (bid % kXcds) * per_xcd + bid / kXcds;
-    if (work >= nwork) return;   // whole workgroup: no barrier is skipped by part of it
+    if (work >= nwork) return;
     const int T = a.T;
-    const long long lh = work / T;
-    const int t = static_cast<int>(work % T);
+    const int chunks = (T + kRowsPerGroup - 1) / kRowsPerGroup;
+    const long long lh = work / chunks;
+    const int r0 = static_cast<int>(work % chunks) * kRowsPerGroup;
+    const int nr = min(kRowsPerGroup, T - r0);
     const long long l = lh / a.H;
     const long long h = lh % a.H;
     const long long HD = static_cast<long long>(a.H) * kD;
     const long long C = 3 * HD;
-    const long long c0 = h * kD + j;   // this lane's q channel; k at +HD, v at +2HD
+    const long long c0 = h * kD + j;
 
-    // conv window rows t-3..t per block: ring rows for t-3+m < 0, raw rows after
-    float xw[3][4];
+    // the conv window of these rows: sequence entries r0 .. r0 + kRowsPerGroup
+    // + 2, where entries 0..2 are the ring rows and entry 3 + r is raw row r;
+    // loads are unconditional, rows past T clamped
+    float xw[3][kRowsPerGroup + kRingRows];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const int r = t - 3 + m;
+    for (int m = 0; m < kRowsPerGroup + kRingRows; ++m) {
+        const int e = r0 + m;
 #pragma unroll
         for (int blk = 0; blk < 3; ++blk) {
-            const long long c = c0 + blk * HD;
-            if (r < 0)
-                xw[blk][m] = a.ring_in[(l * kRingRows + (r + kRingRows)) * C + c];
-            else
-                xw[blk][m] = load1<BF16>(a.x, static_cast<size_t>((l * T + r) * C + c));
+            if (e < kRingRows) {
+                xw[blk][m] = a.ring_in[(l * kRingRows + e) * C + c0 + blk * HD];
+            } else {
+                const int rr = min(e - kRingRows, T - 1);
+                xw[blk][m] = load1<BF16>(a.x, static_cast<size_t>((l * T + rr) * C + c0 + blk * HD));
+            }
         }
     }
-    const float xa = load1<BF16>(a.a, static_cast<size_t>((l * T + t) * HD + c0));
+    float xa[kRowsPerGroup];
+#pragma unroll
+    for (int i = 0; i < kRowsPerGroup; ++i) {
+        const int rr = min(r0 + i, T - 1);
+        xa[i] = load1<BF16>(a.a, static_cast<size_t>((l * T + rr) * HD + c0));
+    }
     float4 w[3];
 #pragma unroll
     for (int blk = 0; blk < 3; ++blk)
         w[blk] = *reinterpret_cast<const float4*>(a.w + (l * C + c0 + blk * HD) * 4);
     float bt = 0.0f;
-    if (j == 0) bt = load1<BF16>(a.b, static_cast<size_t>((l * T + t) * a.H + h));
+    if (j < nr) bt = load1<BF16>(a.b, static_cast<size_t>((l * T + r0 + j) * a.H + h));
 
-    float y[3];
+    __shared__ float part[kRowsPerGroup][2][2];
+    float yq[kRowsPerGroup], yk[kRowsPerGroup];
 #pragma unroll
-    for (int blk = 0; blk < 3; ++blk) {
-        float acc = w[blk].x * xw[blk][0];
-        acc = fmaf(w[blk].y, xw[blk][1], acc);
-        acc = fmaf(w[blk].z, xw[blk][2], acc);
-        acc = fmaf(w[blk].w, xw[blk][3], acc);
-        y[blk] = silu_f(acc);
-    }
-    const size_t o = static_cast<size_t>(((l * T + t) * a.H + h) * kD + j);
-    a.v[o] = y[2];
-    a.g[o] = fmaxf(-softplus_f(xa), kGateLo);
-    if (j == 0) a.beta[(l * T + t) * a.H + h] = rcp_f(1.0f + exp_f(-bt));
-
-    float sq = y[0] * y[0];
-    float sk = y[1] * y[1];
+    for (int i = 0; i < kRowsPerGroup; ++i) {
+        if (i < nr) {
+            float y[3];
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        sq += __shfl_xor(sq, off);
-        sk += __shfl_xor(sk, off);
+            for (int blk = 0; blk < 3; ++blk) {
+                float acc = w[blk].x * xw[blk][i];
+                acc = fmaf(w[blk].y, xw[blk][i + 1], acc);
+                acc = fmaf(w[blk].z, xw[blk][i + 2], acc);
+                acc = fmaf(w[blk].w, xw[blk][i + 3], acc);
+                y[blk] = silu_f(acc);
+            }
+            const size_t o = static_cast<size_t>(((l * T + r0 + i) * a.H + h) * kD + j);
+            a.v[o] = y[2];
+            a.g[o] = fmaxf(-softplus_f(xa[i]), kGateLo);
+            yq[i] = y[0];
+            yk[i] = y[1];
+            float sq = y[0] * y[0];
+            float sk = y[1] * y[1];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                sq += __shfl_xor(sq, off);
+                sk += __shfl_xor(sk, off);
+            }
+            if ((j & 63) == 0) {
+                part[i][wave][0] = sq;
+                part[i][wave][1] = sk;
+            }
+        }
     }
-    __shared__ float part[2][2];   // [wave][q, k]
-    if ((j & 63) == 0) {
-        part[wave][0] = sq;
-        part[wave][1] = sk;
-    }
+    if (j < nr) a.beta[(l * T + r0 + j) * a.H + h] = rcp_f(1.0f + exp_f(-bt));
     __syncthreads();
-    a.q[o] = y[0] * __builtin_amdgcn_rsqf(part[0][0] + part[1][0] + kNormEps);
-    a.k[o] = y[1] * __builtin_amdgcn_rsqf(part[0][1] + part[1][1] + kNormEps);
-
-    if (a.ring_out && t == T - 1) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerGroup; ++i) {
+        if (i < nr) {
+            const size_t o = static_cast<size_t>(((l * T + r0 + i) * a.H + h) * kD + j);
+            a.q[o] = yq[i] * __builtin_amdgcn_rsqf(part[i][0][0] + part[i][1][0] + kNormEps);
+            a.k[o] = yk[i] * __builtin_amdgcn_rsqf(part[i][0][1] + part[i][1][1] + kNormEps);
+        }
+    }
+    if (a.ring_out && r0 + nr == T) {
+        // entries T, T+1, T+2: the ring after all T rows (local index T - r0 + m)
 #pragma unroll
         for (int m = 0; m < kRingRows; ++m)
 #pragma unroll
-            for (int blk = 0; blk < 3; ++blk)
-                a.ring_out[(l * kRingRows + m) * C + c0 + blk * HD] = xw[blk][m + 1];
+            for (int blk = 0; blk < 3; ++blk) {
+                float x = xw[blk][m];
+#pragma unroll
+                for (int n = 1; n <= kRowsPerGroup; ++n)
+                    if (n == nr) x = xw[blk][m + n];
+                a.ring_out[(l * kRingRows + m) * C + c0 + blk * HD] = x;
+            }
     }
 }
 
@@ -1262,7 +1295,7 @@ hipError_t launch_reroll(const RerollArgs& a0, bool bf16, hipStream_t stream) {
 
 hipError_t launch_row_ops(const RowOpsArgs& a0, bool bf16, hipStream_t stream) {
     RowOpsArgs a = a0;
-    a.nwork = static_cast<long long>(a.L) * a.H * a.T;
+    a.nwork = static_cast<long long>(a.L) * a.H * ((a.T + kRowsPerGroup - 1) / kRowsPerGroup);
     const long long per_xcd = (a.nwork + kXcds - 1) / kXcds;
     const unsigned long long blocks = static_cast<unsigned long long>(per_xcd) * kXcds;
     if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;

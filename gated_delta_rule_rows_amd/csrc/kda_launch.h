@@ -103,7 +103,7 @@ struct RowOpsArgs {
     float* v;
     float* g;
     float* beta;            // [L][T][H]
-    long long nwork;        // L*H*T, set by launch_row_ops
+    long long nwork;        // workgroups with work: L*H*ceil(T/3), set by launch_row_ops
     int L;
     int T;
     int H;
