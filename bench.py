@@ -171,6 +171,9 @@ def main() -> int:
     ap.add_argument("--accept-launches", type=int, default=32,
                     help="kda_accept_greedy launches at t=15, V=150,000 (0 skips the figure)")
     ap.add_argument("--no-split", action="store_true", help="skip the split scan + replay pipeline")
+    ap.add_argument("--loop-rounds", type=int, default=16,
+                    help="rounds of the whole verify loop (row ops, fused round, greedy "
+                         "accept with its readback, conv re-roll); 0 skips it")
     ap.add_argument("--columns-rounds", type=int, default=16,
                     help="rounds of the state-column rollback arm (0 skips it)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -651,6 +654,75 @@ def main() -> int:
         }
         del ring_snap, raw, ring_out, dsts, table
 
+    # the whole verify loop of one session, round after round: projections ->
+    # row ops -> fused round (replay of the previous round's kept rows, scan) ->
+    # greedy accept, whose j is read back (one u32, as the serving host needs
+    # it) and sets keep -> the conv ring after keep rows -> next round
+    verify_loop = None
+    if args.loop_rounds > 0:
+        C = 3 * H * D
+        V = synth.VOCAB
+        n_in = 4
+        proj = [synth.row_op_inputs(w.seed, 100 + i, L, T, H) for i in range(n_in)]
+        px = [torch.from_numpy(p_["x"]).cuda() for p_ in proj]
+        pa = [torch.from_numpy(p_["a"]).cuda() for p_ in proj]
+        pb = [torch.from_numpy(p_["b"]).cuda() for p_ in proj]
+        lw = torch.from_numpy(proj[0]["w"]).cuda()
+        rings = [torch.from_numpy(proj[0]["ring"]).cuda(), torch.empty(L, 3, C, device="cuda")]
+        lg = []
+        for i in range(n_in):
+            logits, drafts, _ = synth.accept_round(w.seed, 100 + i, T, V, int(js[i % w.rounds]))
+            lg.append((torch.from_numpy(logits).cuda(),
+                       torch.from_numpy(drafts.view(np.int32)).cuda()))
+        sets = [[torch.empty(L, T, H, D, device="cuda") for _ in range(4)]
+                + [torch.empty(L, T, H, device="cuda"), torch.empty(L, T, H, D, device="cuda")]
+                for _ in range(2)]   # q, k, v, g, beta, e: this round's and the previous
+        lst = [torch.zeros(L, H, D, D, device="cuda") for _ in range(2)]
+        lo = torch.empty(L, T, H, D, device="cuda")
+        vam = torch.empty(T, dtype=torch.int32, device="cuda")
+        out2 = torch.empty(2, dtype=torch.int32, device="cuda")
+        work = kda.accept_workspace()
+        lp = {"keep": 0}
+
+        def loop_round(i):
+            cur, prv = sets[i % 2], sets[(i + 1) % 2]
+            x = px[i % n_in]
+            kda.kda_row_ops(x, pa[i % n_in], pb[i % n_in], lw, rings[i % 2], *cur[:5])
+            if lp["keep"]:
+                kda.kda_verify_round(lst[i % 2], lst[(i + 1) % 2],
+                                     (prv[1], None, prv[3], None, prv[5]), lp["keep"],
+                                     *cur[:5], lo, e=cur[5])
+            else:
+                kda.kda_verify_round(lst[i % 2], lst[(i + 1) % 2], None, 0, *cur[:5], lo,
+                                     e=cur[5])
+            kda.kda_accept_greedy(*lg[i % n_in], vam, out2, work)
+            keep = int(out2[0].item()) + 1   # the round's one readback
+            kda.kda_conv_reroll(rings[i % 2], x, keep, rings[(i + 1) % 2])
+            lp["keep"] = keep
+            return keep
+
+        for i in range(3):
+            loop_round(i)
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        t0 = time.perf_counter()
+        a.record(stream)
+        keeps = [loop_round(3 + i) for i in range(args.loop_rounds)]
+        b.record(stream)
+        torch.cuda.synchronize()
+        lw_s = time.perf_counter() - t0
+        l_us = a.elapsed_time(b) * 1e3 / args.loop_rounds
+        verify_loop = {
+            "rounds": args.loop_rounds, "us_per_round": l_us,
+            "wall_us_per_round": lw_s * 1e6 / args.loop_rounds,
+            "rows_heads_per_s": T * H * L / (l_us * 1e-6),
+            "committed_rows_heads_per_s": float(np.mean(keeps)) * H * L / (l_us * 1e-6),
+            "mean_keep": float(np.mean(keeps)),
+            "note": "kda_row_ops + kda_verify_round + kda_accept_greedy (t=15, V=150,000) "
+                    "+ j read back + kda_conv_reroll, per round, one session",
+        }
+        del px, pa, pb, lw, rings, lg, sets, lst, lo
+
     line = {
         "metric": "verify-scan rows*heads/s and achieved HBM GB/s (% peak), K=14, 64 heads",
         "value": value,
@@ -696,6 +768,7 @@ def main() -> int:
         "state_columns": columns,
         "accept": accept,
         "rollback_extras": rollback_extras,
+        "verify_loop": verify_loop,
         "per_layer_graph": per_layer,
         "tp8_share": tp_share,
         "batched": batched,
