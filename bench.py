@@ -684,44 +684,62 @@ def main() -> int:
         work = kda.accept_workspace()
         lp = {"keep": 0}
 
-        def loop_round(i):
+        out2s = [out2, torch.empty(2, dtype=torch.int32, device="cuda")]
+
+        def loop_round(i, device_keep=False):
             cur, prv = sets[i % 2], sets[(i + 1) % 2]
             x = px[i % n_in]
             kda.kda_row_ops(x, pa[i % n_in], pb[i % n_in], lw, rings[i % 2], *cur[:5])
-            if lp["keep"]:
+            if lp["keep"] is not None:
                 kda.kda_verify_round(lst[i % 2], lst[(i + 1) % 2],
                                      (prv[1], None, prv[3], None, prv[5]), lp["keep"],
                                      *cur[:5], lo, e=cur[5])
             else:
                 kda.kda_verify_round(lst[i % 2], lst[(i + 1) % 2], None, 0, *cur[:5], lo,
                                      e=cur[5])
-            kda.kda_accept_greedy(*lg[i % n_in], vam, out2, work)
-            keep = int(out2[0].item()) + 1   # the round's one readback
+            o2 = out2s[i % 2]
+            kda.kda_accept_greedy(*lg[i % n_in], vam, o2, work)
+            if device_keep:
+                # j stays on the device: the rollback kernels read it themselves
+                kda.kda_conv_reroll(rings[i % 2], x, o2, rings[(i + 1) % 2])
+                lp["keep"] = o2
+                return None
+            keep = int(o2[0].item()) + 1   # the round's one readback
             kda.kda_conv_reroll(rings[i % 2], x, keep, rings[(i + 1) % 2])
             lp["keep"] = keep
             return keep
 
-        for i in range(3):
-            loop_round(i)
-        torch.cuda.synchronize()
-        a, b = ev(), ev()
-        t0 = time.perf_counter()
-        a.record(stream)
-        keeps = [loop_round(3 + i) for i in range(args.loop_rounds)]
-        b.record(stream)
-        torch.cuda.synchronize()
-        lw_s = time.perf_counter() - t0
-        l_us = a.elapsed_time(b) * 1e3 / args.loop_rounds
+        def time_loop(device_keep):
+            lp["keep"] = None
+            for i in range(3):
+                loop_round(i, device_keep)
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            t0 = time.perf_counter()
+            a.record(stream)
+            ks = [loop_round(3 + i, device_keep) for i in range(args.loop_rounds)]
+            b.record(stream)
+            torch.cuda.synchronize()
+            return (a.elapsed_time(b) * 1e3 / args.loop_rounds,
+                    (time.perf_counter() - t0) * 1e6 / args.loop_rounds, ks)
+
+        l_us, l_wall, keeps = time_loop(False)
+        d_us, d_wall, _ = time_loop(True)
         verify_loop = {
             "rounds": args.loop_rounds, "us_per_round": l_us,
-            "wall_us_per_round": lw_s * 1e6 / args.loop_rounds,
+            "wall_us_per_round": l_wall,
             "rows_heads_per_s": T * H * L / (l_us * 1e-6),
             "committed_rows_heads_per_s": float(np.mean(keeps)) * H * L / (l_us * 1e-6),
             "mean_keep": float(np.mean(keeps)),
+            "device_keep": {"us_per_round": d_us, "wall_us_per_round": d_wall,
+                            "rows_heads_per_s": T * H * L / (d_us * 1e-6),
+                            "note": "the same loop with j left on the device "
+                                    "(kda_verify_round_dev, kda_conv_reroll_dev): no "
+                                    "readback between the accept and the rollback"},
             "note": "kda_row_ops + kda_verify_round + kda_accept_greedy (t=15, V=150,000) "
                     "+ j read back + kda_conv_reroll, per round, one session",
         }
-        del px, pa, pb, lw, rings, lg, sets, lst, lo
+        del px, pa, pb, lw, rings, lg, sets, lst, lo, out2s
 
     line = {
         "metric": "verify-scan rows*heads/s and achieved HBM GB/s (% peak), K=14, 64 heads",

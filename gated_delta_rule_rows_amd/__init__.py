@@ -82,6 +82,9 @@ def load():
                                      i, i, i, i, p]
     lib.kda_accept_greedy.argtypes = [p, i, i, ctypes.c_longlong, i, p, p, p, p, p]
     lib.kda_conv_reroll.argtypes = [p, p, p, i, i, i, ctypes.c_longlong, i, p]
+    lib.kda_conv_reroll_dev.argtypes = [p, p, p, i, i, p, ctypes.c_longlong, i, p]
+    lib.kda_verify_round_dev.argtypes = [p, p, p, p, p, p, p, i, p, p, p, p, p, p, p, p,
+                                         i, i, i, i, p]
     lib.kda_copy_batch.argtypes = [p, i, ctypes.c_longlong, p]
     lib.kda_row_ops.argtypes = [p] * 11 + [i, i, i, i, p]
     lib.kda_verify_round_multi.argtypes = [p, p, ctypes.POINTER(_PrevRound), i, p, p, p, p, p,
@@ -89,7 +92,8 @@ def load():
     for fn in (lib.kda_scan_rows, lib.kda_snapshot, lib.kda_replay, lib.kda_scan_batched,
                lib.kda_verify_round, lib.kda_accept_greedy, lib.kda_conv_reroll,
                lib.kda_copy_batch, lib.kda_row_ops, lib.kda_verify_round_multi,
-               lib.kda_scan_rows_columns, lib.kda_abi_version):
+               lib.kda_scan_rows_columns, lib.kda_verify_round_dev, lib.kda_conv_reroll_dev,
+               lib.kda_abi_version):
         fn.restype = i
     lib.kda_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -246,7 +250,17 @@ def kda_replay(snap, s_out, k, v, g, beta, keep: int, e=None, stream=None) -> No
                           H, dt, _stream(stream)))
 
 
-def kda_verify_round(snap_prev, snap_out, prev, keep: int, q, k, v, g, beta, o, e=None,
+def _j_dev(j):
+    """The accepted-draft count on the device: a 1-element (or out2-style) int32
+    or uint32 tensor whose first element is j."""
+    if not (isinstance(j, torch.Tensor) and j.is_cuda):
+        raise TypeError("a device keep is given as j, a device tensor (kda_accept_greedy's out2)")
+    if j.dtype not in (torch.int32, torch.uint32) or j.numel() < 1 or not j.is_contiguous():
+        raise ValueError("j must be a contiguous int32 tensor with j at element 0")
+    return ctypes.c_void_p(j.data_ptr())
+
+
+def kda_verify_round(snap_prev, snap_out, prev, keep, q, k, v, g, beta, o, e=None,
                      stream=None) -> None:
     """One fused verify round.
 
@@ -254,6 +268,8 @@ def kda_verify_round(snap_prev, snap_out, prev, keep: int, q, k, v, g, beta, o, 
     stash e is given; prev may be None when keep == 0).  snap_out receives
     snap_prev advanced by the previous round's first `keep` rows (this round's
     snapshot); o receives this round's outputs, e (optional) its stash plane.
+    keep is an int, or a device tensor j (kda_accept_greedy's out2) for keep =
+    j + 1 read on the device (kda_verify_round_dev).
     """
     lib = load()
     L, T, H = _rows_shape(q, k, v, g, beta)
@@ -272,6 +288,15 @@ def kda_verify_round(snap_prev, snap_out, prev, keep: int, q, k, v, g, beta, o, 
         Lp, T_prev, Hp, pdt = _kept_rows(pk, pv, pg, pb, pe, "prev")
         if (Lp, Hp) != (L, H) or pdt != dt:
             raise ValueError("previous round's rows do not match this round's L, H, dtype")
+    if isinstance(keep, torch.Tensor):
+        if prev is None:
+            raise ValueError("a device keep needs the previous round's rows")
+        _check(lib.kda_verify_round_dev(
+            _dev(snap_prev, "snap_prev"), _dev(snap_out, "snap_out"), _dev(pk, "pk"),
+            _dev(pv, "pv"), _dev(pg, "pg"), _dev(pb, "pbeta"), _dev(pe, "pe"), int(T_prev),
+            _j_dev(keep), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(g, "g"),
+            _dev(beta, "beta"), _dev(o, "o"), _dev(e, "e"), L, T, H, dt, _stream(stream)))
+        return
     _check(lib.kda_verify_round(
         _dev(snap_prev, "snap_prev"), _dev(snap_out, "snap_out"), _dev(pk, "pk"), _dev(pv, "pv"),
         _dev(pg, "pg"), _dev(pb, "pbeta"), _dev(pe, "pe"), int(T_prev), int(keep), _dev(q, "q"),
@@ -434,9 +459,10 @@ def kda_row_ops(x, a, b, conv_w, ring_in, q, k, v, g, beta, ring_out=None, strea
                            L, T, H, dt, _stream(stream)))
 
 
-def kda_conv_reroll(ring_snap, raw, keep: int, ring_out, stream=None) -> None:
+def kda_conv_reroll(ring_snap, raw, keep, ring_out, stream=None) -> None:
     """ring_out = the short-conv ring after `keep` accepted rows: ring_snap [L][3][C]
-    rolled once per kept row over the round's raw conv inputs raw [L][T_round][C]."""
+    rolled once per kept row over the round's raw conv inputs raw [L][T_round][C].
+    keep is an int, or a device tensor j for keep = j + 1 read on the device."""
     lib = load()
     if raw.dim() != 3:
         raise ValueError(f"raw must be [L][T_round][C], got {tuple(raw.shape)}")
@@ -444,6 +470,11 @@ def kda_conv_reroll(ring_snap, raw, keep: int, ring_out, stream=None) -> None:
     _state(ring_snap, (L, RING_ROWS, C), "ring_snap")
     _state(ring_out, (L, RING_ROWS, C), "ring_out")
     dt = _in_dtype((raw,))
+    if isinstance(keep, torch.Tensor):
+        _check(lib.kda_conv_reroll_dev(_dev(ring_snap, "ring_snap"), _dev(raw, "raw"),
+                                       _dev(ring_out, "ring_out"), L, T, _j_dev(keep), C, dt,
+                                       _stream(stream)))
+        return
     _check(lib.kda_conv_reroll(_dev(ring_snap, "ring_snap"), _dev(raw, "raw"),
                                _dev(ring_out, "ring_out"), L, T, int(keep), C, dt,
                                _stream(stream)))

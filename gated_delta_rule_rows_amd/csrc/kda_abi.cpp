@@ -115,10 +115,11 @@ static_assert(kda::kNoToken == KDA_NO_TOKEN, "one sentinel");
 static_assert(kda::kRingRows == KDA_CONV_RING_ROWS, "one ring depth");
 
 // The fused round behind kda_verify_round and kda_verify_round_multi.
+// keep_j (one_round only): the kept rows of prev[0] come from device memory.
 int verify_round(const char* fn, bool one_round, const float* snap_base, float* snap_out,
                  const kda_prev_round* prev, int n_prev, const void* q, const void* k,
                  const void* v, const void* g, const void* beta, float* o, float* e, int L,
-                 int T, int H, int in_dtype, void* stream) {
+                 int T, int H, int in_dtype, void* stream, const uint32_t* keep_j = nullptr) {
     int rc;
     if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H)) ||
         (rc = check_rows(fn, "T", T)))
@@ -133,7 +134,7 @@ int verify_round(const char* fn, bool one_round, const float* snap_base, float* 
     // earlier rounds: validate each, keep those with rows to replay
     kda::ScanArgs a{};
     int stash = -1;   // all replayed rounds read the stash plane (1) or none does (0)
-    Span in[6 + 5 * KDA_MAX_PREV_ROUNDS];
+    Span in[7 + 5 * KDA_MAX_PREV_ROUNDS];
     int n_in = 0;
     in[n_in++] = {one_round ? "snap_prev" : "snap_base", snap_base, chains * kStateBytes, 16,
                   false};
@@ -180,6 +181,7 @@ int verify_round(const char* fn, bool one_round, const float* snap_base, float* 
         d.k = pr.k; d.g = pr.g; d.T = pr.T; d.keep = pr.keep;
         if (st) d.e = pr.e; else { d.v = pr.v; d.beta = pr.beta; }
     }
+    if (keep_j) in[n_in++] = {"j", keep_j, 4, 4, false};   // read by every workgroup
     const Span out[] = {
         {"snap_out", snap_out, chains * kStateBytes, 16, true},
         {"o", o, rows * kRowElems * 4, 16, false},
@@ -191,9 +193,42 @@ int verify_round(const char* fn, bool one_round, const float* snap_base, float* 
     a.s_in = snap_base; a.s_out = snap_out;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.o = o; a.e_out = e;
     a.n_chains = static_cast<long long>(chains); a.H = H; a.T = T; a.T_stride = T;
+    a.keep_j = keep_j;
     const kda::Launch kind = stash == 1 ? kda::Launch::kRoundStash : kda::Launch::kRound;
     return launched(fn, kda::launch_scan(a, kind, in_dtype == KDA_IN_BF16,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int conv_reroll(const char* fn, const float* ring_snap, const void* raw, float* ring_out, int L,
+                int T_round, int keep, const uint32_t* keep_j, long long C, int in_dtype,
+                void* stream) {
+    int rc;
+    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_rows(fn, "T_round", T_round))) return rc;
+    if (L < 1) return refuse(KDA_ERR_RANGE, "%s: L=%d, need L >= 1", fn, L);
+    if (keep < 1 || keep > T_round)
+        return refuse(KDA_ERR_RANGE, "%s: keep=%d outside 1..T_round=%d", fn, keep, T_round);
+    if (C < 1 || C > (1ll << 40) / (static_cast<long long>(L) * T_round))
+        return refuse(KDA_ERR_RANGE, "%s: C=%lld outside 1..%lld", fn, C,
+                      (1ll << 40) / (static_cast<long long>(L) * T_round));
+    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
+    const unsigned long long ring = static_cast<unsigned long long>(L) * KDA_CONV_RING_ROWS * C;
+    const Span in[] = {
+        {"ring_snap", ring_snap, ring * 4, 4, false},
+        {"raw", raw, static_cast<unsigned long long>(L) * T_round * C * es, es, false},
+    };
+    const Span out[] = {{"ring_out", ring_out, ring * 4, 4, false}};
+    if ((rc = check_spans(fn, in, 2)) || (rc = check_spans(fn, out, 1)) ||
+        (rc = check_alias(fn, out, 1, in, 2)))
+        return rc;
+    if (keep_j) {
+        const Span js[] = {{"j", keep_j, 4, 4, false}};
+        if ((rc = check_alias(fn, out, 1, js, 1))) return rc;
+    }
+    kda::RerollArgs a{};
+    a.ring_snap = ring_snap; a.raw = raw; a.ring_out = ring_out;
+    a.C = C; a.L = L; a.T = T_round; a.keep = keep; a.keep_j = keep_j;
+    return launched(fn, kda::launch_reroll(a, in_dtype == KDA_IN_BF16,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -376,6 +411,24 @@ int kda_verify_round(const float* snap_prev, float* snap_out, const void* pk, co
                         o, e, L, T, H, in_dtype, stream);
 }
 
+int kda_verify_round_dev(const float* snap_prev, float* snap_out, const void* pk, const void* pv,
+                         const void* pg, const void* pbeta, const float* pe, int T_prev,
+                         const uint32_t* j, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, float* o, float* e, int L, int T,
+                         int H, int in_dtype, void* stream) {
+    const char* fn = "kda_verify_round_dev";
+    if (T_prev < 1 || T_prev > KDA_T_MAX)
+        return refuse(KDA_ERR_RANGE, "%s: T_prev=%d outside 1..%d", fn, T_prev, KDA_T_MAX);
+    if (!j) return refuse(KDA_ERR_ARG, "%s: j is NULL", fn);
+    if (reinterpret_cast<uintptr_t>(j) % 4 != 0)
+        return refuse(KDA_ERR_ALIGN, "%s: j is not 4-byte aligned", fn);
+    if (!snap_out) return refuse(KDA_ERR_ARG, "%s: snap_out is NULL", fn);
+    // validated for the most rows the device value can select
+    const kda_prev_round pr = {pk, pv, pg, pbeta, pe, T_prev, T_prev};
+    return verify_round(fn, true, snap_prev, snap_out, &pr, 1, q, k, v, g, beta, o, e, L, T, H,
+                        in_dtype, stream, j);
+}
+
 int kda_verify_round_multi(const float* snap_base, float* snap_out, const kda_prev_round* prev,
                            int n_prev, const void* q, const void* k, const void* v,
                            const void* g, const void* beta, float* o, float* e, int L, int T,
@@ -456,30 +509,18 @@ int kda_row_ops(const void* x, const void* a, const void* b, const float* conv_w
 
 int kda_conv_reroll(const float* ring_snap, const void* raw, float* ring_out, int L,
                     int T_round, int keep, long long C, int in_dtype, void* stream) {
-    const char* fn = "kda_conv_reroll";
-    int rc;
-    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_rows(fn, "T_round", T_round))) return rc;
-    if (L < 1) return refuse(KDA_ERR_RANGE, "%s: L=%d, need L >= 1", fn, L);
-    if (keep < 1 || keep > T_round)
-        return refuse(KDA_ERR_RANGE, "%s: keep=%d outside 1..T_round=%d", fn, keep, T_round);
-    if (C < 1 || C > (1ll << 40) / (static_cast<long long>(L) * T_round))
-        return refuse(KDA_ERR_RANGE, "%s: C=%lld outside 1..%lld", fn, C,
-                      (1ll << 40) / (static_cast<long long>(L) * T_round));
-    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
-    const unsigned long long ring = static_cast<unsigned long long>(L) * KDA_CONV_RING_ROWS * C;
-    const Span in[] = {
-        {"ring_snap", ring_snap, ring * 4, 4, false},
-        {"raw", raw, static_cast<unsigned long long>(L) * T_round * C * es, es, false},
-    };
-    const Span out[] = {{"ring_out", ring_out, ring * 4, 4, false}};
-    if ((rc = check_spans(fn, in, 2)) || (rc = check_spans(fn, out, 1)) ||
-        (rc = check_alias(fn, out, 1, in, 2)))
-        return rc;
-    kda::RerollArgs a{};
-    a.ring_snap = ring_snap; a.raw = raw; a.ring_out = ring_out;
-    a.C = C; a.L = L; a.T = T_round; a.keep = keep;
-    return launched(fn, kda::launch_reroll(a, in_dtype == KDA_IN_BF16,
-                                           static_cast<hipStream_t>(stream)));
+    return conv_reroll("kda_conv_reroll", ring_snap, raw, ring_out, L, T_round, keep, nullptr, C,
+                       in_dtype, stream);
+}
+
+int kda_conv_reroll_dev(const float* ring_snap, const void* raw, float* ring_out, int L,
+                        int T_round, const uint32_t* j, long long C, int in_dtype, void* stream) {
+    const char* fn = "kda_conv_reroll_dev";
+    if (!j) return refuse(KDA_ERR_ARG, "%s: j is NULL", fn);
+    if (reinterpret_cast<uintptr_t>(j) % 4 != 0)
+        return refuse(KDA_ERR_ALIGN, "%s: j is not 4-byte aligned", fn);
+    // keep = T_round passes the host range check; the kernel reads the real one
+    return conv_reroll(fn, ring_snap, raw, ring_out, L, T_round, T_round, j, C, in_dtype, stream);
 }
 
 int kda_copy_batch(const uint64_t* table, int n, long long words, void* stream) {

@@ -623,6 +623,8 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         p.row0 = (l * pr.T * a.H + h) * kD; p.rstride = static_cast<size_t>(a.H) * kD;
         p.b0 = l * pr.T * a.H + h;           p.bstride = a.H;
         p.T = pr.keep;
+        if (i == 0 && a.keep_j != nullptr)   // device-side keep (wave-uniform scalar load)
+            p.T = static_cast<int>(min(*a.keep_j, static_cast<uint32_t>(pr.T - 1))) + 1;
         return p;
     };
 
@@ -759,9 +761,12 @@ __global__ void __launch_bounds__(kRerollThreads) kda_reroll_kernel(RerollArgs a
     const long long c = (blockIdx.x % a.blocks_per_layer) * kRerollChans +
                         static_cast<long long>(threadIdx.x) * 4;
     if (c >= a.C) return;
+    const int keep = a.keep_j != nullptr
+                         ? static_cast<int>(min(*a.keep_j, static_cast<uint32_t>(a.T - 1))) + 1
+                         : a.keep;
 #pragma unroll
     for (int m = 0; m < kRingRows; ++m) {
-        const int sidx = a.keep + m;
+        const int sidx = keep + m;
         float4 x;
         if (sidx < kRingRows) {
             const float* src = a.ring_snap + (l * kRingRows + sidx) * a.C;

@@ -48,6 +48,9 @@ struct ScanArgs {
     // from s_in before this launch's rows (entries with keep = 0 left out)
     PrevRows prev[kMaxPrev];
     int n_prev;
+    // if set, prev[0] replays min(*keep_j, prev[0].T - 1) + 1 rows: j, the
+    // accepted-draft count, as the greedy accept left it in device memory
+    const uint32_t* keep_j;
     // state columns (kScanColumns): the state after row t of chain c at
     // s_cols + t * col_stride + c * 128 * 128
     float* s_cols;
@@ -84,6 +87,7 @@ struct RerollArgs {
     float* ring_out;          // [L][3][C]
     long long C;
     long long blocks_per_layer;   // set by launch_reroll
+    const uint32_t* keep_j;       // if set, keep = min(*keep_j, T - 1) + 1
     int L;
     int T;
     int keep;

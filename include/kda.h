@@ -52,7 +52,7 @@ extern "C" {
 #define KDA_HEAD_DIM 128   /* d_k = d_v; glm5_spec_ppn_gate.rs fixture head_dim */
 #define KDA_T_MAX 15       /* verify rows per round: K + 1 <= 15 (glm_spec.rs, WALK-REUSE) */
 #define KDA_B_MAX 15       /* batched-decode sessions per step (same knee) */
-#define KDA_ABI_VERSION 7
+#define KDA_ABI_VERSION 8
 #define KDA_ACCEPT_WORK_BYTES 12288   /* workspace of kda_accept_greedy */
 #define KDA_NO_TOKEN 0xFFFFFFFFu      /* argmax slot of a logits row holding a NaN */
 #define KDA_CONV_RING_ROWS 3          /* short-conv history: kernel size 4 keeps 3 raw rows */
@@ -315,6 +315,29 @@ int kda_row_ops(const void* x, const void* a, const void* b, const float* conv_w
  */
 int kda_conv_reroll(const float* ring_snap, const void* raw, float* ring_out, int L,
                     int T_round, int keep, long long C, int in_dtype, void* stream);
+
+/*
+ * The rollback with the accepted-draft count left on the device: as
+ * kda_verify_round and kda_conv_reroll, with keep = min(*j, T - 1) + 1 read
+ * by the kernels themselves (T = T_prev, or T_round), where j is the u32 that
+ * kda_accept_greedy writes to out2[0].  The host then need not wait for j
+ * between the accept and the rollback: a whole verify round, accept and
+ * rollback included, can be enqueued (or captured in a HIP graph) before j
+ * is read back.  glm_spec.rs (0.123.0), glm5_spec_round step 4 and
+ * glm5_verify_rollback: the round commits keep = j + 1 rows.
+ *   j        : device pointer to one uint32, 4-byte aligned; it must not
+ *              overlap an output.  A j >= T (never produced by the accept) is
+ *              clamped to keep = T.
+ *   others   : as kda_verify_round (with 1 <= T_prev) and kda_conv_reroll;
+ *              the retained rows are validated for all T_prev (T_round) rows.
+ */
+int kda_verify_round_dev(const float* snap_prev, float* snap_out, const void* pk, const void* pv,
+                         const void* pg, const void* pbeta, const float* pe, int T_prev,
+                         const uint32_t* j, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, float* o, float* e, int L, int T,
+                         int H, int in_dtype, void* stream);
+int kda_conv_reroll_dev(const float* ring_snap, const void* raw, float* ring_out, int L,
+                        int T_round, const uint32_t* j, long long C, int in_dtype, void* stream);
 
 /*
  * Batched uniform copy: n buffers of `words` f32 each, in one launch.

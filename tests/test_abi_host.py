@@ -43,7 +43,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) >= {"kda_scan_rows", "kda_snapshot", "kda_replay", "kda_scan_batched",
                           "kda_verify_round", "kda_accept_greedy", "kda_conv_reroll",
                           "kda_copy_batch", "kda_row_ops", "kda_verify_round_multi",
-                          "kda_scan_rows_columns", "kda_last_error", "kda_abi_version"}
+                          "kda_scan_rows_columns", "kda_verify_round_dev", "kda_conv_reroll_dev",
+                          "kda_last_error", "kda_abi_version"}
     for n in names:
         assert hasattr(lib, n), f"libkda.so does not export {n}"
 
@@ -223,6 +224,63 @@ def test_scan_rows_columns_alignment_and_alias(lib, b):
     assert _columns(lib, b, e=off("s_out", cols_bytes - 16)) == ERR_ALIAS
     assert "s_cols overlaps e" in _msg(lib)
     assert _columns(lib, b, o=b["k"]) == ERR_ALIAS and "o overlaps k" in _msg(lib)
+
+
+def _round_dev(lib, b, **kw):
+    a = dict(snap_prev=b["snap"], snap_out=b["s_out"], pk=b["k"], pv=b["v"], pg=b["g"],
+             pbeta=b["beta"], pe=None, T_prev=8, j=b["ptrs"], q=b["q"], k=b["k"], v=b["v"],
+             g=b["g"], beta=b["beta"], o=b["o"], e=None, L=2, T=8, H=2, dt=0)
+    a.update(kw)
+    return lib.kda_verify_round_dev(a["snap_prev"], a["snap_out"], a["pk"], a["pv"], a["pg"],
+                                    a["pbeta"], a["pe"], a["T_prev"], a["j"], a["q"], a["k"],
+                                    a["v"], a["g"], a["beta"], a["o"], a["e"], a["L"], a["T"],
+                                    a["H"], a["dt"], None)
+
+
+def _reroll_dev(lib, b, **kw):
+    a = dict(ring=b["snap"], raw=b["q"], out=b["s_out"], L=2, T=8, j=b["ptrs"], C=384, dt=0)
+    a.update(kw)
+    return lib.kda_conv_reroll_dev(a["ring"], a["raw"], a["out"], a["L"], a["T"], a["j"], a["C"],
+                                   a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(j=None), ERR_ARG, "j is NULL"),
+    (dict(T_prev=0), ERR_RANGE, "T_prev=0"),
+    (dict(T_prev=16), ERR_RANGE, "T_prev=16"),
+    (dict(snap_out=None), ERR_ARG, "snap_out is NULL"),
+    (dict(T=0), ERR_RANGE, "T=0"),
+    (dict(pk=None), ERR_ARG, "pk is NULL"),
+])
+def test_verify_round_dev_refusals(lib, b, kw, code, needle):
+    assert _round_dev(lib, b, **kw) == code
+    assert needle in _msg(lib)
+
+
+def test_verify_round_dev_alignment_and_alias(lib, b):
+    off = lambda n, k: ctypes.c_void_p(b.addr[n] + k)
+    assert _round_dev(lib, b, j=off("ptrs", 2)) == ERR_ALIGN and "j is not 4-byte" in _msg(lib)
+    # j is read by every workgroup: no output may cover it
+    assert _round_dev(lib, b, j=off("o", 64)) == ERR_ALIAS and "o overlaps j" in _msg(lib)
+    assert _round_dev(lib, b, j=off("s_out", 4)) == ERR_ALIAS and "snap_out overlaps j" in _msg(lib)
+    assert _round_dev(lib, b, e=b["ptrs"]) == ERR_ALIAS and "e overlaps j" in _msg(lib)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(j=None), ERR_ARG, "j is NULL"),
+    (dict(T=0), ERR_RANGE, "T_round=0"),
+    (dict(C=0), ERR_RANGE, "C=0"),
+    (dict(out=None), ERR_ARG, "ring_out is NULL"),
+])
+def test_conv_reroll_dev_refusals(lib, b, kw, code, needle):
+    assert _reroll_dev(lib, b, **kw) == code
+    assert needle in _msg(lib)
+
+
+def test_conv_reroll_dev_alignment_and_alias(lib, b):
+    off = lambda n, k: ctypes.c_void_p(b.addr[n] + k)
+    assert _reroll_dev(lib, b, j=off("ptrs", 1)) == ERR_ALIGN
+    assert _reroll_dev(lib, b, j=off("s_out", 8)) == ERR_ALIAS and "ring_out overlaps j" in _msg(lib)
 
 
 def test_replay_alias(lib, b):
