@@ -725,6 +725,40 @@ def main() -> int:
 
         l_us, l_wall, keeps = time_loop(False)
         d_us, d_wall, _ = time_loop(True)
+
+        # with j on the device a round has no host decision left: capture the 4
+        # round shapes (input set i mod 4, buffer parity i mod 2) as HIP graphs
+        # once, then replay them round after round
+        g_us = None
+        try:
+            lp["keep"] = out2s[1]    # every captured round replays the previous round
+            graphs = []
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                for i in range(4):
+                    loop_round(4 + i, True)
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            for i in range(4):
+                lp["keep"] = out2s[(4 + i - 1) % 2]
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    loop_round(4 + i, True)
+                graphs.append(gr)
+            for i in range(4):
+                graphs[i].replay()
+            torch.cuda.synchronize()
+            a, b = ev(), ev()
+            a.record(stream)
+            for i in range(args.loop_rounds):
+                graphs[i % 4].replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            g_us = a.elapsed_time(b) * 1e3 / args.loop_rounds
+            del graphs
+        except RuntimeError as exc:   # capture unsupported: report, do not fall back
+            g_us = f"not captured: {exc}"
         verify_loop = {
             "rounds": args.loop_rounds, "us_per_round": l_us,
             "wall_us_per_round": l_wall,
@@ -736,6 +770,7 @@ def main() -> int:
                             "note": "the same loop with j left on the device "
                                     "(kda_verify_round_dev, kda_conv_reroll_dev): no "
                                     "readback between the accept and the rollback"},
+            "device_keep_graph_us_per_round": g_us,
             "note": "kda_row_ops + kda_verify_round + kda_accept_greedy (t=15, V=150,000) "
                     "+ j read back + kda_conv_reroll, per round, one session",
         }

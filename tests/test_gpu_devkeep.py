@@ -131,3 +131,92 @@ def test_loop_without_readback_equals_loop_with_it():
         for name, x, y in zip(("o", "snapshot", "ring", "accept"), a, b):
             assert same(x, y), f"round {r}: {name}"
     assert [int(h[3][0]) for h in host] == js_planted
+
+
+def test_captured_loop_replays_equal_the_eager_loop():
+    """The device-keep loop, captured as HIP graphs (one per buffer parity), replayed
+    round after round with eager work and synchronizations between the replays:
+    every replay's outputs equal the eager loop's round for round."""
+    L, H, T, V, rounds = 2, 4, 8, 1000, 6
+    js_planted = [3, 7, 0, 5, 2, 6]
+    base = synth.row_op_inputs(96, 0, L, T, H)
+    w = dev(base["w"])
+    proj = [synth.row_op_inputs(97, r, L, T, H) for r in range(2)]
+    xs = [dev(p_["x"]) for p_ in proj]
+    as_ = [dev(p_["a"]) for p_ in proj]
+    bs = [dev(p_["b"]) for p_ in proj]
+    acc = [synth.accept_round(98, r, T, V, js_planted[r]) for r in range(rounds)]
+    logits = [dev(a[0]) for a in acc]
+    drafts = [dev(a[1].view(np.int32)) for a in acc]
+    lg_buf = torch.empty_like(logits[0])
+    dr_buf = torch.empty_like(drafts[0])
+    work = kda.accept_workspace()
+    sets = [[torch.empty(L, T, H, D, device="cuda") for _ in range(4)]
+            + [torch.empty(L, T, H, device="cuda"), torch.empty(L, T, H, D, device="cuda")]
+            for _ in range(2)]
+    st = [torch.zeros(L, H, D, D, device="cuda") for _ in range(2)]
+    rings = [dev(base["ring"]), torch.empty(L, 3, 3 * H * D, device="cuda")]
+    o = torch.empty(L, T, H, D, device="cuda")
+    vam = torch.empty(T, dtype=torch.int32, device="cuda")
+    out2 = [torch.zeros(2, dtype=torch.int32, device="cuda") for _ in range(2)]
+
+    def round_(i, first=False):
+        cur, prv = sets[i % 2], sets[(i + 1) % 2]
+        x = xs[i % 2]
+        kda.kda_row_ops(x, as_[i % 2], bs[i % 2], w, rings[i % 2], *cur[:5])
+        if first:
+            kda.kda_verify_round(st[i % 2], st[(i + 1) % 2], None, 0, *cur[:5], o, e=cur[5])
+        else:
+            kda.kda_verify_round(st[i % 2], st[(i + 1) % 2], (prv[1], None, prv[3], None, prv[5]),
+                                 out2[(i + 1) % 2], *cur[:5], o, e=cur[5])
+        kda.kda_accept_greedy(lg_buf, dr_buf, vam, out2[i % 2], work)
+        kda.kda_conv_reroll(rings[i % 2], x, out2[i % 2], rings[(i + 1) % 2])
+
+    def snap_out(i):
+        return [t.clone() for t in (o, st[(i + 1) % 2], rings[(i + 1) % 2], out2[i % 2])]
+
+    def reset():
+        st[0].zero_()
+        rings[0].copy_(dev(base["ring"]))
+        torch.cuda.synchronize()
+
+    # eager reference
+    reset()
+    ref = []
+    for i in range(rounds):
+        lg_buf.copy_(logits[i]); dr_buf.copy_(drafts[i])
+        round_(i, first=(i == 0))
+        ref.append(snap_out(i))
+    torch.cuda.synchronize()
+
+    # round 0 eagerly, then capture one graph per parity
+    reset()
+    lg_buf.copy_(logits[0]); dr_buf.copy_(drafts[0])
+    round_(0, first=True)
+    torch.cuda.synchronize()
+    got = [snap_out(0)]
+    saved = [t.clone() for t in (st[1], rings[1], out2[0])]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):          # warm the capture path
+        round_(1)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for par in (1, 0):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            round_(par)
+        graphs.append(g)
+    # undo what the warm-up and the captures touched: restore the state after round 0
+    st[1].copy_(saved[0]); rings[1].copy_(saved[1]); out2[0].copy_(saved[2])
+    torch.cuda.synchronize()
+    for i in range(1, rounds):
+        lg_buf.copy_(logits[i]); dr_buf.copy_(drafts[i])   # eager work between replays
+        graphs[0 if i % 2 == 1 else 1].replay()
+        torch.cuda.synchronize()
+        got.append(snap_out(i))
+    for i, (a, b) in enumerate(zip(ref, got)):
+        for name, x, y in zip(("o", "snapshot", "ring", "accept"), a, b):
+            assert same(x, y), f"round {i}: {name}"
+    assert [int(r[3][0]) for r in ref] == js_planted
