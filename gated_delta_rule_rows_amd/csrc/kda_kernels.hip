@@ -50,6 +50,13 @@
 // sequential dependency from row to row -- there is no dense contraction to
 // feed the matrix cores.
 //
+// Memory.  State words stream past the caches (nontemporal loads and stores):
+// each is read once and written once per launch.  Every row input of a phase
+// and the state are in flight before the first wait; the fused round also
+// issues this round's row loads before its replay.  The batched arm walks its
+// table entries in a spread order, so that the workgroups in flight touch
+// sessions far apart in memory.
+//
 // Beside the scan, all HBM- or latency-bound: the pre-scan row ops (short
 // conv, norms, gate, beta) that produce the scan's inputs; the conv-ring
 // rollback; a plain copy (snapshots) and a pointer-table batched copy; and the
@@ -139,17 +146,6 @@ __device__ __forceinline__ float reduce_scatter4(const float (&x)[4]) {
     swap32(lo, hi); // row k: column k over rows k and k^2
     const float r = lo + hi;
     return r + dpp<0x128>(r);   // row_ror:8 pairs lane bit 3
-}
-
-// Column k's value from row k, for k = 0..3, into every lane (the inverse
-// movement of reduce_scatter4).
-__device__ __forceinline__ void all_gather4(float x, float (&y)[4]) {
-    float a = x, b = x;
-    swap32(a, b);   // a: column (row & 1); b: column (row & 1) + 2
-    float a1 = a, b1 = b;
-    swap16(a, a1);  // a: column 0; a1: column 1
-    swap16(b, b1);  // b: column 2; b1: column 3
-    y[0] = a; y[1] = a1; y[2] = b; y[3] = b1;
 }
 
 // ------------------------------------------------------------------ input loads
@@ -288,8 +284,7 @@ struct Stage {
     float4 k[TM * KeyRow<R>::kStride / 4];   // k, key layout
     float4 q[TM * KeyRow<R>::kStride / 4];   // q / sqrt(128), key layout (kFull)
     float4 ve[TM * kD / 4];                  // beta * v, or e for kStash; [t][j]
-    float b[TM];                             // beta
-    float qk[TM];                            // (q / sqrt(128)) . k
+    float2 bq[TM];                           // beta, (q / sqrt(128)) . k: one LDS read
 };
 
 // One phase's row inputs, located for one chain.
@@ -379,7 +374,7 @@ __device__ __forceinline__ void stage_commit(Stage<R, TMAX>& L, const Staged<R, 
                 const float bt = in.b[p];
                 const float4 gv = in.v[p];
                 L.ve[t * 32 + c4] = make_float4(bt * gv.x, bt * gv.y, bt * gv.z, bt * gv.w);
-                if (c4 == 0) L.b[t] = bt;
+                if (c4 == 0) L.bq[t].x = bt;
             }
             if constexpr (has_q(M)) {
                 const float4 gq = in.q[p];
@@ -403,7 +398,7 @@ __device__ __forceinline__ void stage_commit(Stage<R, TMAX>& L, const Staged<R, 
                 p = fmaf(sq[kp], sk[kp], p);
             }
             p = group_sum<16>(p);
-            if (l16 == 0) L.qk[t] = p;
+            if (l16 == 0) L.bq[t].y = p;
         }
         __syncthreads();
     }
@@ -423,7 +418,8 @@ __device__ __forceinline__ void stage(Stage<R, TMAX>& L, const Src& src, int tid
 // kFullCols: `cols` addresses this chain's state in column 0, and row t's
 // state goes to cols + t * col_stride.
 // SW: the swap layout (above); the lane's 4 columns are reduced with
-// reduce_scatter4 and e is shared back with all_gather4.
+// reduce_scatter4, and e comes back to the lanes of its column group through
+// a wave-private LDS slot per column.
 template <int R, int C, Rows M, bool SW, int TM>
 __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C], int T,
                                          float* o, float* e_out, size_t o0, size_t ostride,
@@ -435,6 +431,28 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
 #pragma unroll 1
     for (int t = 0; t < T; ++t) {
         const int kb = t * KR::kStride + KR::at(i0);
+        if constexpr (M == Rows::kStash) {
+            // e is known up front, so each key's decay and update run
+            // together, four keys at a time: few live registers, which lets
+            // the fused round hold the next phase's row loads meanwhile
+            float e[C];
+            load_cols<C>(sve + t * kD + j0, e);
+#pragma unroll
+            for (int r4 = 0; r4 < R / 4; ++r4) {
+                const float4 x = L.k[kb / 4 + r4];
+                const float4 y = L.d[kb / 4 + r4];
+                const float k4[4] = {x.x, x.y, x.z, x.w};
+                const float d4[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+#pragma unroll
+                    for (int c = 0; c < C; ++c)
+                        s[4 * r4 + m][c] = fmaf(k4[m], e[c], s[4 * r4 + m][c] * d4[m]);
+                }
+                asm volatile("" ::: "memory");   // the next four keys' LDS reads wait here
+            }
+            continue;
+        }
         float kk[R], dk[R], qq[R];
 #pragma unroll
         for (int r4 = 0; r4 < R / 4; ++r4) {
@@ -447,76 +465,81 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
                 qq[4 * r4 + 0] = z.x; qq[4 * r4 + 1] = z.y; qq[4 * r4 + 2] = z.z; qq[4 * r4 + 3] = z.w;
             }
         }
-        float ve[C];   // beta * v, or e itself for kStash
-        load_cols<C>(sve + t * kD + j0, ve);
-
+        const float2 bq = L.bq[t];
+        const float nbt = -bq.x;
+        // decay, then the in-lane partial reductions over this lane's keys
+        float u[C], w[C];
+#pragma unroll
+        for (int c = 0; c < C; ++c) { u[c] = 0.0f; w[c] = 0.0f; }
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                s[r][c] = s[r][c] * dk[r];
+                u[c] = fmaf(kk[r], s[r][c], u[c]);
+                if constexpr (has_q(M)) w[c] = fmaf(qq[r], s[r][c], w[c]);
+            }
+        }
         float e[C];
-        if constexpr (M == Rows::kStash) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-#pragma unroll
-                for (int c = 0; c < C; ++c) s[r][c] = s[r][c] * dk[r];
+        if constexpr (SW) {
+            static_assert(C == 4 && TL::NI == 8, "the swap layout is the whole-head tiling");
+            const int lane = threadIdx.x & 63;
+            const int kc = (lane >> 4) & 3;   // the column this lane reduces
+            const uint32_t col = static_cast<uint32_t>(j0 + kc);
+            // the last DPP adds of both reductions stay out of the writer's
+            // branch (sunk there, each becomes a DPP move and an add)
+            float uo = reduce_scatter4(u);
+            asm volatile("" : "+v"(uo));
+            const float eo = fmaf(nbt, uo, sve[t * kD + col]);
+            float ov = 0.0f;
+            if constexpr (has_q(M)) {
+                float wo = reduce_scatter4(w);
+                asm volatile("" : "+v"(wo));
+                ov = fmaf(eo, bq.y, wo);
             }
-#pragma unroll
-            for (int c = 0; c < C; ++c) e[c] = ve[c];
+            // each column's sum sits in two lanes (lane bit 3); the lane with
+            // bit 3 = 0 writes o and e, at a row base held in SGPRs plus its
+            // column, and leaves e in its column's LDS slot
+            __shared__ float ex[TL::WAVES * TL::WCOLS];
+            float* slot = ex + (threadIdx.x >> 6) * TL::WCOLS + (lane & 7) * C;
+            const size_t row = o0 + t * ostride;
+            if ((lane & 8) == 0) {
+                if constexpr (has_q(M)) {
+                    gfloat* orow = (gfloat*)(o + row);
+                    asm volatile("" : "+s"(orow));
+                    orow[col] = ov;
+                }
+                if (e_out != nullptr) {
+                    gfloat* erow = (gfloat*)(e_out + row);
+                    asm volatile("" : "+s"(erow));
+                    erow[col] = eo;
+                }
+                slot[kc] = eo;
+            }
+            __builtin_amdgcn_wave_barrier();   // one wave writes and reads the slots, in order
+            load_cols<C>(slot, e);
         } else {
-            const float nbt = -L.b[t];
-            // decay, then the in-lane partial reductions over this lane's keys
-            float u[C], w[C];
+            float ve[C];   // beta * v
+            load_cols<C>(sve + t * kD + j0, ve);
 #pragma unroll
-            for (int c = 0; c < C; ++c) { u[c] = 0.0f; w[c] = 0.0f; }
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-#pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    s[r][c] = s[r][c] * dk[r];
-                    u[c] = fmaf(kk[r], s[r][c], u[c]);
-                    if constexpr (has_q(M)) w[c] = fmaf(qq[r], s[r][c], w[c]);
-                }
+            for (int c = 0; c < C; ++c) {
+                u[c] = group_sum<TL::NI>(u[c]);
+                if constexpr (has_q(M)) w[c] = group_sum<TL::NI>(w[c]);
             }
-            if constexpr (SW) {
-                static_assert(C == 4 && TL::NI == 8, "the swap layout is the whole-head tiling");
-                const int lane = threadIdx.x & 63;
-                const int kc = (lane >> 4) & 3;   // the column this lane reduces
-                const uint32_t col = static_cast<uint32_t>(j0 + kc);
-                const float uo = reduce_scatter4(u);
-                const float eo = fmaf(nbt, uo, sve[t * kD + col]);
-                // each column's sum sits in two lanes (lane bit 3); bit 3 = 0
-                // writes, at a wave-uniform row base plus this lane's column
-                const bool writer = (lane & 8) == 0;
-                const size_t row = o0 + t * ostride;
-                if constexpr (has_q(M)) {
-                    float wo = reduce_scatter4(w);
-                    // keep the last DPP add out of the writer's branch (sunk
-                    // there it becomes a DPP move and an add)
-                    asm volatile("" : "+v"(wo));
-                    const float ov = fmaf(eo, L.qk[t], wo);
-                    if (writer) ((gfloat*)(o + row))[col] = ov;
-                }
-                if (e_out != nullptr && writer) ((gfloat*)(e_out + row))[col] = eo;
-                all_gather4(eo, e);
-            } else {
+            // e = beta v - beta u
 #pragma unroll
-                for (int c = 0; c < C; ++c) {
-                    u[c] = group_sum<TL::NI>(u[c]);
-                    if constexpr (has_q(M)) w[c] = group_sum<TL::NI>(w[c]);
-                }
-                // e = beta v - beta u
+            for (int c = 0; c < C; ++c) e[c] = fmaf(nbt, u[c], ve[c]);
+            if constexpr (has_q(M)) {
+                // finish w's butterfly on every lane: sunk into the writer's
+                // branch, its last DPP step would become mov 0, mov_dpp, add
 #pragma unroll
-                for (int c = 0; c < C; ++c) e[c] = fmaf(nbt, u[c], ve[c]);
-                if constexpr (has_q(M)) {
-                    // finish w's butterfly on every lane: sunk into the writer's
-                    // branch, its last DPP step would become mov 0, mov_dpp, add
+                for (int c = 0; c < C; ++c) asm volatile("" : "+v"(w[c]));
+                float ov[C];
 #pragma unroll
-                    for (int c = 0; c < C; ++c) asm volatile("" : "+v"(w[c]));
-                    const float qk = L.qk[t];
-                    float ov[C];
-#pragma unroll
-                    for (int c = 0; c < C; ++c) ov[c] = fmaf(e[c], qk, w[c]);
-                    if (ig == 0) store_cols<C>(o + (o0 + t * ostride) + j0, ov);
-                }
-                if (e_out != nullptr && ig == 0) store_cols<C>(e_out + (o0 + t * ostride) + j0, e);
+                for (int c = 0; c < C; ++c) ov[c] = fmaf(e[c], bq.y, w[c]);
+                if (ig == 0) store_cols<C>(o + (o0 + t * ostride) + j0, ov);
             }
+            if (e_out != nullptr && ig == 0) store_cols<C>(e_out + (o0 + t * ostride) + j0, e);
         }
         // delta-rule write: S = S' + k e^T
 #pragma unroll
@@ -652,7 +675,32 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         run_rows<R, C, MB, SW>(LB, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0);
         return;
     } else if constexpr (FUSED) {
-        if (a.n_prev > 0) {
+        // With at most one stash replay, this launch's row loads go out
+        // before the replay (the stash replay leaves registers for them) and
+        // are waited on before the snapshot's stores are issued: a wait after
+        // those stores would wait for them to complete as well.
+        constexpr bool kEarlyRows = MA == Rows::kStash;
+        if (a.n_prev == 0 || (kEarlyRows && a.n_prev == 1)) {
+            Staged<R, C, MB, kTMax> inB;
+            if (kEarlyRows && a.n_prev == 1) {
+                const Src p0 = prev_src(0);
+                Staged<R, C, MA, kTMax> inA;
+                stage_issue<R, C, BF16, MA, kTMax>(inA, p0, tid);
+                load_state();
+                stage_fence<R, C, MA, kTMax>(inA);
+                stage_commit<R, C, MA, kTMax>(L, inA, p0.T, tid);
+                stage_issue<R, C, BF16, MB, kTMax>(inB, b, tid);
+                asm volatile("" ::: "memory");   // keep those loads ahead of the replay
+                run_rows<R, C, MA, SW>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+            } else {
+                stage_issue<R, C, BF16, MB, kTMax>(inB, b, tid);
+                load_state();
+            }
+            stage_fence<R, C, MB, kTMax>(inB);
+            if (a.s_out) store_state();   // the committed state: this round's snapshot
+            __syncthreads();   // every wave is done with the replayed rows
+            stage_commit<R, C, MB, kTMax>(L, inB, b.T, tid);
+        } else {
             const Src p0 = prev_src(0);
             stage<R, C, BF16, MA>(L, p0, tid, load_state);
             run_rows<R, C, MA, SW>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
@@ -663,11 +711,9 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
                 run_rows<R, C, MA, SW>(L, s, pi.T, nullptr, nullptr, 0, 0, ig, i0, j0);
                 __syncthreads();
             }
-        } else {
-            load_state();
+            if (a.s_out) store_state();   // the committed state: this round's snapshot
+            stage<R, C, BF16, MB>(L, b, tid, [] {});
         }
-        if (a.s_out) store_state();   // the committed state: this round's snapshot
-        stage<R, C, BF16, MB>(L, b, tid, [] {});
     } else {
         // the batched arm always scans one row per session
         stage<R, C, BF16, MB, TABLE ? 1 : kTMax>(L, b, tid, load_state);
