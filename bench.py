@@ -146,7 +146,51 @@ def cpu_baseline(host_rounds, js, T, seconds: float):
         "sample": f"{n} verify_k14 round(s) (inputs of rounds 0..{len(host_rounds) - 1} "
                   f"cycled): all {L}x{H} chains, T={T} scan + accept-j replay, f64 oracle on "
                   f"{threads} host threads, {el:.1f} s",
+        "single_core": cpu_single_core(host_rounds, js, T, max(1.0, seconds / 5)),
+        "host": host_cpu(),
     }
+
+
+def cpu_single_core(host_rounds, js, T, seconds: float):
+    """The oracle on one thread, over heads {0, 21, 42, 63} of every layer (the
+    same rounds, scan + replay), until `seconds` pass; per chain-row, so the rate
+    compares with the all-threads figure."""
+    import numpy as np
+    import oracle
+
+    L, _, H, _ = host_rounds[0]["q"].shape
+    heads = sorted({0, H // 3, (2 * H) // 3, H - 1})
+    s = np.zeros((L, len(heads), D, D), np.float32)
+    rows = 0
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        r = host_rounds[n % len(host_rounds)]
+        args = [np.ascontiguousarray(r[k][:, :, heads]) for k in ("q", "k", "v", "g", "beta")]
+        s_full, _ = oracle.scan_rows(s, *args, threads=1)
+        keep = int(js[n % len(js)]) + 1
+        s = oracle.replay(s, *args, keep=keep, threads=1) if keep < T else s_full
+        rows += T * len(heads) * L
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": rows / el, "unit": "rows*heads/s", "threads": 1,
+            "sample": f"{n} round(s), heads {heads} x {L} layers, T={T} scan + replay, {el:.1f} s"}
+
+
+def host_cpu():
+    """The host's logical CPU count and model name (from /proc/cpuinfo)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"logical_cpus": os.cpu_count(), "model": model}
 
 
 def main() -> int:
