@@ -857,8 +857,7 @@ def main() -> int:
         "round_us": stats_us(f_us),
         "round_us_note": "round_us: the K rounds after the timed ones, each launch between "
                          "its own events (the event pairs add a few us per round)",
-        "round_us_mall_cold": ({"mean": float(np.mean(cold_us)), "p50": pctl(cold_us, 50)}
-                               if cold_us else None),
+        "round_us_mall_cold": stats_us(cold_us) if cold_us else None,
         "committed_rows_heads_per_s": sum(int(js[(args.warmup + s) % w.rounds]) + 1
                                           for s in range(args.steps)) * H * L / (f_ms * 1e-3),
         "split": split,

@@ -296,9 +296,6 @@ struct Src {
     int T;
 };
 
-// Load one phase's rows, run `between` (the state loads, when this is the
-// first phase), then stage everything in LDS.  All loads are in flight before
-// the first wait.  Ends with the staged rows visible to every wave.
 // One phase's row inputs in flight: float4 loads per lane per input, enough
 // for TMAX rows of 32 float4.
 template <int R, int C, Rows M, int TMAX>
@@ -405,7 +402,8 @@ __device__ __forceinline__ void stage_commit(Stage<R, TMAX>& L, const Staged<R, 
 }
 
 // A phase's rows from HBM into LDS; `between` runs after the row loads are
-// issued and before anything waits on them (the state loads go there).
+// issued and before anything waits on them (the state loads go there, when
+// this is the first phase).  Ends with the staged rows visible to every wave.
 template <int R, int C, bool BF16, Rows M, int TMAX = kTMax, typename F>
 __device__ __forceinline__ void stage(Stage<R, TMAX>& L, const Src& src, int tid, F&& between) {
     Staged<R, C, M, TMAX> in;
