@@ -431,8 +431,10 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
         const int kb = t * KR::kStride + KR::at(i0);
         if constexpr (M == Rows::kStash) {
             // e is known up front, so each key's decay and update run
-            // together, four keys at a time: few live registers, which lets
-            // the fused round hold the next phase's row loads meanwhile
+            // together.  Whole-head lanes take four keys at a time: few live
+            // registers, which lets the fused round hold the next phase's row
+            // loads meanwhile.  Narrower lanes have registers to spare and
+            // issue all their LDS reads at once (one wait per row).
             float e[C];
             load_cols<C>(sve + t * kD + j0, e);
 #pragma unroll
@@ -447,7 +449,7 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
                     for (int c = 0; c < C; ++c)
                         s[4 * r4 + m][c] = fmaf(k4[m], e[c], s[4 * r4 + m][c] * d4[m]);
                 }
-                asm volatile("" ::: "memory");   // the next four keys' LDS reads wait here
+                if constexpr (C == 4) asm volatile("" ::: "memory");   // next four keys' reads wait here
             }
             continue;
         }
