@@ -489,6 +489,21 @@ def test_long_chain_drift_verify_k14_all_rounds():
     assert last <= 4 * first + 1e-7, f"state error grows along the chain: {first} -> {last}"
 
 
+def test_very_long_chain_small_shape_drift():
+    # 300 fused rounds of 15 rows on 2 layers x 4 heads (4,500 rows per chain),
+    # every chain against the oracle each round: the error stays at rounding
+    # level and does not grow with the chain
+    w = synth.Workload("long_small", L=2, H=4, T=15, rounds=300, seed=5)
+    log = []
+    _fused_pipeline(w, w.rounds, list(range(w.H)), log=log)
+    worst = max(x[1] for x in log)
+    print(f"\n300 rounds: worst max|d| state {worst:.3e}, worst max ulp state "
+          f"{max(x[2] for x in log):.1f}, worst max|d| o {max(x[3] for x in log):.3e}")
+    first = max(x[1] for x in log[:50])
+    last = max(x[1] for x in log[-50:])
+    assert last <= 4 * first + 1e-7, f"state error grows along the chain: {first} -> {last}"
+
+
 def test_fused_pipeline_serving_mix_bf16_sampled_vs_oracle():
     w = synth.WORKLOADS["serving_mix_bf16"]
     Ks = synth.serving_ks(w.seed, 3)
