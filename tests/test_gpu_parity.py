@@ -224,6 +224,35 @@ def test_gpu_identity_and_clamp_and_one_hot():
     assert not np.delete(sz[0, 0], m, axis=0).any()
 
 
+def test_gpu_keeps_f32_denormals_like_the_oracle():
+    # beta = 0, g = -5 on every row: each row multiplies the state by the one
+    # decay factor d.  Reading d back after one row, 19 rows from S = 1 must
+    # equal 19 IEEE f32 multiplies by d (numpy keeps denormals): the state
+    # falls to about 5e-42, below the smallest normal f32, and is not flushed
+    L, H = 1, 1
+    rng = np.random.default_rng(7)
+    def rows(T):
+        q = rng.standard_normal((L, T, H, D)).astype(np.float32)
+        k = rng.standard_normal((L, T, H, D)).astype(np.float32)
+        v = rng.standard_normal((L, T, H, D)).astype(np.float32)
+        g = np.full((L, T, H, D), -5.0, np.float32)
+        b = np.zeros((L, T, H), np.float32)
+        return [dev(x) for x in (q, k, v, g, b)]
+    one = torch.ones(L, H, D, D, device="cuda")
+    s1, _ = scan(one, rows(1))
+    d = host(s1)[0, 0, 0, 0]
+    assert np.all(host(s1) == d) and 0 < d < 1
+    s = one
+    for T in (15, 4):
+        s, _ = scan(s, rows(T))
+    ref = np.float32(1.0)
+    for _ in range(19):
+        ref = np.float32(ref * d)
+    assert 0 < ref < np.finfo(np.float32).tiny
+    got = host(s)
+    assert np.all(got.view(np.int32) == np.float32(ref).view(np.int32)), (got.max(), ref)
+
+
 def test_snapshot_is_a_bit_copy():
     s = dev(rand_state(6, 3, 5))
     snap = torch.full_like(s, float("nan"))
