@@ -71,6 +71,24 @@ def test_row_ops_match_oracle_bf16(L, T, H):
     _close(got, _ref(inp, H, bf16=True))
 
 
+@pytest.mark.parametrize("L,T,H", [(1, 8, 64), (34, 15, 64)])
+def test_row_ops_small_rows_where_the_norm_epsilon_dominates(L, T, H):
+    # raw projections and ring scaled by 1e-4: the conv outputs are ~3e-5, so
+    # sum y^2 over a head (~1e-7) sits well below the norm's 1e-6 and q, k are
+    # y / sqrt(sum y^2 + 1e-6), far from unit rows.  A kernel whose epsilon
+    # differed from the oracle's (1e-7, 1e-8, 0) would miss the 1e-5 gate by
+    # orders of magnitude.
+    inp = synth.row_op_inputs(8, L * 100 + T, L, T, H)
+    inp["x"] *= np.float32(1e-4)
+    inp["ring"] *= np.float32(1e-4)
+    ref = _ref(inp, H)
+    for n in ("q", "k"):
+        sq = (ref[n].astype(np.float64) ** 2).sum(-1)   # = sum y^2 / (sum y^2 + eps)
+        assert sq.max() < 0.5, f"{n}: epsilon does not dominate this input"
+    got, _ = _run(inp, L, T, H)
+    _close(got, ref)
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 7])
 def test_row_ops_ring_is_the_full_accept_reroll(T):
     # the ring after all T rows (written by the last row's workgroup, from ring

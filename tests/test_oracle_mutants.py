@@ -50,6 +50,9 @@ MUTANTS = [
     ("conv ring not rolled", "for (long c = 0; c < C; ++c) ring[m * C + c] = ring[(m + 1) * C + c];",
      ""),
     ("norm without epsilon", "1.0 / sqrt(sq + ORACLE_NORM_EPS)", "1.0 / sqrt(sq)"),
+    ("norm epsilon 1e-8", "#define ORACLE_NORM_EPS 1e-6", "#define ORACLE_NORM_EPS 1e-8"),
+    ("norm epsilon 1e-7", "#define ORACLE_NORM_EPS 1e-6", "#define ORACLE_NORM_EPS 1e-7"),
+    ("norm epsilon 1e-5", "#define ORACLE_NORM_EPS 1e-6", "#define ORACLE_NORM_EPS 1e-5"),
     ("q and k blocks swapped", "q[o + j] = (float)(y[h * d + j] * nq);",
      "q[o + j] = (float)(y[HD + h * d + j] * nq);"),
     ("gate bound missing", "if (gg < ORACLE_GATE_LO) gg = ORACLE_GATE_LO;", ""),
@@ -77,6 +80,7 @@ PIN_TESTS = [
     lambda: pins.test_row_ops_identity_taps_give_silu_closed_forms(),
     lambda: pins.test_row_ops_taps_reach_back_through_the_ring(),
     lambda: pins.test_row_ops_norms_gate_and_beta_closed_forms(),
+    lambda: pins.test_row_ops_norm_epsilon_dominates_small_rows(),
     lambda: pins.test_row_ops_split_rounds_chain_through_the_ring(),
     lambda: pins.test_row_ops_channels_heads_and_layers_stay_apart(),
 ]

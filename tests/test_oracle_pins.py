@@ -521,6 +521,37 @@ def test_row_ops_norms_gate_and_beta_closed_forms():
         np.testing.assert_allclose(np.linalg.norm(o2[n], axis=-1), 1.0, rtol=1e-5)
 
 
+def test_row_ops_norm_epsilon_dominates_small_rows():
+    # reading r15 fixes the norm as y / sqrt(sum y^2 + 1e-6).  With one nonzero
+    # channel per head, q = y / sqrt(y^2 + eps): at y^2 = eps the row comes out
+    # at 1/sqrt(2), not 1, and the three heads below tell eps = 1e-6 apart
+    # from 1e-7, 1e-8 or 0 by far more than any rounding.
+    L, T, H, d = 1, 1, 3, 4
+    x, a, b, w, ring = _ops_inputs(L, T, H, d, taps=(0, 0, 0, 2))
+    HD = H * d
+    x[0, 0, :2 * HD] = 0.0
+    # conv output = SiLU(2 x); pick x so that y^2 is 1e-4, 1e-6, 1e-8 (to a
+    # few parts in 1e3: SiLU(z) = z / (1 + e^-z) ~ z / 2 for small z)
+    ys = np.array([1e-2, 1e-3, 1e-4])
+    for h, y in enumerate(ys):
+        x[0, 0, h * d] = y             # q block, head h, channel 0
+        x[0, 0, HD + h * d + 1] = y    # k block, head h, channel 1
+    out = oracle.row_ops(x, a, b, w, ring, H, d)
+    z = 2.0 * x[0, 0, :HD].astype(np.float64)
+    y = z / (1.0 + np.exp(-z))          # SiLU of the conv output, f64
+    for h in range(H):
+        yq = y[h * d]
+        want = yq / np.sqrt(yq * yq + 1e-6)
+        np.testing.assert_allclose(out["q"][0, 0, h, 0], want, rtol=1e-6)
+        np.testing.assert_allclose(out["k"][0, 0, h, 1], want, rtol=1e-6)
+        assert np.all(out["q"][0, 0, h, 1:] == 0) and out["k"][0, 0, h, 0] == 0
+    # y^2 = eps (head 1, to 0.2%): the unit row shrinks to about 1/sqrt(2)
+    assert abs(out["q"][0, 0, 1, 0] - 2 ** -0.5) < 2e-3
+    # y^2 = 1e-2 eps: about 0.1, and y^2 = 100 eps: within 0.5% of 1
+    assert abs(out["q"][0, 0, 2, 0] - 0.1) < 1e-3
+    assert abs(out["q"][0, 0, 0, 0] - 1.0) < 6e-3
+
+
 def test_row_ops_split_rounds_chain_through_the_ring():
     # causality: rows 0..2 then rows 3..5 (ring carried) equal rows 0..5;
     # the ring after the round is the conv-ring roll of all T rows
