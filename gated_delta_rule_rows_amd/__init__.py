@@ -73,10 +73,12 @@ def load():
             f"{_LIB_PATH} is not built; run `python -m gated_delta_rule_rows_amd.build`")
     lib = ctypes.CDLL(_LIB_PATH)
     p, i = ctypes.c_void_p, ctypes.c_int
-    lib.kda_scan_rows.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, p]
+    lib.kda_scan_rows.argtypes = [p, p, p, p, p, p, p, p, i, i, i, i, p]
+    lib.kda_scan_rows_stash.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, p]
     lib.kda_scan_rows_columns.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, p]
     lib.kda_snapshot.argtypes = [p, p, i, i, p]
     lib.kda_replay.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, p]
+    lib.kda_replay_stash.argtypes = [p, p, p, p, p, i, i, i, i, i, p]
     lib.kda_scan_batched.argtypes = [p, p, p, p, p, p, p, i, i, i, i, p]
     lib.kda_verify_round.argtypes = [p, p, p, p, p, p, p, i, i, p, p, p, p, p, p, p,
                                      i, i, i, i, p]
@@ -93,7 +95,7 @@ def load():
                lib.kda_verify_round, lib.kda_accept_greedy, lib.kda_conv_reroll,
                lib.kda_copy_batch, lib.kda_row_ops, lib.kda_verify_round_multi,
                lib.kda_scan_rows_columns, lib.kda_verify_round_dev, lib.kda_conv_reroll_dev,
-               lib.kda_abi_version):
+               lib.kda_scan_rows_stash, lib.kda_replay_stash, lib.kda_abi_version):
         fn.restype = i
     lib.kda_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -166,22 +168,39 @@ def _plane(t, shape, name):
         _f32(t, name)
 
 
-def kda_scan_rows(s_in, s_out, q, k, v, g, beta, o=None, e=None, stream=None) -> None:
+def kda_scan_rows(s_in, s_out, q, k, v, g, beta, o=None, stream=None) -> None:
     """Scan the T rows of q/k/v/g/beta over every (layer, head) state.
 
     s_out may be s_in (in place); a distinct s_out leaves s_in as the snapshot.
-    o receives the outputs, e (optional) the stash plane for a cheaper replay.
+    o (optional) receives the outputs.
     """
     lib = load()
     L, T, H = _rows_shape(q, k, v, g, beta)
     _state(s_in, (L, H, D, D), "s_in")
     _state(s_out, (L, H, D, D), "s_out")
     _plane(o, (L, T, H, D), "o")
-    _plane(e, (L, T, H, D), "e")
     dt = _in_dtype((q, k, v, g, beta))
     _check(lib.kda_scan_rows(_dev(s_in, "s_in"), _dev(s_out, "s_out"), _dev(q, "q"), _dev(k, "k"),
                              _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"), _dev(o, "o"),
-                             _dev(e, "e"), L, T, H, dt, _stream(stream)))
+                             L, T, H, dt, _stream(stream)))
+
+
+def kda_scan_rows_stash(s_in, s_out, q, k, v, g, beta, o, e, stream=None) -> None:
+    """kda_scan_rows that also writes the stash plane e [L][T][H][D] (float32,
+    required): each row's delta vector, read by kda_replay_stash and the fused
+    round.  o may be None."""
+    lib = load()
+    L, T, H = _rows_shape(q, k, v, g, beta)
+    _state(s_in, (L, H, D, D), "s_in")
+    _state(s_out, (L, H, D, D), "s_out")
+    _plane(o, (L, T, H, D), "o")
+    if e is None:
+        raise ValueError("e is required")
+    _plane(e, (L, T, H, D), "e")
+    dt = _in_dtype((q, k, v, g, beta))
+    _check(lib.kda_scan_rows_stash(_dev(s_in, "s_in"), _dev(s_out, "s_out"), _dev(q, "q"),
+                                   _dev(k, "k"), _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"),
+                                   _dev(o, "o"), _dev(e, "e"), L, T, H, dt, _stream(stream)))
 
 
 def kda_scan_rows_columns(s_in, s_cols, q, k, v, g, beta, o, e=None, stream=None) -> None:
@@ -235,19 +254,35 @@ def _kept_rows(k, v, g, beta, e, what):
     return L, T, H, _in_dtype(present)
 
 
-def kda_replay(snap, s_out, k, v, g, beta, keep: int, e=None, stream=None) -> None:
+def kda_replay(snap, s_out, q, k, v, g, beta, keep: int, stream=None) -> None:
     """s_out = state after rows 0..keep-1 of the round, rebuilt from snap.
 
-    k, v, g [L][T_round][H][D] and beta [L][T_round][H] are the round's retained
-    inputs; keep = j + 1.  With the round's stash plane e, v and beta may be None.
+    q, k, v, g [L][T_round][H][D] and beta [L][T_round][H] are the round's
+    retained inputs, the tensors given to its kda_scan_rows (q is not read);
+    keep = j + 1.
     """
     lib = load()
-    L, T_round, H, dt = _kept_rows(k, v, g, beta, e, "replay")
+    L, T_round, H = _rows_shape(q, k, v, g, beta)
+    dt = _in_dtype((q, k, v, g, beta))
     _state(snap, (L, H, D, D), "snap")
     _state(s_out, (L, H, D, D), "s_out")
-    _check(lib.kda_replay(_dev(snap, "snap"), _dev(s_out, "s_out"), _dev(k, "k"), _dev(v, "v"),
-                          _dev(g, "g"), _dev(beta, "beta"), _dev(e, "e"), L, T_round, int(keep),
+    _check(lib.kda_replay(_dev(snap, "snap"), _dev(s_out, "s_out"), _dev(q, "q"), _dev(k, "k"),
+                          _dev(v, "v"), _dev(g, "g"), _dev(beta, "beta"), L, T_round, int(keep),
                           H, dt, _stream(stream)))
+
+
+def kda_replay_stash(snap, s_out, k, g, e, keep: int, stream=None) -> None:
+    """kda_replay from the round's stash plane e (written by kda_scan_rows_stash):
+    only k, g [L][T_round][H][D] and e are read; same bits as kda_replay."""
+    lib = load()
+    if e is None:
+        raise ValueError("e is required")
+    L, T_round, H, dt = _kept_rows(k, None, g, None, e, "replay")
+    _state(snap, (L, H, D, D), "snap")
+    _state(s_out, (L, H, D, D), "s_out")
+    _check(lib.kda_replay_stash(_dev(snap, "snap"), _dev(s_out, "s_out"), _dev(k, "k"),
+                                _dev(g, "g"), _dev(e, "e"), L, T_round, int(keep), H, dt,
+                                _stream(stream)))
 
 
 def _j_dev(j):
@@ -517,5 +552,6 @@ __all__ = [
     "kda_replay", "kda_scan_batched", "kda_verify_round", "state_table", "kda_abi_version",
     "kda_last_error", "kda_accept_greedy", "accept_workspace", "ACCEPT_WORK_BYTES", "NO_TOKEN",
     "kda_conv_reroll", "copy_table", "kda_copy_batch", "RING_ROWS", "kda_row_ops",
-    "kda_verify_round_multi", "MAX_PREV_ROUNDS", "kda_scan_rows_columns",
+    "kda_verify_round_multi", "MAX_PREV_ROUNDS", "kda_scan_rows_columns", "kda_scan_rows_stash",
+    "kda_replay_stash",
 ]

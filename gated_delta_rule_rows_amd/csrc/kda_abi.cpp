@@ -231,18 +231,10 @@ int conv_reroll(const char* fn, const float* ring_snap, const void* raw, float* 
                                            static_cast<hipStream_t>(stream)));
 }
 
-}  // namespace
-
-extern "C" {
-
-int kda_abi_version(void) { return KDA_ABI_VERSION; }
-
-const char* kda_last_error(void) { return g_err; }
-
-int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k, const void* v,
-                  const void* g, const void* beta, float* o, float* e, int L, int T, int H,
-                  int in_dtype, void* stream) {
-    const char* fn = "kda_scan_rows";
+// kda_scan_rows / kda_scan_rows_stash: e (the stash plane) is written when given.
+int scan_rows(const char* fn, const float* s_in, float* s_out, const void* q, const void* k,
+              const void* v, const void* g, const void* beta, float* o, float* e, int L, int T,
+              int H, int in_dtype, void* stream) {
     int rc;
     if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H)) ||
         (rc = check_rows(fn, "T", T)))
@@ -273,6 +265,70 @@ int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k,
     const kda::Launch kind = o ? kda::Launch::kScanOut : kda::Launch::kScanState;
     return launched(fn, kda::launch_scan(a, kind, in_dtype == KDA_IN_BF16,
                                          static_cast<hipStream_t>(stream)));
+}
+
+// kda_replay (q, v, beta given, e NULL) / kda_replay_stash (e given; q, v,
+// beta NULL and not read).  q is validated like the other rows although a
+// replay never reads it: the caller passes the round's own buffers.
+int replay(const char* fn, const float* snap, float* s_out, const void* q, const void* k,
+           const void* v, const void* g, const void* beta, const float* e, int L, int T_round,
+           int keep, int H, int in_dtype, void* stream) {
+    int rc;
+    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H)) ||
+        (rc = check_rows(fn, "T_round", T_round)))
+        return rc;
+    if (keep < 1 || keep > T_round)
+        return refuse(KDA_ERR_RANGE,
+                      "%s: keep=%d outside 1..=%d (the anchor row is always committed; "
+                      "keep = accepted drafts + 1)",
+                      fn, keep, T_round);
+    const unsigned long long chains = static_cast<unsigned long long>(L) * H;
+    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
+    const unsigned long long rows = chains * T_round;
+    const bool stash = e != nullptr;   // with the stash plane, q, v and beta are not passed
+    const Span in[] = {
+        {"snap", snap, chains * kStateBytes, 16, false},
+        {"q", q, rows * kRowElems * es, 16, stash},
+        {"k", k, rows * kRowElems * es, 16, false},
+        {"v", v, rows * kRowElems * es, 16, stash},
+        {"g", g, rows * kRowElems * es, 16, false},
+        {"beta", beta, rows * es, es, stash},
+        {"e", e, rows * kRowElems * 4, 16, true},
+    };
+    const Span out[] = {{"s_out", s_out, chains * kStateBytes, 16, false}};
+    if ((rc = check_spans(fn, in, 7)) || (rc = check_spans(fn, out, 1)) ||
+        (rc = check_alias(fn, out, 1, in, 7)))
+        return rc;
+    kda::ScanArgs a{};
+    a.s_in = snap; a.s_out = s_out;
+    a.k = k; a.v = v; a.g = g; a.beta = beta; a.e_in = e;
+    a.n_chains = static_cast<long long>(chains); a.H = H; a.T = keep; a.T_stride = T_round;
+    const kda::Launch kind = stash ? kda::Launch::kReplayStash : kda::Launch::kReplay;
+    return launched(fn, kda::launch_scan(a, kind, in_dtype == KDA_IN_BF16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_last_error(void) { return g_err; }
+
+int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k, const void* v,
+                  const void* g, const void* beta, float* o, int L, int T, int H, int in_dtype,
+                  void* stream) {
+    return scan_rows("kda_scan_rows", s_in, s_out, q, k, v, g, beta, o, nullptr, L, T, H,
+                     in_dtype, stream);
+}
+
+int kda_scan_rows_stash(const float* s_in, float* s_out, const void* q, const void* k,
+                        const void* v, const void* g, const void* beta, float* o, float* e, int L,
+                        int T, int H, int in_dtype, void* stream) {
+    if (!e) return refuse(KDA_ERR_ARG, "kda_scan_rows_stash: e is NULL");
+    return scan_rows("kda_scan_rows_stash", s_in, s_out, q, k, v, g, beta, o, e, L, T, H,
+                     in_dtype, stream);
 }
 
 int kda_scan_rows_columns(const float* s_in, float* s_cols, const void* q, const void* k,
@@ -324,42 +380,19 @@ int kda_snapshot(const float* s, float* snap, int L, int H, void* stream) {
                                          static_cast<hipStream_t>(stream)));
 }
 
-int kda_replay(const float* snap, float* s_out, const void* k, const void* v, const void* g,
-               const void* beta, const float* e, int L, int T_round, int keep, int H, int in_dtype,
+int kda_replay(const float* snap, float* s_out, const void* q, const void* k, const void* v,
+               const void* g, const void* beta, int L, int T_round, int keep, int H, int in_dtype,
                void* stream) {
-    const char* fn = "kda_replay";
-    int rc;
-    if ((rc = check_dtype(fn, in_dtype)) || (rc = check_counts(fn, L, H)) ||
-        (rc = check_rows(fn, "T_round", T_round)))
-        return rc;
-    if (keep < 1 || keep > T_round)
-        return refuse(KDA_ERR_RANGE,
-                      "%s: keep=%d outside 1..=%d (the anchor row is always committed; "
-                      "keep = accepted drafts + 1)",
-                      fn, keep, T_round);
-    const unsigned long long chains = static_cast<unsigned long long>(L) * H;
-    const unsigned es = in_dtype == KDA_IN_BF16 ? 2 : 4;
-    const unsigned long long rows = chains * T_round;
-    const bool stash = e != nullptr;   // with the stash plane, v and beta are not read
-    const Span in[] = {
-        {"snap", snap, chains * kStateBytes, 16, false},
-        {"k", k, rows * kRowElems * es, 16, false},
-        {"g", g, rows * kRowElems * es, 16, false},
-        {"v", v, rows * kRowElems * es, 16, stash},
-        {"beta", beta, rows * es, es, stash},
-        {"e", e, rows * kRowElems * 4, 16, true},
-    };
-    const Span out[] = {{"s_out", s_out, chains * kStateBytes, 16, false}};
-    if ((rc = check_spans(fn, in, 6)) || (rc = check_spans(fn, out, 1)) ||
-        (rc = check_alias(fn, out, 1, in, 6)))
-        return rc;
-    kda::ScanArgs a{};
-    a.s_in = snap; a.s_out = s_out;
-    a.k = k; a.v = v; a.g = g; a.beta = beta; a.e_in = e;
-    a.n_chains = static_cast<long long>(chains); a.H = H; a.T = keep; a.T_stride = T_round;
-    const kda::Launch kind = stash ? kda::Launch::kReplayStash : kda::Launch::kReplay;
-    return launched(fn, kda::launch_scan(a, kind, in_dtype == KDA_IN_BF16,
-                                         static_cast<hipStream_t>(stream)));
+    return replay("kda_replay", snap, s_out, q, k, v, g, beta, nullptr, L, T_round, keep, H,
+                  in_dtype, stream);
+}
+
+int kda_replay_stash(const float* snap, float* s_out, const void* k, const void* g,
+                     const float* e, int L, int T_round, int keep, int H, int in_dtype,
+                     void* stream) {
+    if (!e) return refuse(KDA_ERR_ARG, "kda_replay_stash: e is NULL");
+    return replay("kda_replay_stash", snap, s_out, nullptr, k, nullptr, g, nullptr, e, L, T_round,
+                  keep, H, in_dtype, stream);
 }
 
 int kda_scan_batched(float* const* s_ptrs, const void* q, const void* k, const void* v,

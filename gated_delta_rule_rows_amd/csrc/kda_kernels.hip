@@ -500,7 +500,8 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
             // each column's sum sits in two lanes (lane bit 3); the lane with
             // bit 3 = 0 writes o and e, at a row base held in SGPRs plus its
             // column, and leaves e in its column's LDS slot
-            __shared__ float ex[TL::WAVES * TL::WCOLS];
+            // read back as one float4 per lane (load_cols<4>): 16-byte aligned
+            __shared__ __attribute__((aligned(16))) float ex[TL::WAVES * TL::WCOLS];
             float* slot = ex + (threadIdx.x >> 6) * TL::WCOLS + (lane & 7) * C;
             const size_t row = o0 + t * ostride;
             if ((lane & 8) == 0) {
@@ -993,8 +994,9 @@ __global__ void __launch_bounds__(kOpsThreads) kda_row_ops_kernel(RowOpsArgs a) 
 // ------------------------------------------------------------------ batched copy
 
 // n copies of `words` floats, driven by a device table [src_0..src_{n-1},
-// dst_0..dst_{n-1}] (memra-engine 0.123.0 glm_spec.rs, the batched GDN state
-// snapshot: one table refresh and one launch instead of a copy per layer).
+// dst_0..dst_{n-1}] (memra-engine 0.98.0 dflash.rs, DsparkSnapBatch and its
+// uniform batched f32 copy: one table refresh and one launch instead of a
+// copy per layer of the GDN state snapshot).
 // blockIdx.y picks the buffer pair; its pointers are wave-uniform, so the
 // choice between 16-byte and 4-byte moves is made per pair at run time.
 __global__ void __launch_bounds__(256) kda_copy_batch_kernel(const uint64_t* table, int n,

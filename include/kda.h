@@ -52,7 +52,7 @@ extern "C" {
 #define KDA_HEAD_DIM 128   /* d_k = d_v; glm5_spec_ppn_gate.rs fixture head_dim */
 #define KDA_T_MAX 15       /* verify rows per round: K + 1 <= 15 (glm_spec.rs, WALK-REUSE) */
 #define KDA_B_MAX 15       /* batched-decode sessions per step (same knee) */
-#define KDA_ABI_VERSION 8
+#define KDA_ABI_VERSION 9
 #define KDA_ACCEPT_WORK_BYTES 12288   /* workspace of kda_accept_greedy */
 #define KDA_NO_TOKEN 0xFFFFFFFFu      /* argmax slot of a logits row holding a NaN */
 #define KDA_CONV_RING_ROWS 3          /* short-conv history: kernel size 4 keeps 3 raw rows */
@@ -80,18 +80,31 @@ enum {
  *   q, k, v, g  : [L][T][H][128] in in_dtype.
  *   beta        : [L][T][H] in in_dtype.
  *   o           : [L][T][H][128] f32, or NULL to skip the outputs.
- *   e           : [L][T][H][128] f32, or NULL.  If given, row t's delta
- *                 vector e_t = beta_t (v_t - S'^T k_t) is written: the stash
- *                 plane that lets kda_replay / kda_verify_round rebuild the
- *                 state without the two reductions, bit for bit.
  *   L, H >= 1;  1 <= T <= KDA_T_MAX.
- * The caller keeps k, g (and v, beta, or e) alive until it has either
- * replayed or accepted every row: they are the round's stash (glm_spec.rs,
- * ROLLBACK: the row inputs are retained with zero copies).
+ * The caller keeps q, k, v, g, beta alive until it has either replayed or
+ * accepted every row: they are the round's stash (glm_spec.rs, ROLLBACK: the
+ * row inputs are retained with zero copies), and kda_replay takes the same
+ * pointers.
  */
 int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k,
-                  const void* v, const void* g, const void* beta, float* o, float* e, int L,
-                  int T, int H, int in_dtype, void* stream);
+                  const void* v, const void* g, const void* beta, float* o, int L, int T, int H,
+                  int in_dtype, void* stream);
+
+/*
+ * kda_scan_rows that also writes the round's stash plane e.
+ *   e           : [L][T][H][128] f32, required: row t's delta vector
+ *                 e_t = beta_t (v_t - S'^T k_t), the exact value the scan
+ *                 added (S = S' + k_t e_t^T).  kda_replay_stash and the fused
+ *                 round rebuild the state from k, g and e without the two
+ *                 reductions, bit for bit.  The pages size their stash at
+ *                 about 160 KB per row per layer (glm_spec.rs, ROLLBACK):
+ *                 one such f32 plane (32 KiB at 64 heads) above the five row
+ *                 inputs.
+ *   The rest as kda_scan_rows.  e must not overlap any other argument.
+ */
+int kda_scan_rows_stash(const float* s_in, float* s_out, const void* q, const void* k,
+                        const void* v, const void* g, const void* beta, float* o, float* e,
+                        int L, int T, int H, int in_dtype, void* stream);
 
 /*
  * The per-row state-column variant of a verify scan: T rows as kda_scan_rows,
@@ -107,7 +120,8 @@ int kda_scan_rows(const float* s_in, float* s_out, const void* q, const void* k,
  *                 s_cols + t*L*H*128*128, is the state after rows 0..t: the
  *                 bits of kda_scan_rows over rows 0..t and of kda_replay with
  *                 keep = t + 1.  Column T-1 is the state after the round.
- *   q..beta, e  : as kda_scan_rows.
+ *   q..beta     : as kda_scan_rows.
+ *   e           : as kda_scan_rows_stash, or NULL.
  *   o           : [L][T][H][128] f32, required.
  *   No output may overlap an input.  L, H >= 1;  1 <= T <= KDA_T_MAX.
  */
@@ -135,17 +149,30 @@ int kda_snapshot(const float* s, float* snap, int L, int H, void* stream);
  *   T_round needs no replay (the resident state already is it); the call stays
  *   legal and then returns the scan's final state bits.
  *   snap, s_out : [L][H][128][128] f32; they must not overlap.
- *   k, v, g     : the round's row buffers [L][T_round][H][128] (in_dtype),
- *   beta        : [L][T_round][H], as passed to the round's kda_scan_rows;
- *                 rows keep..T_round-1 are not read.
- *   e           : the stash plane that scan wrote ([L][T_round][H][128] f32),
- *                 or NULL.  With e, v and beta are not read (may be NULL) and
- *                 each row is only the decay and the rank-1 update.
+ *   q, k, v, g  : the round's row buffers [L][T_round][H][128] (in_dtype),
+ *   beta        : [L][T_round][H] -- the very pointers passed to the round's
+ *                 kda_scan_rows.  q is not read (a replay writes no outputs)
+ *                 but must be a valid non-NULL aligned pointer, like the
+ *                 others; rows keep..T_round-1 are not read.
  *   No outputs are written.
  */
-int kda_replay(const float* snap, float* s_out, const void* k, const void* v, const void* g,
-               const void* beta, const float* e, int L, int T_round, int keep, int H,
+int kda_replay(const float* snap, float* s_out, const void* q, const void* k, const void* v,
+               const void* g, const void* beta, int L, int T_round, int keep, int H,
                int in_dtype, void* stream);
+
+/*
+ * kda_replay from the stash plane: the same rollback, reading each kept row's
+ * delta vector e from the plane kda_scan_rows_stash wrote instead of
+ * recomputing it from v, beta and S'^T k.  Each row is then only the decay
+ * and the rank-1 update, and s_out carries the same bits as kda_replay.
+ *   glm_spec.rs (0.123.0), ROLLBACK: accept-j replays the stolen scan inputs
+ *   from the snapshot.
+ *   k, g : [L][T_round][H][128] in in_dtype;  e : [L][T_round][H][128] f32.
+ *   The rest as kda_replay.
+ */
+int kda_replay_stash(const float* snap, float* s_out, const void* k, const void* g,
+                     const float* e, int L, int T_round, int keep, int H, int in_dtype,
+                     void* stream);
 
 /*
  * Batched-decode arm: B independent sessions, one row each (t = 1), each
@@ -182,13 +209,14 @@ int kda_scan_batched(float* const* s_ptrs, const void* q, const void* k, const v
  *                 The state after this round's rows is NOT stored: the next
  *                 round (or kda_replay) rebuilds what the accept keeps.
  *   pk, pv, pg, pbeta, pe : the previous round's retained rows and stash, as
- *                 for kda_replay, in a [L][T_prev][H] layout.  With pe, pv and
- *                 pbeta are not read.  All may be NULL when keep == 0.
+ *                 for kda_replay (kda_replay_stash with pe), in a
+ *                 [L][T_prev][H] layout.  With pe, pv and pbeta are not read.  All may be NULL when keep == 0.
  *   T_prev      : the previous round's row count, 0..KDA_T_MAX.
  *   keep        : previous-round rows to keep, 0..T_prev (0: snap_prev is
  *                 already committed; then snap_out is a copy of it).
  *   q..beta, o  : this round's rows and outputs, as for kda_scan_rows; o is
- *                 required.  e (optional) receives this round's stash plane.
+ *                 required.  e (optional) receives this round's stash plane,
+ *                 as kda_scan_rows_stash writes it.
  *   1 <= T <= KDA_T_MAX.
  * Bit for bit, snap_out equals kda_replay(snap_prev, ..., keep) and o equals
  * kda_scan_rows(snap_out, ...)'s outputs.
@@ -341,8 +369,9 @@ int kda_conv_reroll_dev(const float* ring_snap, const void* raw, float* ring_out
 
 /*
  * Batched uniform copy: n buffers of `words` f32 each, in one launch.
- *   glm_spec.rs (0.123.0), the batched GDN state snapshot: one pointer-table
- *   refresh and one launch replace a copy per layer.
+ *   dflash.rs (memra-engine 0.98.0), DsparkSnapBatch / copy_batch_uniform_f32:
+ *   the batched GDN state snapshot, where one pointer-table refresh and one
+ *   launch replace a copy per layer.
  *   table : DEVICE array of 2n u64, [src_0 .. src_{n-1}, dst_0 .. dst_{n-1}],
  *           8-byte aligned; each entry a device address of `words` f32
  *           (4-byte aligned; pairs that are both 16-byte aligned, with words a

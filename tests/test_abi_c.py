@@ -1,6 +1,11 @@
 """include/kda.h is a C header: a C99 program compiles against it, links
 libkda.so and calls the entry points through plain C.
 
+The program declares the four hot-path calls itself, with the argument lists
+of the boundary as it is specified (scan, snapshot, replay, batched arm), and
+those declarations must agree with the header's: a C compiler rejects a
+redeclaration with different parameter types.
+
 No GPU is needed: the program checks the ABI version and that validation
 refuses bad arguments (null pointers, ranges) with the documented status codes
 before anything reaches the device.
@@ -20,6 +25,24 @@ C_SRC = r"""
 #include <string.h>
 #include "kda.h"
 
+/* The boundary's four hot-path calls, written out from their specification.
+   Redeclaring a function with an incompatible prototype is a compile error. */
+int kda_scan_rows(const float* s_in, float* s_out,
+                  const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, float* o,
+                  int L, int T, int H, int in_dtype, void* stream);
+int kda_snapshot(const float* s, float* snap, int L, int H, void* stream);
+int kda_replay(const float* snap, float* s_out,
+               const void* q, const void* k, const void* v, const void* g,
+               const void* beta,
+               int L, int T_round, int keep, int H, int in_dtype, void* stream);
+int kda_scan_batched(float* const* s_ptrs,
+                     const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, float* o,
+                     int L, int B, int H, int in_dtype, void* stream);
+const char* kda_last_error(void);
+int kda_abi_version(void);
+
 static int expect(int got, int want, const char* what) {
     if (got != want) {
         printf("FAIL %s: status %d, want %d (%s)\n", what, got, want, kda_last_error());
@@ -35,12 +58,19 @@ int main(void) {
         return 1;
     }
     /* refusals happen on the host, before any device work */
-    bad |= expect(kda_scan_rows(0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 16, 1, KDA_IN_F32, 0),
+    bad |= expect(kda_scan_rows(0, 0, 0, 0, 0, 0, 0, 0, 1, 16, 1, KDA_IN_F32, 0),
                   KDA_ERR_RANGE, "scan T=16");
-    bad |= expect(kda_scan_rows(0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 8, 1, KDA_IN_F32, 0),
+    bad |= expect(kda_scan_rows(0, 0, 0, 0, 0, 0, 0, 0, 1, 8, 1, KDA_IN_F32, 0),
                   KDA_ERR_ARG, "scan null state");
+    bad |= expect(kda_snapshot(0, 0, 0, 1, 0), KDA_ERR_RANGE, "snapshot L=0");
     bad |= expect(kda_replay(0, 0, 0, 0, 0, 0, 0, 1, 8, 0, 1, KDA_IN_F32, 0),
                   KDA_ERR_RANGE, "replay keep=0");
+    bad |= expect(kda_replay(0, 0, 0, 0, 0, 0, 0, 1, 8, 9, 1, KDA_IN_F32, 0),
+                  KDA_ERR_RANGE, "replay keep=9");
+    bad |= expect(kda_scan_rows_stash(0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 8, 1, KDA_IN_F32, 0),
+                  KDA_ERR_ARG, "scan_stash null e");
+    bad |= expect(kda_replay_stash(0, 0, 0, 0, 0, 1, 8, 3, 1, KDA_IN_F32, 0),
+                  KDA_ERR_ARG, "replay_stash null e");
     bad |= expect(kda_scan_batched(0, 0, 0, 0, 0, 0, 0, 1, KDA_B_MAX + 1, 1, KDA_IN_BF16, 0),
                   KDA_ERR_RANGE, "batched B=16");
     bad |= expect(kda_verify_round(0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 1, 8, 1, 7, 0),

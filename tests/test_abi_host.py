@@ -41,6 +41,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert set(names) >= {"kda_scan_rows", "kda_snapshot", "kda_replay", "kda_scan_batched",
+                          "kda_scan_rows_stash", "kda_replay_stash",
                           "kda_verify_round", "kda_accept_greedy", "kda_conv_reroll",
                           "kda_copy_batch", "kda_row_ops", "kda_verify_round_multi",
                           "kda_scan_rows_columns", "kda_verify_round_dev", "kda_conv_reroll_dev",
@@ -94,10 +95,19 @@ def b():
 
 def _scan(lib, b, **kw):
     a = dict(s_in=b["s_in"], s_out=b["s_out"], q=b["q"], k=b["k"], v=b["v"], g=b["g"],
-             beta=b["beta"], o=b["o"], e=None, L=2, T=8, H=2, dt=0)
+             beta=b["beta"], o=b["o"], L=2, T=8, H=2, dt=0)
     a.update(kw)
     return lib.kda_scan_rows(a["s_in"], a["s_out"], a["q"], a["k"], a["v"], a["g"], a["beta"],
-                             a["o"], a["e"], a["L"], a["T"], a["H"], a["dt"], None)
+                             a["o"], a["L"], a["T"], a["H"], a["dt"], None)
+
+
+def _scan_stash(lib, b, **kw):
+    a = dict(s_in=b["s_in"], s_out=b["s_out"], q=b["q"], k=b["k"], v=b["v"], g=b["g"],
+             beta=b["beta"], o=b["o"], e=b["ptrs"], L=2, T=8, H=2, dt=0)
+    a.update(kw)
+    return lib.kda_scan_rows_stash(a["s_in"], a["s_out"], a["q"], a["k"], a["v"], a["g"],
+                                   a["beta"], a["o"], a["e"], a["L"], a["T"], a["H"], a["dt"],
+                                   None)
 
 
 def _columns(lib, b, **kw):
@@ -110,11 +120,19 @@ def _columns(lib, b, **kw):
 
 
 def _replay(lib, b, **kw):
-    a = dict(snap=b["snap"], s_out=b["s_out"], k=b["k"], v=b["v"], g=b["g"], beta=b["beta"],
-             e=None, L=2, T=8, keep=3, H=2, dt=0)
+    a = dict(snap=b["snap"], s_out=b["s_out"], q=b["q"], k=b["k"], v=b["v"], g=b["g"],
+             beta=b["beta"], L=2, T=8, keep=3, H=2, dt=0)
     a.update(kw)
-    return lib.kda_replay(a["snap"], a["s_out"], a["k"], a["v"], a["g"], a["beta"], a["e"],
+    return lib.kda_replay(a["snap"], a["s_out"], a["q"], a["k"], a["v"], a["g"], a["beta"],
                           a["L"], a["T"], a["keep"], a["H"], a["dt"], None)
+
+
+def _replay_stash(lib, b, **kw):
+    a = dict(snap=b["snap"], s_out=b["s_out"], k=b["k"], g=b["g"], e=b["ptrs"], L=2, T=8,
+             keep=3, H=2, dt=0)
+    a.update(kw)
+    return lib.kda_replay_stash(a["snap"], a["s_out"], a["k"], a["g"], a["e"], a["L"], a["T"],
+                                a["keep"], a["H"], a["dt"], None)
 
 
 def _round(lib, b, **kw):
@@ -179,8 +197,10 @@ def test_scan_rows_alignment_and_alias(lib, b):
     assert _scan(lib, b, s_out=b["v"]) == ERR_ALIAS and "s_out overlaps v" in _msg(lib)
     assert _scan(lib, b, o=b["s_in"]) == ERR_ALIAS and "o overlaps s_in" in _msg(lib)
     assert _scan(lib, b, o=off("q", 1024)) == ERR_ALIAS
-    assert _scan(lib, b, e=b["o"]) == ERR_ALIAS and "o overlaps e" in _msg(lib)
-    assert _scan(lib, b, e=off("ptrs", 8)) == ERR_ALIGN
+    assert _scan_stash(lib, b, e=b["o"]) == ERR_ALIAS and "o overlaps e" in _msg(lib)
+    assert _scan_stash(lib, b, e=off("ptrs", 8)) == ERR_ALIGN
+    assert _scan_stash(lib, b, e=None) == ERR_ARG and "e is NULL" in _msg(lib)
+    assert _scan_stash(lib, b, T=16) == ERR_RANGE and "kda_scan_rows_stash" in _msg(lib)
 
 
 @pytest.mark.parametrize("kw,code,needle", [
@@ -189,6 +209,9 @@ def test_scan_rows_alignment_and_alias(lib, b):
     (dict(T=0, keep=1), ERR_RANGE, "T_round=0"),
     (dict(T=16, keep=1), ERR_RANGE, "T_round=16"),
     (dict(snap=None), ERR_ARG, "snap is NULL"),
+    (dict(q=None), ERR_ARG, "q is NULL"),
+    (dict(v=None), ERR_ARG, "v is NULL"),
+    (dict(beta=None), ERR_ARG, "beta is NULL"),
     (dict(dt=-1), ERR_ARG, "in_dtype"),
 ])
 def test_replay_refusals(lib, b, kw, code, needle):
@@ -286,16 +309,21 @@ def test_conv_reroll_dev_alignment_and_alias(lib, b):
 def test_replay_alias(lib, b):
     assert _replay(lib, b, s_out=b["snap"]) == ERR_ALIAS and "s_out overlaps snap" in _msg(lib)
     assert _replay(lib, b, s_out=b["g"]) == ERR_ALIAS
-    assert _replay(lib, b, e=b["ptrs"], s_out=b["ptrs"]) == ERR_ALIAS and "overlaps e" in _msg(lib)
+    assert _replay(lib, b, s_out=b["q"]) == ERR_ALIAS and "s_out overlaps q" in _msg(lib)
+    off = lambda n, k: ctypes.c_void_p(b.addr[n] + k)
+    assert _replay(lib, b, q=off("q", 4)) == ERR_ALIGN and "q is not 16-byte" in _msg(lib)
 
 
-def test_replay_stash_makes_v_and_beta_optional(lib, b):
-    # without the stash plane, v and beta are required
-    assert _replay(lib, b, v=None) == ERR_ARG and "v is NULL" in _msg(lib)
-    assert _replay(lib, b, beta=None) == ERR_ARG and "beta is NULL" in _msg(lib)
-    # with it they are optional; the refusal then comes from the (bad) keep only
-    assert _replay(lib, b, v=None, beta=None, e=b["ptrs"], keep=0) == ERR_RANGE
-    assert _replay(lib, b, e=ctypes.c_void_p(b.addr["ptrs"] + 4), keep=1) == ERR_ALIGN
+def test_replay_stash_refusals(lib, b):
+    off = lambda n, k: ctypes.c_void_p(b.addr[n] + k)
+    assert _replay_stash(lib, b, e=None) == ERR_ARG and "e is NULL" in _msg(lib)
+    assert _replay_stash(lib, b, keep=0) == ERR_RANGE and "keep=0" in _msg(lib)
+    assert _replay_stash(lib, b, keep=9) == ERR_RANGE and "kda_replay_stash" in _msg(lib)
+    assert _replay_stash(lib, b, k=None) == ERR_ARG and "k is NULL" in _msg(lib)
+    assert _replay_stash(lib, b, g=None) == ERR_ARG and "g is NULL" in _msg(lib)
+    assert _replay_stash(lib, b, e=off("ptrs", 4)) == ERR_ALIGN
+    assert _replay_stash(lib, b, s_out=b["ptrs"]) == ERR_ALIAS and "overlaps e" in _msg(lib)
+    assert _replay_stash(lib, b, s_out=b["snap"]) == ERR_ALIAS
 
 
 @pytest.mark.parametrize("kw,code,needle", [

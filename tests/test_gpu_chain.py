@@ -70,7 +70,7 @@ def test_accept_j_then_continue_equals_never_drafted_chain(bf16):
         # rollback: replay the kept rows from the snapshot (no work at full accept)
         if keep < T:
             s = torch.empty_like(s0)
-            kda.kda_replay(s0, s, *draft[1:], keep=keep)
+            kda.kda_replay(s0, s, *draft, keep=keep)
         else:
             s = s_all
         # the never-drafted chain over the committed rows
@@ -88,7 +88,7 @@ def test_accept_j_then_continue_equals_never_drafted_chain(bf16):
         assert same(s, p), f"j={j}: state after the continuation"
     # non-vacuity: a partial accept really differs from the full-accept state
     part_state = torch.empty_like(s0)
-    kda.kda_replay(s0, part_state, *draft[1:], keep=1)
+    kda.kda_replay(s0, part_state, *draft, keep=1)
     assert not same(part_state, s_all)
 
 
@@ -125,5 +125,5 @@ def test_fused_session_equals_never_drafted_chain(stash):
     # the last round's commit, by a plain replay
     p_rd, _, p_keep = prev
     last = torch.empty_like(snap)
-    kda.kda_replay(snap, last, *p_rd[1:], keep=p_keep)
+    kda.kda_replay(snap, last, *p_rd, keep=p_keep)
     assert same(last, chain)

@@ -66,7 +66,7 @@ def test_columns_equal_replays_and_the_scan(L, H, T, bf16):
     s_out = torch.empty_like(s0)
     o_ref = torch.empty_like(o)
     e_ref = torch.empty_like(e)
-    kda.kda_scan_rows(s0, s_out, *rd, o=o_ref, e=e_ref)
+    kda.kda_scan_rows_stash(s0, s_out, *rd, o_ref, e_ref)
     torch.cuda.synchronize()
     assert same_bits(s0, s0_copy), "s_in changed"
     assert same_bits(o, o_ref), "o differs from kda_scan_rows"
@@ -74,7 +74,7 @@ def test_columns_equal_replays_and_the_scan(L, H, T, bf16):
     assert same_bits(cols[T - 1], s_out), "last column != scan state"
     rep = torch.empty_like(s0)
     for t in range(T):
-        kda.kda_replay(s0, rep, *rd[1:], keep=t + 1)
+        kda.kda_replay(s0, rep, *rd, keep=t + 1)
         torch.cuda.synchronize()
         assert same_bits(cols[t], rep), f"column {t} != replay(keep={t + 1})"
 

@@ -43,7 +43,7 @@ def test_verify_round_dev_equals_host_keep(L, H, stash):
     rng = np.random.default_rng(91)
     s0 = dev((0.5 * rng.standard_normal((L, H, D, D))).astype(np.float32))
     e_prev = torch.empty(L, T_prev, H, D, device="cuda")
-    kda.kda_scan_rows(s0, torch.empty_like(s0), *prev, o=None, e=e_prev)
+    kda.kda_scan_rows_stash(s0, torch.empty_like(s0), *prev, None, e_prev)
     p = (prev[1], None, prev[3], None, e_prev) if stash else \
         (prev[1], prev[2], prev[3], prev[4], None)
     js = [0, 1, 5, T_prev - 1, T_prev, 1000, 0xFFFFFFFF] if L * H <= 256 else [0, 7, T_prev - 1,

@@ -90,7 +90,7 @@ def test_tiny_workload_rounds_with_replay():
         assert maxerr(host(s_full), S_ref) <= TOL
         keep = int(js[r]) + 1
         s_rep = torch.empty_like(s_gpu)
-        kda.kda_replay(s_gpu, s_rep, *rd[1:], keep=keep)     # s_gpu is the snapshot
+        kda.kda_replay(s_gpu, s_rep, *rd, keep=keep)     # s_gpu is the snapshot
         S_rep = oracle.replay(s_ref, *rows_np(rw), keep=keep)
         assert maxerr(host(s_rep), S_rep) <= TOL
         s_gpu, s_ref = s_rep, S_rep
@@ -112,7 +112,7 @@ def test_one_layer_workload_replay_sweep():
     for j in range(w.T):
         keep = j + 1
         s_rep = torch.empty_like(s_in)
-        kda.kda_replay(s_in, s_rep, *rd[1:], keep=keep)
+        kda.kda_replay(s_in, s_rep, *rd, keep=keep)
         S_rep = oracle.replay(s0, *rows_np(rw), keep=keep, threads=oracle.max_threads())
         assert maxerr(host(s_rep), S_rep) <= TOL, f"keep={keep}"
     assert bits_equal(s_in, dev(s0))   # the scan was out of place: the snapshot is intact
@@ -145,7 +145,7 @@ def test_verify_k14_full_size_sampled_chains():
         keep = int(js[r]) + 1
         if keep < w.T:
             s_rep = torch.empty_like(s_gpu)
-            kda.kda_replay(s_gpu, s_rep, *rd[1:], keep=keep)
+            kda.kda_replay(s_gpu, s_rep, *rd, keep=keep)
             S_ref = oracle.replay(s_ref, *sub, keep=keep, threads=oracle.max_threads())
             assert maxerr(host(s_rep)[:, SAMPLE_HEADS], S_ref) <= TOL
             s_gpu = s_rep
@@ -190,7 +190,7 @@ def test_serving_mix_bf16_sampled_chains(K):
             s_gpu, s_ref = s_full, S_ref
         else:
             s_rep = torch.empty_like(s_gpu)
-            kda.kda_replay(s_gpu, s_rep, *rd[1:], keep=j + 1)
+            kda.kda_replay(s_gpu, s_rep, *rd, keep=j + 1)
             s_ref = oracle.replay(s_ref, *sub, keep=j + 1, threads=oracle.max_threads())
             s_gpu = s_rep
         assert maxerr(host(s_gpu)[:, heads], s_ref) <= TOL
@@ -285,12 +285,12 @@ def test_replay_equals_state_after_keep_rows(bf16):
     for keep in range(1, T + 1):
         chained, _ = scan(chained, slice_rows(rd, keep - 1, keep))
         s_rep = torch.empty_like(snap)
-        kda.kda_replay(snap, s_rep, *rd[1:], keep=keep)
+        kda.kda_replay(snap, s_rep, *rd, keep=keep)
         assert bits_equal(s_rep, chained), f"keep={keep}"
         s_k, _ = scan(snap, slice_rows(rd, 0, keep), want_o=False)
         assert bits_equal(s_rep, s_k)
     s_rep = torch.empty_like(snap)
-    kda.kda_replay(snap, s_rep, *rd[1:], keep=T)
+    kda.kda_replay(snap, s_rep, *rd, keep=T)
     assert bits_equal(s_rep, s_full)     # keep == T returns the resident bits
 
 
@@ -368,12 +368,12 @@ def test_red_arms_diverge():
     s_full, _ = scan(snap, rd)
     keep = 3
     good = torch.empty_like(snap)
-    kda.kda_replay(snap, good, *rd[1:], keep=keep)
+    kda.kda_replay(snap, good, *rd, keep=keep)
     # red 1: no replay -- the resident post-row-K state stands in for the rollback
     n1 = int((host(s_full).view(np.uint32) != host(good).view(np.uint32)).sum())
     # red 2: replay from the wrong snapshot (the post-scan state)
     bad = torch.empty_like(snap)
-    kda.kda_replay(s_full, bad, *rd[1:], keep=keep)
+    kda.kda_replay(s_full, bad, *rd, keep=keep)
     n2 = int((host(bad).view(np.uint32) != host(good).view(np.uint32)).sum())
     assert n1 > 0 and n2 > 0, (n1, n2)
     # non-vacuity: the scan really moved the state away from the snapshot
@@ -392,7 +392,7 @@ def scan_e(s_in, rows):
     s_out = torch.empty_like(s_in)
     o = torch.empty(L, T, H, D, device="cuda")
     e = torch.empty(L, T, H, D, device="cuda")
-    kda.kda_scan_rows(s_in, s_out, *rows, o=o, e=e)
+    kda.kda_scan_rows_stash(s_in, s_out, *rows, o, e)
     return s_out, o, e
 
 
@@ -406,9 +406,9 @@ def test_stash_replay_equals_recomputed_replay(bf16):
     assert bits_equal(s_full, s2) and bits_equal(o, o2)
     for keep in range(1, T + 1):
         a = torch.empty_like(snap)
-        kda.kda_replay(snap, a, *rd[1:], keep=keep)
+        kda.kda_replay(snap, a, *rd, keep=keep)
         b = torch.empty_like(snap)
-        kda.kda_replay(snap, b, rd[1], None, rd[3], None, keep=keep, e=e)
+        kda.kda_replay_stash(snap, b, rd[1], rd[3], e, keep=keep)
         assert bits_equal(a, b), f"keep={keep}"
     assert bits_equal(b, s_full)       # keep == T: the resident bits
 
@@ -428,7 +428,7 @@ def test_verify_round_equals_replay_then_scan(bf16, stash):
     for keep in (0, 1, 7, T_prev):
         if keep:
             ref_snap = torch.empty_like(snap_prev)
-            kda.kda_replay(snap_prev, ref_snap, *prev[1:], keep=keep)
+            kda.kda_replay(snap_prev, ref_snap, *prev, keep=keep)
         else:
             ref_snap = snap_prev
         _, ref_o, ref_e = scan_e(ref_snap, cur)
@@ -444,7 +444,7 @@ def test_verify_round_equals_replay_then_scan(bf16, stash):
     o = torch.empty(L, T, H, D, device="cuda")
     kda.kda_verify_round(x, x, _prev(prev, e_prev, stash), 7, *cur, o)
     ref_snap = torch.empty_like(snap_prev)
-    kda.kda_replay(snap_prev, ref_snap, *prev[1:], keep=7)
+    kda.kda_replay(snap_prev, ref_snap, *prev, keep=7)
     assert bits_equal(x, ref_snap)
 
 
@@ -563,11 +563,11 @@ def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L
     s0 = dev(rand_state(92, L, H, 0.5))
     s_full, o_full = scan(s0, rows)
     e_full = torch.empty(L, T, H, D, device="cuda")
-    kda.kda_scan_rows(s0, torch.empty_like(s0), *rows, o=torch.empty_like(o_full), e=e_full)
+    kda.kda_scan_rows_stash(s0, torch.empty_like(s0), *rows, torch.empty_like(o_full), e_full)
     rep_full = torch.empty_like(s0)
-    kda.kda_replay(s0, rep_full, *rows[1:], keep=6)
+    kda.kda_replay(s0, rep_full, *rows, keep=6)
     reps_full = torch.empty_like(s0)
-    kda.kda_replay(s0, reps_full, rows[1], None, rows[3], None, keep=9, e=e_full)
+    kda.kda_replay_stash(s0, reps_full, rows[1], rows[3], e_full, keep=9)
     snap_full, o2_full = torch.empty_like(s0), torch.empty_like(o_full)
     kda.kda_verify_round(s0, snap_full, (rows[1], None, rows[3], None, e_full), 11, *rows, o2_full)
     torch.cuda.synchronize()
@@ -580,10 +580,10 @@ def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L
         si = lay(s0, l0, l1)
         so, oo = scan(si, rr)
         rp = torch.empty_like(si)
-        kda.kda_replay(si, rp, *rr[1:], keep=6)
+        kda.kda_replay(si, rp, *rr, keep=6)
         el = lay(e_full, l0, l1)
         rps = torch.empty_like(si)
-        kda.kda_replay(si, rps, rr[1], None, rr[3], None, keep=9, e=el)
+        kda.kda_replay_stash(si, rps, rr[1], rr[3], el, keep=9)
         sn, o2 = torch.empty_like(si), torch.empty_like(oo)
         kda.kda_verify_round(si, sn, (rr[1], None, rr[3], None, el), 11, *rr, o2)
         return so, oo, rp, rps, sn, o2
@@ -614,13 +614,13 @@ def test_verify_round_multi_equals_replays_then_scan(L, keeps, store, stash, bf1
         Tn = [15, 9, 12, 15][n]
         r = rows_dev(rand_rows(72 + n, L, Tn, H, bf16=bf16))
         e_n = torch.empty(L, Tn, H, D, device="cuda")
-        kda.kda_scan_rows(ref, torch.empty_like(ref), *r, o=None, e=e_n)
+        kda.kda_scan_rows_stash(ref, torch.empty_like(ref), *r, None, e_n)
         if keep:
             nxt = torch.empty_like(ref)
             if stash:
-                kda.kda_replay(ref, nxt, r[1], None, r[3], None, keep=keep, e=e_n)
+                kda.kda_replay_stash(ref, nxt, r[1], r[3], e_n, keep=keep)
             else:
-                kda.kda_replay(ref, nxt, *r[1:], keep=keep)
+                kda.kda_replay(ref, nxt, *r, keep=keep)
             ref = nxt
         if stash:
             prevs.append((r[1], None, r[3], None, e_n, keep))
@@ -643,10 +643,10 @@ def test_verify_round_multi_in_place_and_refusals():
     s0 = dev(rand_state(81, L, H, 0.5))
     r1 = rows_dev(rand_rows(82, L, 10, H))
     e1 = torch.empty(L, 10, H, D, device="cuda")
-    kda.kda_scan_rows(s0, torch.empty_like(s0), *r1, o=None, e=e1)
+    kda.kda_scan_rows_stash(s0, torch.empty_like(s0), *r1, None, e1)
     cur = rows_dev(rand_rows(83, L, T, H))
     ref = torch.empty_like(s0)
-    kda.kda_replay(s0, ref, r1[1], None, r1[3], None, keep=4, e=e1)
+    kda.kda_replay_stash(s0, ref, r1[1], r1[3], e1, keep=4)
     x = s0.clone()
     o = torch.empty(L, T, H, D, device="cuda")
     kda.kda_verify_round_multi(x, x, [(r1[1], None, r1[3], None, e1, 4)], *cur, o)

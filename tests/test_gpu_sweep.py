@@ -61,7 +61,7 @@ def test_sweep_fused_and_split_vs_oracle(case):
 
     # the previous round's stash plane, from its own scan
     e_prev = torch.empty(L, T_prev, H, D, device="cuda")
-    kda.kda_scan_rows(s0, torch.empty_like(s0), *prev, o=None, e=e_prev)
+    kda.kda_scan_rows_stash(s0, torch.empty_like(s0), *prev, None, e_prev)
 
     # fused round
     snap = torch.empty_like(s0)
@@ -74,9 +74,9 @@ def test_sweep_fused_and_split_vs_oracle(case):
     rep = torch.empty_like(s0)
     if keep:
         if stash:
-            kda.kda_replay(s0, rep, prev[1], None, prev[3], None, keep=keep, e=e_prev)
+            kda.kda_replay_stash(s0, rep, prev[1], prev[3], e_prev, keep=keep)
         else:
-            kda.kda_replay(s0, rep, *prev[1:], keep=keep)
+            kda.kda_replay(s0, rep, *prev, keep=keep)
     else:
         rep.copy_(s0)
     s_after = torch.empty_like(s0)
