@@ -65,6 +65,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "kda_launch.h"
 
@@ -413,145 +414,422 @@ __device__ __forceinline__ void stage(Stage<R, TMAX>& L, const Src& src, int tid
     stage_commit<R, C, M, TMAX>(L, in, src.T, tid);
 }
 
+// ------------------------------------------------------------------ quad key broadcast
+//
+// Every tiling puts the column group on lane bits 0-2 and the key group on
+// bits 3-5 (key-group bits 0, 1, 2 on lane bits 4, 5, 3: the swap layout), so
+// the four lanes of a quad (bits 0-1) hold different value columns of the
+// same 16 keys.  Quad lane n reads keys 4n..4n+3 of a row's per-key vectors
+// (decay, k, scaled q) as one float4; key r of the group is then register
+// r % 4 of quad lane r / 4, and each VALU op that consumes it reads it
+// through a DPP quad_perm broadcast.  A lane reads 3 float4 per row instead of
+// 12 (all 16 of its keys, for each vector), with the same arithmetic in the
+// same order.
+
+// x of quad lane N, as the first operand of the consuming op (the compiler
+// folds this into v_mul_f32_dpp)
+template <int N>
+__device__ __forceinline__ float quad_lane(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), N * 0x55, 0xF, 0xF, true));
+}
+
+// acc = (x of quad lane N) * y + acc, one v_fmac_f32 with a DPP operand (the
+// compiler does not fold a broadcast into fmac).  x is always a register an
+// LDS read wrote, never a VALU op, so the DPP read needs no wait states.
+template <int N>
+__device__ __forceinline__ void fmac_quad(float& acc, float x, float y);
+#define KDA_FMAC_QUAD(N)                                                                        \
+    template <>                                                                                 \
+    __device__ __forceinline__ void fmac_quad<N>(float& acc, float x, float y) {                \
+        asm("v_fmac_f32_dpp %0, %1, %2 quad_perm:[" #N "," #N "," #N "," #N                     \
+            "] row_mask:0xf bank_mask:0xf"                                                      \
+            : "+v"(acc)                                                                         \
+            : "v"(x), "v"(y));                                                                  \
+    }
+KDA_FMAC_QUAD(0)
+KDA_FMAC_QUAD(1)
+KDA_FMAC_QUAD(2)
+KDA_FMAC_QUAD(3)
+#undef KDA_FMAC_QUAD
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// A row's per-key values for this lane's 16 keys, and the ops that consume
+// them.  Two sources with the same arithmetic, so every tiling gives the same
+// bits:
+//   DPP = false: all 16 keys of each vector read from LDS (12 float4 per row);
+//   DPP = true:  3 float4 per row, each key broadcast within the quad.
+// An op with a DPP operand issues in about 1.2x the cycles of a plain one
+// (measured on gfx950), so the VALU-bound whole-head tiling reads its keys
+// from LDS, and the narrow tilings -- one wave per SIMD, where a row's LDS
+// traffic and latency dominate -- broadcast them.
+template <bool DPP>
+struct RowKeys;
+
+template <>
+struct RowKeys<false> {
+    float k[16], d[16], q[16];
+    template <int R, bool Q, int TM>
+    __device__ __forceinline__ void read(const Stage<R, TM>& L, int t, int i0, int) {
+        using KR = KeyRow<R>;
+        const int kb = (t * KR::kStride + KR::at(i0)) / 4;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const float4 x = L.k[kb + r4], y = L.d[kb + r4];
+            k[4 * r4 + 0] = x.x; k[4 * r4 + 1] = x.y; k[4 * r4 + 2] = x.z; k[4 * r4 + 3] = x.w;
+            d[4 * r4 + 0] = y.x; d[4 * r4 + 1] = y.y; d[4 * r4 + 2] = y.z; d[4 * r4 + 3] = y.w;
+            if constexpr (Q) {
+                const float4 z = L.q[kb + r4];
+                q[4 * r4 + 0] = z.x; q[4 * r4 + 1] = z.y; q[4 * r4 + 2] = z.z; q[4 * r4 + 3] = z.w;
+            }
+        }
+    }
+    template <int r> __device__ __forceinline__ float decay(float x) const { return d[r] * x; }
+    template <int r> __device__ __forceinline__ float kmul(float x) const { return k[r] * x; }
+    template <int r> __device__ __forceinline__ float qmul(float x) const { return q[r] * x; }
+    template <int r> __device__ __forceinline__ void kfma(float& acc, float x) const { acc = fmaf(k[r], x, acc); }
+    template <int r> __device__ __forceinline__ void qfma(float& acc, float x) const { acc = fmaf(q[r], x, acc); }
+};
+
+template <>
+struct RowKeys<true> {
+    float k[4], d[4], q[4];   // keys i0 + 4n .. i0 + 4n + 3 of quad lane n
+    template <int R, bool Q, int TM>
+    __device__ __forceinline__ void read(const Stage<R, TM>& L, int t, int i0, int n) {
+        using KR = KeyRow<R>;
+        const int at = (t * KR::kStride + KR::at(i0 + 4 * n)) / 4;
+        const float4 kk = L.k[at], dd = L.d[at];
+        k[0] = kk.x; k[1] = kk.y; k[2] = kk.z; k[3] = kk.w;
+        d[0] = dd.x; d[1] = dd.y; d[2] = dd.z; d[3] = dd.w;
+        if constexpr (Q) {
+            const float4 qq = L.q[at];
+            q[0] = qq.x; q[1] = qq.y; q[2] = qq.z; q[3] = qq.w;
+        }
+    }
+    template <int r> __device__ __forceinline__ float decay(float x) const { return quad_lane<r / 4>(d[r % 4]) * x; }
+    template <int r> __device__ __forceinline__ float kmul(float x) const { return quad_lane<r / 4>(k[r % 4]) * x; }
+    template <int r> __device__ __forceinline__ float qmul(float x) const { return quad_lane<r / 4>(q[r % 4]) * x; }
+    template <int r> __device__ __forceinline__ void kfma(float& acc, float x) const { fmac_quad<r / 4>(acc, k[r % 4], x); }
+    template <int r> __device__ __forceinline__ void qfma(float& acc, float x) const { fmac_quad<r / 4>(acc, q[r % 4], x); }
+};
+
+// Decay, then the in-lane partial sums u (and w) over the 16 keys in order;
+// the first key starts each sum with a plain product.
+template <int C, bool Q>
+__device__ __forceinline__ void decay_sums(const RowKeys<false>& x, float (&s)[16][C],
+                                           float (&u)[C], float (&w)[C]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            s[r][c] = x.d[r] * s[r][c];
+            if (r == 0) {
+                u[c] = x.k[0] * s[0][c];
+                if constexpr (Q) w[c] = x.q[0] * s[0][c];
+            } else {
+                u[c] = fmaf(x.k[r], s[r][c], u[c]);
+                if constexpr (Q) w[c] = fmaf(x.q[r], s[r][c], w[c]);
+            }
+        }
+    }
+}
+
+template <int C, bool Q>
+__device__ __forceinline__ void decay_sums(const RowKeys<true>& x, float (&s)[16][C],
+                                           float (&u)[C], float (&w)[C]) {
+    static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            s[r][c] = x.template decay<r>(s[r][c]);
+            if constexpr (r == 0) {
+                u[c] = x.template kmul<0>(s[0][c]);
+                if constexpr (Q) w[c] = x.template qmul<0>(s[0][c]);
+            } else {
+                x.template kfma<r>(u[c], s[r][c]);
+                if constexpr (Q) x.template qfma<r>(w[c], s[r][c]);
+            }
+        }
+    });
+}
+
+// The rank-1 write S += k e^T.
+template <int C>
+__device__ __forceinline__ void write_rows(const RowKeys<false>& x, float (&s)[16][C],
+                                           const float (&e)[C]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int c = 0; c < C; ++c) s[r][c] = fmaf(x.k[r], e[c], s[r][c]);
+}
+
+template <int C>
+__device__ __forceinline__ void write_rows(const RowKeys<true>& x, float (&s)[16][C],
+                                           const float (&e)[C]) {
+    static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+#pragma unroll
+        for (int c = 0; c < C; ++c) x.template kfma<r>(s[r][c], e[c]);
+    });
+}
+
+// A stash replay row: decay, then the rank-1 write, key by key.  From LDS
+// the keys come four at a time: few live registers, which leaves room for the
+// next phase's row loads the fused round holds meanwhile.
+template <int C, bool Q, int R, int TM>
+__device__ __forceinline__ void stash_rows_lds(const Stage<R, TM>& L, int t, int i0,
+                                               float (&s)[16][C], const float (&e)[C]) {
+    using KR = KeyRow<R>;
+    const int kb = (t * KR::kStride + KR::at(i0)) / 4;
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 x = L.k[kb + r4];
+        const float4 y = L.d[kb + r4];
+        const float k4[4] = {x.x, x.y, x.z, x.w};
+        const float d4[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int c = 0; c < C; ++c)
+                s[4 * r4 + m][c] = fmaf(k4[m], e[c], d4[m] * s[4 * r4 + m][c]);
+        asm volatile("" ::: "memory");   // the next four keys' reads wait here
+    }
+}
+
+template <int C, typename K>
+__device__ __forceinline__ void stash_rows(const K& x, float (&s)[16][C], const float (&e)[C]) {
+    static_for<0, 16>([&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            s[r][c] = x.template decay<r>(s[r][c]);
+            x.template kfma<r>(s[r][c], e[c]);
+        }
+    });
+}
+
+// Sum over the 8 key groups of one value in every lane: the pairs (g, g^1),
+// (g, g^2), (g, g^4) on lane bits 4, 5, 3, each lane adding its partner's.
+__device__ __forceinline__ float sum_groups(float x) {
+    float y = x;
+    swap16(x, y);   // even rows: (own, odd partner); odd rows: (even partner, own)
+    x = x + y;
+    y = x;
+    swap32(x, y);
+    x = x + y;
+    return x + dpp<0x128>(x);   // row_ror:8
+}
+
+// Sums over the 8 key groups of two values a, b: rows with lane bit 4 clear
+// end with a's sum, the others with b's.
+__device__ __forceinline__ float sum_groups2(float a, float b) {
+    swap16(a, b);   // even rows: (a own, a odd partner); odd rows: (b even partner, b own)
+    float x = a + b;
+    float y = x;
+    swap32(x, y);
+    x = x + y;
+    return x + dpp<0x128>(x);
+}
+
+// A value of every lane in row r, copied to the lanes of row r ^ 1 (bit 4) and
+// kept: the lane of row r gets (x of the even row of its pair, x of the odd).
+__device__ __forceinline__ void gather_pair16(float& lo, float& hi) {
+    hi = lo;
+    swap16(lo, hi);
+}
+
+// Lane layouts.  Swap (every launch but the two below): column group on lane
+// bits 0-2, key group on bits 4, 5, 3 (see reduce_scatter4 and quad_lane).
+// Plain (the batched arm and the state-column arm at whole heads, which
+// measured faster with it): key group on bits 0-2, column group on bits 3-5,
+// each column reduced with group_sum<8>.  Both reduce with the same pairs in
+// the same order, so they give the same bits.
+template <int C, Rows M, bool TABLE>
+constexpr bool plain_layout() {
+    return C == 4 && (TABLE || M == Rows::kFullCols);
+}
+
+// One row t of one phase over the staged rows L.  The lane's key group starts
+// at i0, its columns at j0 (ig: its key group, used by the plain layout).
 // kFullCols: `cols` addresses this chain's state in column 0, and row t's
 // state goes to cols + t * col_stride.
-// SW: the swap layout (above); the lane's 4 columns are reduced with
-// reduce_scatter4, and e comes back to the lanes of its column group through
-// a wave-private LDS slot per column.
-template <int R, int C, Rows M, bool SW, int TM>
+template <int R, int C, Rows M, bool PLAIN, int TM, typename K>
+__device__ __forceinline__ void row_step(const Stage<R, TM>& L, const K& x, float (&s)[R][C], int t,
+                                         float* o, float* e_out, size_t o0, size_t ostride,
+                                         int ig, int i0, int j0, gfloat* cols, size_t col_stride) {
+    const float* sve = reinterpret_cast<const float*>(L.ve);
+    const int lane = threadIdx.x & 63;
+    constexpr bool Q = has_q(M);
+    if constexpr (M == Rows::kStash) {
+        float e[C];
+        load_cols<C>(sve + t * kD + j0, e);
+        if constexpr (C < 4) stash_rows<C>(x, s, e);
+        else stash_rows_lds<C, false, R, TM>(L, t, i0, s, e);
+        return;
+    }
+    const float2 bq = L.bq[t];
+    const float nbt = -bq.x;
+    float u[C], w[C];
+    decay_sums<C, Q>(x, s, u, w);
+    float e[C];
+    if constexpr (PLAIN) {
+        float ve[C];   // beta * v
+        load_cols<C>(sve + t * kD + j0, ve);
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            u[c] = group_sum<8>(u[c]);
+            if constexpr (Q) w[c] = group_sum<8>(w[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < C; ++c) e[c] = fmaf(nbt, u[c], ve[c]);   // e = beta v - beta u
+        const size_t row = o0 + t * ostride;
+        if constexpr (Q) {
+            // finish w's butterfly on every lane: sunk into the writer's
+            // branch, its last DPP step would become mov 0, mov_dpp, add
+#pragma unroll
+            for (int c = 0; c < C; ++c) asm volatile("" : "+v"(w[c]));
+            float ov[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) ov[c] = fmaf(e[c], bq.y, w[c]);
+            if (ig == 0) store_cols<C>(o + row + j0, ov);
+        }
+        if (e_out != nullptr && ig == 0) store_cols<C>(e_out + row + j0, e);
+    } else if constexpr (C == 4) {
+        // row k (lane bits 4-5) ends with column k's sums; e comes back to
+        // the lanes of its column group through a wave-private LDS slot
+        const int kc = (lane >> 4) & 3;
+        const uint32_t col = static_cast<uint32_t>(j0 + kc);
+        float uo = reduce_scatter4(u);
+        asm volatile("" : "+v"(uo));
+        const float eo = fmaf(nbt, uo, sve[t * kD + col]);
+        float ov = 0.0f;
+        if constexpr (Q) {
+            float wo = reduce_scatter4(w);
+            asm volatile("" : "+v"(wo));
+            ov = fmaf(eo, bq.y, wo);
+        }
+        // read back as one float4 per lane: 16-byte aligned
+        __shared__ __attribute__((aligned(16))) float ex[4 * 8 * 4];
+        float* slot = ex + (threadIdx.x >> 6) * 32 + (lane & 7) * 4;
+        const size_t row = o0 + t * ostride;
+        if ((lane & 8) == 0) {
+            if constexpr (Q) {
+                gfloat* orow = (gfloat*)(o + row);
+                asm volatile("" : "+s"(orow));
+                orow[col] = ov;
+            }
+            if (e_out != nullptr) {
+                gfloat* erow = (gfloat*)(e_out + row);
+                asm volatile("" : "+s"(erow));
+                erow[col] = eo;
+            }
+            slot[kc] = eo;
+        }
+        __builtin_amdgcn_wave_barrier();   // one wave writes and reads the slots, in order
+        load_cols<4>(slot, e);
+    } else if constexpr (C == 2) {
+        // column c = lane bit 4 (row & 1)
+        const uint32_t col = static_cast<uint32_t>(j0 + ((lane >> 4) & 1));
+        const size_t row = o0 + t * ostride;
+        float ec;
+        if constexpr (Q) {
+            // rows 0, 1 end with u of columns 0, 1; rows 2, 3 with w
+            const float sums[4] = {u[0], u[1], w[0], w[1]};
+            const float x4 = reduce_scatter4(sums);
+            ec = fmaf(nbt, x4, sve[t * kD + col]);   // valid in rows 0, 1
+            float e2 = ec;
+            swap32(ec, e2);                          // rows 2, 3 take e from rows 0, 1
+            const float ov = fmaf(ec, bq.y, x4);     // valid in rows 2, 3
+            if ((lane & 0x28) == 0x20) {
+                gfloat* orow = (gfloat*)(o + row);
+                asm volatile("" : "+s"(orow));
+                orow[col] = ov;
+            }
+        } else {
+            ec = fmaf(nbt, sum_groups2(u[0], u[1]), sve[t * kD + col]);
+        }
+        if (e_out != nullptr && (lane & 0x28) == 0) {
+            gfloat* erow = (gfloat*)(e_out + row);
+            asm volatile("" : "+s"(erow));
+            erow[col] = ec;
+        }
+        gather_pair16(ec, e[1]);
+        e[0] = ec;
+    } else {
+        const uint32_t col = static_cast<uint32_t>(j0);
+        const size_t row = o0 + t * ostride;
+        if constexpr (Q) {
+            const float x2 = sum_groups2(u[0], w[0]);   // even rows u, odd rows w
+            float ec = fmaf(nbt, x2, sve[t * kD + col]); // valid in even rows
+            float odd;
+            gather_pair16(ec, odd);                     // ec: the even row's e, in all rows
+            const float ov = fmaf(ec, bq.y, x2);        // valid in odd rows
+            if ((lane & 0x38) == 0x10) {
+                gfloat* orow = (gfloat*)(o + row);
+                asm volatile("" : "+s"(orow));
+                orow[col] = ov;
+            }
+            e[0] = ec;
+        } else {
+            e[0] = fmaf(nbt, sum_groups(u[0]), sve[t * kD + col]);
+        }
+        if (e_out != nullptr && (lane & 0x38) == 0) {
+            gfloat* erow = (gfloat*)(e_out + row);
+            asm volatile("" : "+s"(erow));
+            erow[col] = e[0];
+        }
+    }
+    // delta-rule write: S = S' + k e^T
+    write_rows<C>(x, s, e);
+    if constexpr (M == Rows::kFullCols) {
+        gfloat* colp = cols + t * col_stride + (i0 * kD + j0);
+#pragma unroll
+        for (int r = 0; r < R; ++r) store_gcols<C, false>(colp + r * kD, s[r]);
+    }
+}
+
+// T rows of one phase.  The whole-head tiling (several waves per SIMD hide
+// each other's latency) reads each row's keys when it starts it.  The narrow
+// tilings run one wave per SIMD, so each row's key reads are issued during the
+// previous row (two register sets, used in turn: no copies between them).
+template <int R, int C, Rows M, bool PLAIN, bool PF, int TM>
 __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C], int T,
                                          float* o, float* e_out, size_t o0, size_t ostride,
                                          int ig, int i0, int j0, gfloat* cols = nullptr,
                                          size_t col_stride = 0) {
-    using TL = Tile<R, C>;
-    using KR = KeyRow<R>;
-    const float* sve = reinterpret_cast<const float*>(L.ve);
+    static_assert(R == 16, "a quad covers 16 keys");
+    constexpr bool DPP = C < 4;
+    constexpr bool Q = has_q(M);
+    const int n = threadIdx.x & 3;
+    if constexpr (!DPP || !PF) {
 #pragma unroll 1
-    for (int t = 0; t < T; ++t) {
-        const int kb = t * KR::kStride + KR::at(i0);
-        if constexpr (M == Rows::kStash) {
-            // e is known up front, so each key's decay and update run
-            // together.  Whole-head lanes take four keys at a time: few live
-            // registers, which lets the fused round hold the next phase's row
-            // loads meanwhile.  Narrower lanes have registers to spare and
-            // issue all their LDS reads at once (one wait per row).
-            float e[C];
-            load_cols<C>(sve + t * kD + j0, e);
-#pragma unroll
-            for (int r4 = 0; r4 < R / 4; ++r4) {
-                const float4 x = L.k[kb / 4 + r4];
-                const float4 y = L.d[kb / 4 + r4];
-                const float k4[4] = {x.x, x.y, x.z, x.w};
-                const float d4[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-#pragma unroll
-                    for (int c = 0; c < C; ++c)
-                        s[4 * r4 + m][c] = fmaf(k4[m], e[c], s[4 * r4 + m][c] * d4[m]);
-                }
-                if constexpr (C == 4) asm volatile("" ::: "memory");   // next four keys' reads wait here
-            }
-            continue;
+        for (int t = 0; t < T; ++t) {
+            RowKeys<DPP> x;   // a stash row reads its keys itself from LDS, four at a time
+            if constexpr (M != Rows::kStash || DPP) x.template read<R, Q, TM>(L, t, i0, n);
+            row_step<R, C, M, PLAIN, TM>(L, x, s, t, o, e_out, o0, ostride, ig, i0, j0, cols,
+                                         col_stride);
         }
-        float kk[R], dk[R], qq[R];
-#pragma unroll
-        for (int r4 = 0; r4 < R / 4; ++r4) {
-            const float4 x = L.k[kb / 4 + r4];
-            const float4 y = L.d[kb / 4 + r4];
-            kk[4 * r4 + 0] = x.x; kk[4 * r4 + 1] = x.y; kk[4 * r4 + 2] = x.z; kk[4 * r4 + 3] = x.w;
-            dk[4 * r4 + 0] = y.x; dk[4 * r4 + 1] = y.y; dk[4 * r4 + 2] = y.z; dk[4 * r4 + 3] = y.w;
-            if constexpr (has_q(M)) {
-                const float4 z = L.q[kb / 4 + r4];
-                qq[4 * r4 + 0] = z.x; qq[4 * r4 + 1] = z.y; qq[4 * r4 + 2] = z.z; qq[4 * r4 + 3] = z.w;
-            }
-        }
-        const float2 bq = L.bq[t];
-        const float nbt = -bq.x;
-        // decay, then the in-lane partial reductions over this lane's keys
-        float u[C], w[C];
-#pragma unroll
-        for (int c = 0; c < C; ++c) { u[c] = 0.0f; w[c] = 0.0f; }
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                s[r][c] = s[r][c] * dk[r];
-                u[c] = fmaf(kk[r], s[r][c], u[c]);
-                if constexpr (has_q(M)) w[c] = fmaf(qq[r], s[r][c], w[c]);
-            }
-        }
-        float e[C];
-        if constexpr (SW) {
-            static_assert(C == 4 && TL::NI == 8, "the swap layout is the whole-head tiling");
-            const int lane = threadIdx.x & 63;
-            const int kc = (lane >> 4) & 3;   // the column this lane reduces
-            const uint32_t col = static_cast<uint32_t>(j0 + kc);
-            // the last DPP adds of both reductions stay out of the writer's
-            // branch (sunk there, each becomes a DPP move and an add)
-            float uo = reduce_scatter4(u);
-            asm volatile("" : "+v"(uo));
-            const float eo = fmaf(nbt, uo, sve[t * kD + col]);
-            float ov = 0.0f;
-            if constexpr (has_q(M)) {
-                float wo = reduce_scatter4(w);
-                asm volatile("" : "+v"(wo));
-                ov = fmaf(eo, bq.y, wo);
-            }
-            // each column's sum sits in two lanes (lane bit 3); the lane with
-            // bit 3 = 0 writes o and e, at a row base held in SGPRs plus its
-            // column, and leaves e in its column's LDS slot
-            // read back as one float4 per lane (load_cols<4>): 16-byte aligned
-            __shared__ __attribute__((aligned(16))) float ex[TL::WAVES * TL::WCOLS];
-            float* slot = ex + (threadIdx.x >> 6) * TL::WCOLS + (lane & 7) * C;
-            const size_t row = o0 + t * ostride;
-            if ((lane & 8) == 0) {
-                if constexpr (has_q(M)) {
-                    gfloat* orow = (gfloat*)(o + row);
-                    asm volatile("" : "+s"(orow));
-                    orow[col] = ov;
-                }
-                if (e_out != nullptr) {
-                    gfloat* erow = (gfloat*)(e_out + row);
-                    asm volatile("" : "+s"(erow));
-                    erow[col] = eo;
-                }
-                slot[kc] = eo;
-            }
-            __builtin_amdgcn_wave_barrier();   // one wave writes and reads the slots, in order
-            load_cols<C>(slot, e);
-        } else {
-            float ve[C];   // beta * v
-            load_cols<C>(sve + t * kD + j0, ve);
-#pragma unroll
-            for (int c = 0; c < C; ++c) {
-                u[c] = group_sum<TL::NI>(u[c]);
-                if constexpr (has_q(M)) w[c] = group_sum<TL::NI>(w[c]);
-            }
-            // e = beta v - beta u
-#pragma unroll
-            for (int c = 0; c < C; ++c) e[c] = fmaf(nbt, u[c], ve[c]);
-            if constexpr (has_q(M)) {
-                // finish w's butterfly on every lane: sunk into the writer's
-                // branch, its last DPP step would become mov 0, mov_dpp, add
-#pragma unroll
-                for (int c = 0; c < C; ++c) asm volatile("" : "+v"(w[c]));
-                float ov[C];
-#pragma unroll
-                for (int c = 0; c < C; ++c) ov[c] = fmaf(e[c], bq.y, w[c]);
-                if (ig == 0) store_cols<C>(o + (o0 + t * ostride) + j0, ov);
-            }
-            if (e_out != nullptr && ig == 0) store_cols<C>(e_out + (o0 + t * ostride) + j0, e);
-        }
-        // delta-rule write: S = S' + k e^T
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-#pragma unroll
-            for (int c = 0; c < C; ++c) s[r][c] = fmaf(kk[r], e[c], s[r][c]);
-        }
-        if constexpr (M == Rows::kFullCols) {
-            gfloat* col = cols + t * col_stride + (i0 * kD + j0);
-#pragma unroll
-            for (int r = 0; r < R; ++r) store_gcols<C, false>(col + r * kD, s[r]);
+    } else {
+        if (T <= 0) return;
+        RowKeys<true> xa, xb;
+        xa.template read<R, Q, TM>(L, 0, i0, n);
+#pragma unroll 1
+        for (int t = 0; t < T; t += 2) {
+            if (t + 1 < T) xb.template read<R, Q, TM>(L, t + 1, i0, n);
+            row_step<R, C, M, PLAIN, TM>(L, xa, s, t, o, e_out, o0, ostride, ig, i0, j0, cols,
+                                         col_stride);
+            if (t + 1 >= T) break;
+            if (t + 2 < T) xa.template read<R, Q, TM>(L, t + 2, i0, n);
+            row_step<R, C, M, PLAIN, TM>(L, xb, s, t + 1, o, e_out, o0, ostride, ig, i0, j0, cols,
+                                         col_stride);
         }
     }
 }
@@ -560,7 +838,9 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
 // kMaxPrev earlier rounds, oldest first, from the snapshot, then -- when
 // a.s_out is set -- that committed state is stored), then phase B (this
 // launch's rows).  Without FUSED the state after phase B is stored.
-template <int R, int C, bool BF16, Rows MA, Rows MB, bool TABLE, bool DUAL>
+// TAIL: the split tail of a whole-head launch, built within that launch's
+// register budget (no next-row prefetch).
+template <int R, int C, bool BF16, Rows MA, Rows MB, bool TABLE, bool DUAL, bool TAIL = false>
 __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1 : kTMax>* Ls,
                                            size_t chain, int blk) {
     using TL = Tile<R, C>;
@@ -574,9 +854,9 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
     // the swap layout serves the launches whose time is VALU-bound: the
     // whole-head verify scan and fused round (batched and state-column
     // launches measured faster with the plain layout)
-    constexpr bool SW = C == 4 && !TABLE && MB == Rows::kFull;
-    const int ig = SW ? (((lane >> 4) & 3) | ((lane >> 1) & 4)) : lane % TL::NI;
-    const int jg = SW ? (lane & 7) : lane / TL::NI;
+    constexpr bool PLAIN = plain_layout<C, MB, TABLE>();
+    const int ig = PLAIN ? (lane & 7) : (((lane >> 4) & 3) | ((lane >> 1) & 4));
+    const int jg = PLAIN ? (lane >> 3) : (lane & 7);
     const int i0 = ig * R;
     // --- this workgroup: column block blk of chain `chain`
     const int j0 = blk * TL::BCOLS + wave * TL::WCOLS + jg * C;
@@ -667,13 +947,13 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         load_state();
         if (replay) stage_fence<R, C, MA, kTMax>(inA);
         stage_fence<R, C, MB, kTMax>(inB);
-        if (replay) {
-            stage_commit<R, C, MA, kTMax>(L, inA, p.T, tid);
-            run_rows<R, C, MA, SW>(L, s, p.T, nullptr, nullptr, 0, 0, ig, i0, j0);
-        }
-        if (a.s_out) store_state();   // the committed state: this round's snapshot
+        // both phases' rows go to LDS while the state is still arriving, so
+        // the scan follows the replay and the snapshot store directly
+        if (replay) stage_commit<R, C, MA, kTMax>(L, inA, p.T, tid);
         stage_commit<R, C, MB, kTMax>(LB, inB, b.T, tid);
-        run_rows<R, C, MB, SW>(LB, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0);
+        if (replay) run_rows<R, C, MA, PLAIN, !TAIL>(L, s, p.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+        if (a.s_out) store_state();   // the committed state: this round's snapshot
+        run_rows<R, C, MB, PLAIN, !TAIL>(LB, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0);
         return;
     } else if constexpr (FUSED) {
         // With at most one stash replay, this launch's row loads go out
@@ -692,7 +972,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
                 stage_commit<R, C, MA, kTMax>(L, inA, p0.T, tid);
                 stage_issue<R, C, BF16, MB, kTMax>(inB, b, tid);
                 asm volatile("" ::: "memory");   // keep those loads ahead of the replay
-                run_rows<R, C, MA, SW>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+                run_rows<R, C, MA, PLAIN, !TAIL>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
             } else {
                 stage_issue<R, C, BF16, MB, kTMax>(inB, b, tid);
                 load_state();
@@ -704,12 +984,12 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         } else {
             const Src p0 = prev_src(0);
             stage<R, C, BF16, MA>(L, p0, tid, load_state);
-            run_rows<R, C, MA, SW>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+            run_rows<R, C, MA, PLAIN, !TAIL>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
             __syncthreads();   // every wave is done with these staged rows
             for (int i = 1; i < a.n_prev; ++i) {
                 const Src pi = prev_src(i);
                 stage<R, C, BF16, MA>(L, pi, tid, [] {});
-                run_rows<R, C, MA, SW>(L, s, pi.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+                run_rows<R, C, MA, PLAIN, !TAIL>(L, s, pi.T, nullptr, nullptr, 0, 0, ig, i0, j0);
                 __syncthreads();
             }
             if (a.s_out) store_state();   // the committed state: this round's snapshot
@@ -722,11 +1002,11 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
     if constexpr (MB == Rows::kFullCols) {
         // the last column is the state after all rows: no separate store
         static_assert(!FUSED && !TABLE, "state columns serve the plain scan");
-        run_rows<R, C, MB, SW>(L, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0,
+        run_rows<R, C, MB, PLAIN, !TAIL>(L, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0,
                            (gfloat*)a.s_cols + chain * kDD, a.col_stride);
         return;
     }
-    run_rows<R, C, MB, SW>(L, s, b.T, a.o, TABLE ? nullptr : a.e_out, o0, ostride, ig, i0, j0);
+    run_rows<R, C, MB, PLAIN, !TAIL>(L, s, b.T, a.o, TABLE ? nullptr : a.e_out, o0, ostride, ig, i0, j0);
     if constexpr (!FUSED) store_state();
 }
 
@@ -750,7 +1030,7 @@ kda_scan_kernel(ScanArgs a) {
         if (blockIdx.x >= head_blocks) {
             const unsigned long long t = blockIdx.x - head_blocks;
             constexpr int kSplit = Tile<R, TAILC>::BLOCKS;
-            scan_chain<R, TAILC, BF16, MA, MB, TABLE, DUAL>(
+            scan_chain<R, TAILC, BF16, MA, MB, TABLE, DUAL, true>(
                 a, Ls, static_cast<size_t>(a.n_head_chains + t / kSplit),
                 static_cast<int>(t % kSplit));
             return;
