@@ -83,6 +83,7 @@ def load():
     lib.kda_verify_round.argtypes = [p, p, p, p, p, p, p, i, i, p, p, p, p, p, p, p,
                                      i, i, i, i, p]
     lib.kda_accept_greedy.argtypes = [p, i, i, ctypes.c_longlong, i, p, p, p, p, p]
+    lib.kda_accept_greedy_noalloc.argtypes = [p, i, i, ctypes.c_longlong, i, p, p, p, p]
     lib.kda_conv_reroll.argtypes = [p, p, p, i, i, i, ctypes.c_longlong, i, p]
     lib.kda_conv_reroll_dev.argtypes = [p, p, p, i, i, p, ctypes.c_longlong, i, p]
     lib.kda_verify_round_dev.argtypes = [p, p, p, p, p, p, p, i, p, p, p, p, p, p, p, p,
@@ -95,7 +96,8 @@ def load():
                lib.kda_verify_round, lib.kda_accept_greedy, lib.kda_conv_reroll,
                lib.kda_copy_batch, lib.kda_row_ops, lib.kda_verify_round_multi,
                lib.kda_scan_rows_columns, lib.kda_verify_round_dev, lib.kda_conv_reroll_dev,
-               lib.kda_scan_rows_stash, lib.kda_replay_stash, lib.kda_abi_version):
+               lib.kda_scan_rows_stash, lib.kda_replay_stash, lib.kda_accept_greedy_noalloc,
+               lib.kda_abi_version):
         fn.restype = i
     lib.kda_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -434,15 +436,7 @@ def _u32(t, n, name):
     _shape(t, (n,), name)
 
 
-def kda_accept_greedy(logits, drafts, vam, out2, work, stream=None) -> None:
-    """Greedy accept: vam[r] = argmax of logits row r (lowest index on ties,
-    NO_TOKEN for a row holding a NaN), out2 = (j, bonus) with j the number of
-    leading drafts equal to vam and bonus = vam[j].
-
-    logits: [t][V] float32 or bfloat16, unit element stride (any row stride).
-    drafts: [t-1] token ids (None allowed when t == 1).
-    """
-    lib = load()
+def _accept_args(logits, drafts, vam, out2):
     if not isinstance(logits, torch.Tensor) or logits.dim() != 2:
         raise ValueError("logits must be a [t][V] tensor")
     if not logits.is_cuda:
@@ -461,12 +455,33 @@ def kda_accept_greedy(logits, drafts, vam, out2, work, stream=None) -> None:
         _u32(drafts, max(t - 1, 0), "drafts")
     _u32(vam, t, "vam")
     _u32(out2, 2, "out2")
-    if work.dtype != torch.uint8 or work.numel() < ACCEPT_WORK_BYTES:
-        raise ValueError(f"work must be a uint8 tensor of >= {ACCEPT_WORK_BYTES} bytes")
     lp = ctypes.c_void_p(logits.data_ptr())
     dp = _dev(drafts, "drafts") if drafts is not None and t > 1 else None
-    _check(lib.kda_accept_greedy(lp, int(t), int(V), int(ld), dt, dp, _dev(vam, "vam"),
-                                 _dev(out2, "out2"), _dev(work, "work"), _stream(stream)))
+    return lp, int(t), int(V), int(ld), dt, dp, _dev(vam, "vam"), _dev(out2, "out2")
+
+
+def kda_accept_greedy_noalloc(logits, drafts, vam, out2, stream=None) -> None:
+    """kda_accept_greedy without a workspace: the partial argmaxes go to the
+    library's static device array (one per GPU, shared by every call on it, so
+    calls that may overlap on one GPU must not use this form)."""
+    lib = load()
+    _check(lib.kda_accept_greedy_noalloc(*_accept_args(logits, drafts, vam, out2),
+                                         _stream(stream)))
+
+
+def kda_accept_greedy(logits, drafts, vam, out2, work, stream=None) -> None:
+    """Greedy accept: vam[r] = argmax of logits row r (lowest index on ties,
+    NO_TOKEN for a row holding a NaN), out2 = (j, bonus) with j the number of
+    leading drafts equal to vam and bonus = vam[j].
+
+    logits: [t][V] float32 or bfloat16, unit element stride (any row stride).
+    drafts: [t-1] token ids (None allowed when t == 1).
+    """
+    lib = load()
+    args = _accept_args(logits, drafts, vam, out2)
+    if work.dtype != torch.uint8 or work.numel() < ACCEPT_WORK_BYTES:
+        raise ValueError(f"work must be a uint8 tensor of >= {ACCEPT_WORK_BYTES} bytes")
+    _check(lib.kda_accept_greedy(*args, _dev(work, "work"), _stream(stream)))
 
 
 def kda_row_ops(x, a, b, conv_w, ring_in, q, k, v, g, beta, ring_out=None, stream=None) -> None:
@@ -553,5 +568,5 @@ __all__ = [
     "kda_last_error", "kda_accept_greedy", "accept_workspace", "ACCEPT_WORK_BYTES", "NO_TOKEN",
     "kda_conv_reroll", "copy_table", "kda_copy_batch", "RING_ROWS", "kda_row_ops",
     "kda_verify_round_multi", "MAX_PREV_ROUNDS", "kda_scan_rows_columns", "kda_scan_rows_stash",
-    "kda_replay_stash",
+    "kda_replay_stash", "kda_accept_greedy_noalloc",
 ]

@@ -308,6 +308,10 @@ int replay(const char* fn, const float* snap, float* s_out, const void* q, const
                                          static_cast<hipStream_t>(stream)));
 }
 
+int accept_greedy(const char* fn, const void* logits, int t, int V, long long ld, int in_dtype,
+                  const uint32_t* drafts, uint32_t* vam, uint32_t* out2, void* work, void* stream,
+                  bool static_work = false);
+
 }  // namespace
 
 extern "C" {
@@ -473,7 +477,36 @@ int kda_verify_round_multi(const float* snap_base, float* snap_out, const kda_pr
 int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dtype,
                       const uint32_t* drafts, uint32_t* vam, uint32_t* out2, void* work,
                       void* stream) {
-    const char* fn = "kda_accept_greedy";
+    return accept_greedy("kda_accept_greedy", logits, t, V, ld, in_dtype, drafts, vam, out2, work,
+                         stream);
+}
+
+int kda_accept_greedy_noalloc(const void* logits, int t, int V, long long ld, int in_dtype,
+                              const uint32_t* drafts, uint32_t* vam, uint32_t* out2,
+                              void* stream) {
+    const char* fn = "kda_accept_greedy_noalloc";
+    if (t < 1 || t > KDA_T_MAX)
+        return refuse(KDA_ERR_RANGE,
+                      "%s: t=%d outside 1..%d (the static scratch holds partial argmaxes for "
+                      "at most %d rows)",
+                      fn, t, KDA_T_MAX, KDA_T_MAX);
+    kda::AcceptScratch* ws = nullptr;
+    const hipError_t e = kda::accept_static_scratch(&ws);
+    if (e != hipSuccess)
+        return refuse(KDA_ERR_HIP, "%s: no static scratch on the current device: %s", fn,
+                      hipGetErrorString(e));
+    return accept_greedy(fn, logits, t, V, ld, in_dtype, drafts, vam, out2, ws, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// kda_accept_greedy and its variant on the static scratch (static_work: the
+// workspace is the library's own, so it is not checked as a caller buffer).
+int accept_greedy(const char* fn, const void* logits, int t, int V, long long ld, int in_dtype,
+                  const uint32_t* drafts, uint32_t* vam, uint32_t* out2, void* work, void* stream,
+                  bool static_work) {
     int rc;
     if ((rc = check_dtype(fn, in_dtype)) || (rc = check_rows(fn, "t", t))) return rc;
     if (V < 1) return refuse(KDA_ERR_RANGE, "%s: V=%d, need V >= 1", fn, V);
@@ -491,8 +524,9 @@ int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dty
         {"out2", out2, 8, 4, false},
         {"work", work, KDA_ACCEPT_WORK_BYTES, 16, false},
     };
-    if ((rc = check_spans(fn, in, 2)) || (rc = check_spans(fn, out, 3)) ||
-        (rc = check_alias(fn, out, 3, in, 2)))
+    const int n_out = static_work ? 2 : 3;
+    if ((rc = check_spans(fn, in, 2)) || (rc = check_spans(fn, out, n_out)) ||
+        (rc = check_alias(fn, out, n_out, in, 2)))
         return rc;
     auto* ws = static_cast<kda::AcceptScratch*>(work);
     kda::AcceptArgs a{};
@@ -502,6 +536,10 @@ int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dty
     return launched(fn, kda::launch_accept(a, in_dtype == KDA_IN_BF16,
                                            static_cast<hipStream_t>(stream)));
 }
+
+}  // namespace
+
+extern "C" {
 
 int kda_row_ops(const void* x, const void* a, const void* b, const float* conv_w,
                 const float* ring_in, float* ring_out, float* q, float* k, float* v, float* g,

@@ -65,6 +65,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "kda_launch.h"
@@ -1574,6 +1575,40 @@ hipError_t launch_dtype(const ScanArgs& a, Launch kind, hipStream_t stream) {
 
 hipError_t launch_scan(const ScanArgs& a, Launch kind, bool bf16, hipStream_t stream) {
     return bf16 ? launch_dtype<true>(a, kind, stream) : launch_dtype<false>(a, kind, stream);
+}
+
+// ------------------------------------------------------------------ accept scratch, no allocation
+//
+// The greedy accept's partial argmaxes for callers that cannot allocate: one
+// file-scope device array per GPU, sized for the largest table any call needs
+// (kTMax rows x kAcceptPMax partials, 11.25 KiB).  Its device address is
+// looked up once per device with that device current and kept; host code
+// passes that address to the kernels, never the array's name, which on the
+// host is only a stand-in.  Every call on one device shares the array, so
+// calls that overlap on a device race.  Nothing in it needs clearing: a call
+// reads only the slots it has written.
+static __device__ __align__(256) AcceptScratch scratch;
+
+namespace {
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+AcceptScratch* g_scratch[kScratchDevices];
+}  // namespace
+
+hipError_t accept_static_scratch(AcceptScratch** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kScratchDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = static_cast<AcceptScratch*>(p);
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
 }
 
 int accept_workgroups_per_row(int V) {

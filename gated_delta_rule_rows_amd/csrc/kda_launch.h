@@ -146,4 +146,8 @@ struct AcceptArgs {
 int accept_workgroups_per_row(int V);
 hipError_t launch_accept(const AcceptArgs& a, bool bf16, hipStream_t stream);
 
+// The calling thread's current device's static accept scratch (device
+// address), looked up on the first call for that device.
+hipError_t accept_static_scratch(AcceptScratch** out);
+
 }  // namespace kda

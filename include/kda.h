@@ -52,7 +52,7 @@ extern "C" {
 #define KDA_HEAD_DIM 128   /* d_k = d_v; glm5_spec_ppn_gate.rs fixture head_dim */
 #define KDA_T_MAX 15       /* verify rows per round: K + 1 <= 15 (glm_spec.rs, WALK-REUSE) */
 #define KDA_B_MAX 15       /* batched-decode sessions per step (same knee) */
-#define KDA_ABI_VERSION 9
+#define KDA_ABI_VERSION 10
 #define KDA_ACCEPT_WORK_BYTES 12288   /* workspace of kda_accept_greedy */
 #define KDA_NO_TOKEN 0xFFFFFFFFu      /* argmax slot of a logits row holding a NaN */
 #define KDA_CONV_RING_ROWS 3          /* short-conv history: kernel size 4 keeps 3 raw rows */
@@ -292,6 +292,23 @@ int kda_verify_round_multi(const float* snap_base, float* snap_out, const kda_pr
 int kda_accept_greedy(const void* logits, int t, int V, long long ld, int in_dtype,
                       const uint32_t* drafts, uint32_t* vam, uint32_t* out2, void* work,
                       void* stream);
+
+/*
+ * kda_accept_greedy with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid allocation, harnesses without an allocator).  The per-row partial
+ * argmaxes go to a static device array inside the library, one per GPU,
+ * sized for the largest call (KDA_T_MAX rows); its address is looked up on
+ * the first call on each device.  The call itself allocates and frees
+ * nothing.  Every call on one GPU shares that GPU's array: calls that can
+ * overlap on one GPU (different streams, different host threads) race and
+ * must use kda_accept_greedy with their own workspaces instead.  Arguments,
+ * results and refusals are those of kda_accept_greedy; t outside
+ * 1..KDA_T_MAX is refused as beyond the static array.
+ */
+int kda_accept_greedy_noalloc(const void* logits, int t, int V, long long ld, int in_dtype,
+                              const uint32_t* drafts, uint32_t* vam, uint32_t* out2,
+                              void* stream);
 
 /*
  * Pre-scan row ops: one layer-set's projections to scan inputs, all t rows.

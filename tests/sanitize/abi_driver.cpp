@@ -53,6 +53,12 @@ hipError_t launch_accept(const AcceptArgs& a, bool, hipStream_t) {
     ++g_launches; g_accept = a;
     return hipSuccess;
 }
+AcceptScratch g_static_scratch;   // stands in for the library's device array
+float* kda_static_probe() { return g_static_scratch.pv; }
+hipError_t accept_static_scratch(AcceptScratch** out) {
+    *out = &g_static_scratch;
+    return hipSuccess;
+}
 }  // namespace kda
 
 extern "C" const char* hipGetErrorString(hipError_t) { return "stub"; }
@@ -131,6 +137,13 @@ int main() {
                             (uint32_t*)out2, work, nullptr) == KDA_OK, "accept");
     CHECK(g_accept.t == 3 && (char*)g_accept.pv >= work &&
           (char*)(g_accept.pn + 15 * 64) <= work + KDA_ACCEPT_WORK_BYTES, "accept workspace");
+    CHECK(kda_accept_greedy_noalloc(lg, 3, 1000, 1000, KDA_IN_F32, (const uint32_t*)q,
+                                    (uint32_t*)vam, (uint32_t*)out2, nullptr) == KDA_OK,
+          "accept noalloc");
+    CHECK(g_accept.pv == kda::kda_static_probe(), "accept noalloc uses the static scratch");
+    CHECK(kda_accept_greedy_noalloc(lg, 16, 1000, 1000, KDA_IN_F32, (const uint32_t*)q,
+                                    (uint32_t*)vam, (uint32_t*)out2, nullptr) == KDA_ERR_RANGE &&
+          std::strstr(kda_last_error(), "static scratch") != nullptr, "accept noalloc t=16");
     const long long C = 3ll * H * 128;
     char *ring = buf(4ull * L * 3 * C), *ring2 = buf(4ull * L * 3 * C), *raw = buf(4ull * L * T * C);
     CHECK(kda_conv_reroll((float*)ring, raw, (float*)ring2, L, T, 6, C, KDA_IN_F32, nullptr) == KDA_OK,
