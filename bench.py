@@ -363,6 +363,82 @@ def _headline_rows(rows, key_id, warmup, steps):
     return sel[warmup:warmup + steps]
 
 
+def _valu_rows(d: str, keep=None):
+    """Per-kernel means of the two SQ passes under d: {label: dict}."""
+    import numpy as np
+    agg, dur = {}, {}
+    for part in ("a", "b"):
+        for r in _csv(_one(os.path.join(d, f"valu_{part}", "**", "*counter_collection.csv"))):
+            k = kernel_label(r["Kernel_Name"])
+            if not k or (keep is not None and k not in keep):
+                continue
+            if keep is None and (k in ("copy", "fill", "copy_batch", "conv_reroll") or "accept" in k):
+                continue
+            c = r["Counter_Name"] + ("_" + part if r["Counter_Name"] == "GRBM_GUI_ACTIVE" else "")
+            agg.setdefault(k, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and part == "a":
+                dur.setdefault(k, []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = {}
+    for k in agg:
+        if k not in dur:
+            continue
+        m = {c: float(np.mean(x)) for c, x in agg[k].items()}
+        us = float(np.mean(dur[k]))
+        cyc = m["GRBM_GUI_ACTIVE_a"] / 8
+        waves = m["SQ_WAVES"]
+        out[k] = {
+            "dispatches": len(dur[k]), "us": us, "ghz": cyc / us / 1e3, "waves": waves,
+            "valu_per_wave": m["SQ_INSTS_VALU"] / waves,
+            "valu_vs_peak": m["SQ_INSTS_VALU"] * 4 / (1024 * 2.4e3 * us),
+            "valu_active": m["SQ_ACTIVE_INST_VALU"] * 4 / (cyc * 1024),
+            "lds_per_wave": m["SQ_INSTS_LDS"] / waves,
+            "lds_active": m["SQ_ACTIVE_INST_LDS"] * 4 / (cyc * 1024),
+            "wait": m["SQ_WAIT_INST_ANY"] / max(m["SQ_WAVE_CYCLES"], 1),
+            "bank": m["SQ_LDS_BANK_CONFLICT"] / 256 / cyc,
+            "vmem_per_wave": m["SQ_INSTS_VMEM"] / waves,
+        }
+    return out
+
+
+VALU_HEAD = ("| kernel | dispatches | mean us | clock GHz | waves | VALU ops/wave | VALU vs peak | "
+             "VALU active | LDS ops/wave | LDS active | wait | LDS bank conflict | VMEM ops/wave |"
+             "\n|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+
+
+def _valu_line(k, v):
+    return (f"| {k} | {v['dispatches']} | {v['us']:.1f} | {v['ghz']:.2f} | {v['waves']:.0f} | "
+            f"{v['valu_per_wave']:.0f} | {v['valu_vs_peak']:.2f} | {v['valu_active']:.2f} | "
+            f"{v['lds_per_wave']:.0f} | {v['lds_active']:.2f} | {v['wait']:.2f} | "
+            f"{v['bank']:.3f} | {v['vmem_per_wave']:.0f} |\n")
+
+
+def layer_counters(before: str, after: str, before_sha: str) -> None:
+    """profiles/one_layer_round_counters.md: the one-layer fused launch (64
+    heads, 4 workgroups per head) under the SQ passes of two kernel sources."""
+    after_sha = _last_json(os.path.join(after, "valu_a.log"))["config"]["kernel_source_sha256_16"]
+    keep = {"round_stash_c1_dual", "round_stash_c2", "round_stash"}
+    with open(os.path.join(ROOT, "profiles", "one_layer_round_counters.md"), "w") as f:
+        f.write("# SQ counters: the one-layer fused round (1 layer x 64 heads, T=15, keep_prev 8, "
+                "f32), one MI355X\n\nThe kernel of the per-layer HIP graph round "
+                "(`round_stash_c1_dual`: 4 workgroups per head, one wave per SIMD), before and "
+                "after the quad key broadcast and the reordered staging; the 34-layer fused round "
+                "(`round_stash`) and the TP=8 share's tiling (`round_stash_c2`) beside them.  "
+                "Commands: the two `valu_*` runs of `PROF_RUNS` in bench.py, for each source.  "
+                "Reduced by `python bench.py --layer-counters BEFORE AFTER SHA`.\n\n"
+                "wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; the other columns as in "
+                "verify_k14_valu.md.  Dispatches of a few us have a counter window wider than the "
+                "dispatch, so their clock reads high and their cycle fractions low; compare the "
+                "two sources with each other.\n\n")
+        for title, d, sha in (("Before", before, before_sha), ("After", after, after_sha)):
+            rows = _valu_rows(d, keep)
+            f.write(f"## {title}: kernel source sha256[:16] `{sha}`\n\n" + VALU_HEAD)
+            for k in ("round_stash_c1_dual", "round_stash_c2", "round_stash"):
+                if k in rows:
+                    f.write(_valu_line(k, rows[k]))
+            f.write("\n")
+
+
 def profile_summary(d: str) -> None:
     import numpy as np
 
@@ -506,17 +582,7 @@ def profile_summary(d: str) -> None:
     # ---- VALU load (two SQ passes), if they were taken
     if not os.path.isdir(os.path.join(d, "valu_a")):
         return
-    agg, dur = {}, {}
-    for part in ("a", "b"):
-        for r in _csv(_one(os.path.join(d, f"valu_{part}", "**", "*counter_collection.csv"))):
-            k = kernel_label(r["Kernel_Name"])
-            if not k or k in ("copy", "fill", "copy_batch", "conv_reroll") or "accept" in k:
-                continue
-            c = r["Counter_Name"] + ("_" + part if r["Counter_Name"] == "GRBM_GUI_ACTIVE" else "")
-            agg.setdefault(k, {}).setdefault(c, []).append(float(r["Counter_Value"]))
-            if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and part == "a":
-                dur.setdefault(k, []).append(
-                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    rows = _valu_rows(d)
     with open(os.path.join(out, "verify_k14_valu.md"), "w") as f:
         f.write("# VALU load of the scan kernels: verify_k14 shapes (34 layers x 64 heads, "
                 "T=15, f32), one MI355X\n\nCommands (from the repository root, after `cd /tmp "
@@ -532,28 +598,12 @@ def profile_summary(d: str) -> None:
                 "- LDS active = SQ_ACTIVE_INST_LDS x 4 / (1,024 SIMDs x cycles);\n"
                 "- wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES: the share of wave cycles spent "
                 "waiting on a memory counter;\n"
-                "- LDS bank conflicts = SQ_LDS_BANK_CONFLICT / 256 CUs / cycles.\n\n")
-        f.write("| kernel | dispatches | mean us | clock GHz | waves | VALU ops/wave | VALU vs "
-                "peak | VALU active | LDS ops/wave | LDS active | wait | LDS bank conflict | "
-                "VMEM ops/wave |\n|---|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+                "- LDS bank conflicts = SQ_LDS_BANK_CONFLICT / 256 CUs / cycles.\n\n" + VALU_HEAD)
         order = ["round_stash", "round_recompute", "scan", "replay", "round_stash_c1_dual",
                  "round_stash_c2", "round_stash_c2_dual", "batched", "scan_columns", "row_ops"]
-        for k in order + sorted(set(agg) - set(order)):
-            if k not in agg or k not in dur:
-                continue
-            m = {c: float(np.mean(x)) for c, x in agg[k].items()}
-            us = float(np.mean(dur[k]))
-            cyc = m["GRBM_GUI_ACTIVE_a"] / 8
-            waves = m["SQ_WAVES"]
-            f.write(f"| {k} | {len(dur[k])} | {us:.1f} | {cyc / us / 1e3:.2f} | {waves:.0f} | "
-                    f"{m['SQ_INSTS_VALU'] / waves:.0f} | "
-                    f"{m['SQ_INSTS_VALU'] * 4 / (1024 * 2.4e3 * us):.2f} | "
-                    f"{m['SQ_ACTIVE_INST_VALU'] * 4 / (cyc * 1024):.2f} | "
-                    f"{m['SQ_INSTS_LDS'] / waves:.0f} | "
-                    f"{m['SQ_ACTIVE_INST_LDS'] * 4 / (cyc * 1024):.2f} | "
-                    f"{m['SQ_WAIT_INST_ANY'] / max(m['SQ_WAVE_CYCLES'], 1):.2f} | "
-                    f"{m['SQ_LDS_BANK_CONFLICT'] / 256 / cyc:.3f} | "
-                    f"{m['SQ_INSTS_VMEM'] / waves:.0f} |\n")
+        for k in order + sorted(set(rows) - set(order)):
+            if k in rows:
+                f.write(_valu_line(k, rows[k]))
         f.write("\nA whole-head wave's scan row does 4 VALU ops per state element (decay "
                 "multiply, u, w and update FMAs; 64 elements per lane, 256 per row) and a stash "
                 "replay row does 2 (128 per row).\n")
@@ -588,9 +638,15 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="write profiles/ from the rocprofv3 runs under DIR and exit (no GPU)")
+    ap.add_argument("--layer-counters", nargs=3, metavar=("BEFORE", "AFTER", "BEFORE_SHA"),
+                    help="write profiles/one_layer_round_counters.md from the SQ passes of two "
+                         "kernel sources and exit (no GPU)")
     args = ap.parse_args()
     if args.profile_summary:
         profile_summary(args.profile_summary)
+        return 0
+    if args.layer_counters:
+        layer_counters(*args.layer_counters)
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
