@@ -479,7 +479,8 @@ def profile_summary(d: str) -> None:
         f.write("## The headline launches\n\n")
         f.write(f"The {len(head)} timed rounds of the traced run (dispatches "
                 f"{kt_line['warmup'] + 1}..{kt_line['warmup'] + len(head)} of the fused-round "
-                f"kernel; each follows a 512 MiB flush), with keep_prev drawn as the bench "
+                f"kernel; each follows a 512 MiB flush: written, then read back), with "
+                f"keep_prev drawn as the bench "
                 f"draws it (mean {np.mean(keeps):.2f}):\n\n")
         f.write("| | mean us | p10 | p50 | p90 |\n|---|---|---|---|---|\n")
         f.write(f"| kernel time (rocprofv3 trace) | {k_mean:.1f} | {np.percentile(head_us, 10):.1f} "
@@ -491,6 +492,10 @@ def profile_summary(d: str) -> None:
             pu = plain["round_us"]
             f.write(f"| events, plain run (no tracer) | {pu['mean']:.1f} | {pu['p10']:.1f} | "
                     f"{pu['p50']:.1f} | {pu['p90']:.1f} |\n")
+        if "each" in ru and len(ru["each"]) == len(head_us):
+            gap = np.asarray(ru["each"]) - np.asarray(head_us)
+            f.write(f"\nEvents minus kernel time, launch by launch in the traced run: median "
+                    f"{np.median(gap):.1f} us, min {gap.min():.1f}, max {gap.max():.1f}.\n")
         f.write(f"\nAlgorithmic bytes per launch (mean over these rounds): "
                 f"{np.mean(alg_bytes) / 1e6:.1f} MB, so {np.mean(alg_bytes) / (k_mean * 1e-6) / 1e9:.0f}"
                 f" GB/s by kernel time ({np.mean(alg_bytes) / (k_mean * 1e-6) / 1e9 / PEAK_HBM_GBPS:.3f}"
@@ -511,7 +516,8 @@ def profile_summary(d: str) -> None:
                 "round); `_c1`, `_c2` = 4 or 2 workgroups per head, `_dual` = both phases staged "
                 "up front (the one-layer launches); `scan` = kda_scan_rows (T=15); `replay` = "
                 "kda_replay (T=keep); `copy` = kda_snapshot's copy; `fill` = torch's zero_() "
-                "of the flush buffer and of state buffers.\n")
+                "of the flush buffer and of state buffers; torch's `reduce_kernel` is the "
+                "flush's read pass.\n")
 
     # ---- HBM traffic: FETCH_SIZE and WRITE_SIZE, calibrated on the plain copy
     cnt = {}
@@ -736,19 +742,34 @@ def main() -> int:
         pair[0], pair[1] = nxt, snap
         return keep_prev
 
-    # the MALL flush: a write of 512 MiB (twice the 256 MB Infinity Cache)
-    # before every timed launch, outside its events, as the rest of a model's
-    # layers evict the state between one round's scan and the next
+    # the MALL flush before every timed launch, outside its events, as the rest
+    # of a model's layers evict the state between one round's scan and the
+    # next: 512 MiB written (twice the 256 MB Infinity Cache), then read back.
+    # The read pass makes the cache write back the lines the write pass left
+    # dirty before the launch starts; without it, up to 256 MB of those
+    # write-backs land inside the timed launch (reported separately below).
     flush = torch.empty(512 << 18, dtype=torch.float32, device="cuda")
+    flush_sink = torch.zeros(1, dtype=torch.float32, device="cuda")
 
-    def cold(step_fn, first, n_steps):
+    def flush_mall(write_only=False):
+        flush.zero_()
+        if not write_only:
+            flush_sink.add_(flush.sum())
+
+    def cold(step_fn, first, n_steps, write_only=False):
         """n_steps steps, each launch MALL-cold between its own pair of events.
         Returns (per-launch us, step infos)."""
         marks = [(ev(), ev()) for _ in range(n_steps)]
         info = []
+        # one untimed flush and event pair first: the first of each in a
+        # process measured ~180 us late
+        p0, p1 = ev(), ev()
+        flush_mall(write_only)
+        p0.record(stream)
+        p1.record(stream)
         torch.cuda.synchronize()
         for s in range(n_steps):
-            flush.zero_()
+            flush_mall(write_only)
             info.append(step_fn(first + s, marks[s]))
         torch.cuda.synchronize()
         return [m0.elapsed_time(m1) * 1e3 for m0, m1 in marks], info
@@ -785,11 +806,18 @@ def main() -> int:
             "rows_heads_per_s": args.steps * T * H * L / (w_ms * 1e-3),
             "hbm_gbps": sum(chains * round_bytes_per_head(kp, T) for kp in winfo)
             / (w_ms * 1e-3) / 1e9,
-            "note": "K rounds back to back between two events, no flush (the state of one "
-                    "round is still partly in the MALL when the next starts)"}
+            "note": "K rounds back to back between two events, no flush: each round starts "
+                    "with the previous round's writes (snapshot, o, e) in the Infinity Cache, "
+                    "and its loads share HBM with their write-back"}
     fm, _, _, _ = timed(fused_round, 0, args.steps, 2, first=args.warmup + 2 * args.steps)
     warm["round_us"] = stats_us([fm[s][0].elapsed_time(fm[s][1]) * 1e3
                                  for s in range(args.steps)])
+    # secondary: the same protocol with the write pass alone
+    wo_us, _ = cold(fused_round, args.warmup + 3 * args.steps, args.steps, write_only=True)
+    write_only_flush = {
+        "round_us": stats_us(wo_us),
+        "note": "each launch after the 512 MiB write pass alone: the write-back of the "
+                "dirty lines it leaves in the Infinity Cache happens inside the launch"}
 
     # ---------------- split pipeline: scan, then replay when j < 14
     split = None
@@ -810,7 +838,7 @@ def main() -> int:
             replayed = keep < T
             if replayed:
                 if m is not None:
-                    flush.zero_()
+                    flush_mall()
                     m[2].record(stream)
                 kda.kda_replay(snap, live, *rows, keep=keep)
                 if m is not None:
@@ -824,7 +852,7 @@ def main() -> int:
         sinfo = []
         torch.cuda.synchronize()
         for s_ in range(args.steps):
-            flush.zero_()
+            flush_mall()
             sinfo.append(split_round(args.warmup + s_, sm[s_]))
         torch.cuda.synchronize()
         scan_us = [sm[s_][0].elapsed_time(sm[s_][1]) * 1e3 for s_ in range(args.steps)]
@@ -934,7 +962,7 @@ def main() -> int:
         # a flush; then warm, back to back between two events
         marks = [(ev(), ev()) for _ in range(args.per_layer_rounds)]
         for m0, m1 in marks:
-            flush.zero_()
+            flush_mall()
             m0.record(stream)
             graph.replay()
             m1.record(stream)
@@ -1342,11 +1370,12 @@ def main() -> int:
                                 "algorithmic bytes (scan of T rows, replay of the kept rows when "
                                 "keep < T), which the fused kernel does not move"}},
         },
-        "round_us": stats_us(f_us),
-        "round_us_note": "the headline: each timed round's launch MALL-cold (512 MiB written "
-                         "before it, outside its events) between its own pair of events; "
-                         "ms_per_step is the median",
+        "round_us": dict(stats_us(f_us), each=[round(x, 2) for x in f_us]),
+        "round_us_note": "the headline: each timed round's launch MALL-cold (512 MiB written, "
+                         "then read back, before it and outside its events) between its own "
+                         "pair of events; ms_per_step is the median",
         "warm": warm,
+        "write_only_flush": write_only_flush,
         "committed_rows_heads_per_s": committed * H * L / (sum(f_us) * 1e-6),
         "split": split,
         "state_columns": columns,
