@@ -422,7 +422,8 @@ def layer_counters(before: str, after: str, before_sha: str) -> None:
         f.write("# SQ counters: the one-layer fused round (1 layer x 64 heads, T=15, keep_prev 8, "
                 "f32), one MI355X\n\nThe kernel of the per-layer HIP graph round "
                 "(`round_stash_c1_dual`: 4 workgroups per head, one wave per SIMD), before and "
-                "after the quad key broadcast and the reordered staging; the 34-layer fused round "
+                "after the quad key broadcast, the reordered staging and the next row's key reads "
+                "issued at the start of each row; the 34-layer fused round "
                 "(`round_stash`) and the TP=8 share's tiling (`round_stash_c2`) beside them.  "
                 "Commands: the two `valu_*` runs of `PROF_RUNS` in bench.py, for each source.  "
                 "Reduced by `python bench.py --layer-counters BEFORE AFTER SHA`.\n\n"

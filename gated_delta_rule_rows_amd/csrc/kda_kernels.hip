@@ -662,22 +662,37 @@ constexpr bool plain_layout() {
 // at i0, its columns at j0 (ig: its key group, used by the plain layout).
 // kFullCols: `cols` addresses this chain's state in column 0, and row t's
 // state goes to cols + t * col_stride.
-template <int R, int C, Rows M, bool PLAIN, int TM, typename K>
+template <int R, int C, Rows M, bool PLAIN, int TM, bool PFK, typename K, typename F>
 __device__ __forceinline__ void row_step(const Stage<R, TM>& L, const K& x, float (&s)[R][C], int t,
                                          float* o, float* e_out, size_t o0, size_t ostride,
-                                         int ig, int i0, int j0, gfloat* cols, size_t col_stride) {
+                                         int ig, int i0, int j0, gfloat* cols, size_t col_stride,
+                                         F&& next_keys) {
     const float* sve = reinterpret_cast<const float*>(L.ve);
     const int lane = threadIdx.x & 63;
     constexpr bool Q = has_q(M);
     if constexpr (M == Rows::kStash) {
         float e[C];
         load_cols<C>(sve + t * kD + j0, e);
+        if constexpr (PFK) {
+            next_keys();
+            asm volatile("" ::: "memory");   // issued ahead of the row's arithmetic
+        }
         if constexpr (C < 4) stash_rows<C>(x, s, e);
         else stash_rows_lds<C, false, R, TM>(L, t, i0, s, e);
         return;
     }
     const float2 bq = L.bq[t];
     const float nbt = -bq.x;
+    // With the next row's keys read during this row, this row's beta*v is
+    // read first: LDS reads return in order, so a read issued after those
+    // would wait for them too.
+    float ve1 = 0.0f;
+    if constexpr (PFK) {
+        static_assert(!PLAIN && C < 4, "the narrow tilings read keys ahead");
+        ve1 = sve[t * kD + j0 + (C == 2 ? ((lane >> 4) & 1) : 0)];
+        next_keys();
+        asm volatile("" ::: "memory");   // issued ahead of the row's arithmetic
+    }
     float u[C], w[C];
     decay_sums<C, Q>(x, s, u, w);
     float e[C];
@@ -745,7 +760,7 @@ __device__ __forceinline__ void row_step(const Stage<R, TM>& L, const K& x, floa
             // rows 0, 1 end with u of columns 0, 1; rows 2, 3 with w
             const float sums[4] = {u[0], u[1], w[0], w[1]};
             const float x4 = reduce_scatter4(sums);
-            ec = fmaf(nbt, x4, sve[t * kD + col]);   // valid in rows 0, 1
+            ec = fmaf(nbt, x4, PFK ? ve1 : sve[t * kD + col]);         // valid in rows 0, 1
             float e2 = ec;
             swap32(ec, e2);                          // rows 2, 3 take e from rows 0, 1
             const float ov = fmaf(ec, bq.y, x4);     // valid in rows 2, 3
@@ -755,7 +770,7 @@ __device__ __forceinline__ void row_step(const Stage<R, TM>& L, const K& x, floa
                 orow[col] = ov;
             }
         } else {
-            ec = fmaf(nbt, sum_groups2(u[0], u[1]), sve[t * kD + col]);
+            ec = fmaf(nbt, sum_groups2(u[0], u[1]), PFK ? ve1 : sve[t * kD + col]);
         }
         if (e_out != nullptr && (lane & 0x28) == 0) {
             gfloat* erow = (gfloat*)(e_out + row);
@@ -769,7 +784,7 @@ __device__ __forceinline__ void row_step(const Stage<R, TM>& L, const K& x, floa
         const size_t row = o0 + t * ostride;
         if constexpr (Q) {
             const float x2 = sum_groups2(u[0], w[0]);   // even rows u, odd rows w
-            float ec = fmaf(nbt, x2, sve[t * kD + col]); // valid in even rows
+            float ec = fmaf(nbt, x2, PFK ? ve1 : sve[t * kD + col]);       // valid in even rows
             float odd;
             gather_pair16(ec, odd);                     // ec: the even row's e, in all rows
             const float ov = fmaf(ec, bq.y, x2);        // valid in odd rows
@@ -780,7 +795,7 @@ __device__ __forceinline__ void row_step(const Stage<R, TM>& L, const K& x, floa
             }
             e[0] = ec;
         } else {
-            e[0] = fmaf(nbt, sum_groups(u[0]), sve[t * kD + col]);
+            e[0] = fmaf(nbt, sum_groups(u[0]), PFK ? ve1 : sve[t * kD + col]);
         }
         if (e_out != nullptr && (lane & 0x38) == 0) {
             gfloat* erow = (gfloat*)(e_out + row);
@@ -797,6 +812,10 @@ __device__ __forceinline__ void row_step(const Stage<R, TM>& L, const K& x, floa
     }
 }
 
+struct NoKeys {
+    __device__ void operator()() const {}
+};
+
 // T rows of one phase.  The whole-head tiling (several waves per SIMD hide
 // each other's latency) reads each row's keys when it starts it.  The narrow
 // tilings run one wave per SIMD, so each row's key reads are issued during the
@@ -810,27 +829,42 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
     constexpr bool DPP = C < 4;
     constexpr bool Q = has_q(M);
     const int n = threadIdx.x & 3;
+    if constexpr (!PLAIN) {
+        // the key group again from an opaque copy of the thread index: held
+        // from the launch's start instead, it spilled in one variant
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        ig = ((lane >> 4) & 3) | ((lane >> 1) & 4);
+        i0 = ig * R;
+    }
     if constexpr (!DPP || !PF) {
 #pragma unroll 1
         for (int t = 0; t < T; ++t) {
             RowKeys<DPP> x;   // a stash row reads its keys itself from LDS, four at a time
             if constexpr (M != Rows::kStash || DPP) x.template read<R, Q, TM>(L, t, i0, n);
-            row_step<R, C, M, PLAIN, TM>(L, x, s, t, o, e_out, o0, ostride, ig, i0, j0, cols,
-                                         col_stride);
+            row_step<R, C, M, PLAIN, TM, false>(L, x, s, t, o, e_out, o0, ostride, ig, i0, j0,
+                                                cols, col_stride, NoKeys{});
         }
     } else {
+        // The next row's keys go out at the start of each row, after that
+        // row's own reads; the last row reads its own keys again (a clamped
+        // index keeps the reads unconditional, which lets the compiler count
+        // them exactly instead of waiting on them at once).
         if (T <= 0) return;
         RowKeys<true> xa, xb;
         xa.template read<R, Q, TM>(L, 0, i0, n);
 #pragma unroll 1
         for (int t = 0; t < T; t += 2) {
-            if (t + 1 < T) xb.template read<R, Q, TM>(L, t + 1, i0, n);
-            row_step<R, C, M, PLAIN, TM>(L, xa, s, t, o, e_out, o0, ostride, ig, i0, j0, cols,
-                                         col_stride);
+            row_step<R, C, M, PLAIN, TM, true>(L, xa, s, t, o, e_out, o0, ostride, ig, i0, j0,
+                                               cols, col_stride, [&] {
+                xb.template read<R, Q, TM>(L, min(t + 1, T - 1), i0, n);
+            });
             if (t + 1 >= T) break;
-            if (t + 2 < T) xa.template read<R, Q, TM>(L, t + 2, i0, n);
-            row_step<R, C, M, PLAIN, TM>(L, xb, s, t + 1, o, e_out, o0, ostride, ig, i0, j0, cols,
-                                         col_stride);
+            row_step<R, C, M, PLAIN, TM, true>(L, xb, s, t + 1, o, e_out, o0, ostride, ig, i0,
+                                               j0, cols, col_stride, [&] {
+                xa.template read<R, Q, TM>(L, min(t + 2, T - 1), i0, n);
+            });
         }
     }
 }
