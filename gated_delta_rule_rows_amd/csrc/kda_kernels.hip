@@ -1045,6 +1045,26 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
     if constexpr (!FUSED) store_state();
 }
 
+// The B workgroups that split one head (C < 4) each read all of that head's
+// row inputs.  The hardware hands workgroup i to XCD i mod 8, each XCD with
+// its own L2, so the parts of a head get indices equal mod 8 (where the
+// range allows): index i -> head (i / 8 / B) * 8 + i mod 8, part (i / 8) mod B.
+// One XCD's L2 then serves the repeated row reads.  Any count of XCDs gives
+// a correct mapping; 8 is MI355X's.
+template <int B>
+__device__ __forceinline__ void split_index(unsigned long long i, unsigned long long n,
+                                            unsigned long long& head, int& part) {
+    constexpr unsigned long long kXcd = 8, kGroup = kXcd * B;
+    if (B > 1 && i < n - n % kGroup) {
+        const unsigned long long k = i / kXcd;
+        head = (k / B) * kXcd + i % kXcd;
+        part = static_cast<int>(k % B);
+    } else {
+        head = i / B;
+        part = static_cast<int>(i % B);
+    }
+}
+
 // DUAL: phase A and phase B rows each get an LDS area, so both are loaded up
 // front (one memory round trip fewer per launch, twice the LDS).
 // TAILC (0, 1 or 2): the chains past a.n_head_chains -- the last, sparse fill
@@ -1063,11 +1083,15 @@ kda_scan_kernel(ScanArgs a) {
         const unsigned long long head_blocks =
             static_cast<unsigned long long>(a.n_head_chains) * TL::BLOCKS;
         if (blockIdx.x >= head_blocks) {
-            const unsigned long long t = blockIdx.x - head_blocks;
+            // head_blocks is a multiple of the chip's 4 x CUs slots (1,024
+            // on MI355X), so there the tail index and the workgroup index
+            // agree mod 8
             constexpr int kSplit = Tile<R, TAILC>::BLOCKS;
+            unsigned long long head;
+            int part;
+            split_index<kSplit>(blockIdx.x - head_blocks, gridDim.x - head_blocks, head, part);
             scan_chain<R, TAILC, BF16, MA, MB, TABLE, DUAL, true>(
-                a, Ls, static_cast<size_t>(a.n_head_chains + t / kSplit),
-                static_cast<int>(t % kSplit));
+                a, Ls, static_cast<size_t>(a.n_head_chains + head), part);
             return;
         }
     }
@@ -1081,8 +1105,10 @@ kda_scan_kernel(ScanArgs a) {
         const unsigned long long entries = static_cast<unsigned long long>(a.n_chains) / h;
         bid = (bid / h) * a.entry_mul % entries * h + bid % h;
     }
-    scan_chain<R, C, BF16, MA, MB, TABLE, DUAL>(a, Ls, bid / TL::BLOCKS,
-                                                static_cast<int>(bid % TL::BLOCKS));
+    unsigned long long head;
+    int part;
+    split_index<TL::BLOCKS>(bid, gridDim.x, head, part);
+    scan_chain<R, C, BF16, MA, MB, TABLE, DUAL>(a, Ls, static_cast<size_t>(head), part);
 }
 
 // ------------------------------------------------------------------ copy
