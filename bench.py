@@ -440,12 +440,14 @@ def layer_counters(before: str, after: str, before_sha: str) -> None:
             f.write("\n")
 
 
-def profile_summary(d: str) -> None:
+def profile_summary(d: str, out: str = None) -> None:
+    """Reduce the rocprofv3 output of the PROF_RUNS under d (and the plain
+    run's bench.log) into the summaries under out (default: profiles/)."""
     import numpy as np
 
     from gated_delta_rule_rows_amd import synth
 
-    out = os.path.join(ROOT, "profiles")
+    out = out or os.path.join(ROOT, "profiles")
     # the kernel source the profiled runs executed, as their bench lines record it
     shas = {_last_json(os.path.join(d, f"{n}.log"))["config"].get("kernel_source_sha256_16")
             for n in PROF_RUNS if os.path.exists(os.path.join(d, f"{n}.log"))}
