@@ -55,7 +55,13 @@
 // and the state are in flight before the first wait; the fused round also
 // issues this round's row loads before its replay.  The batched arm walks its
 // table entries in a spread order, so that the workgroups in flight touch
-// sessions far apart in memory.
+// sessions far apart in memory.  The workgroups that split one head run on one
+// XCD (workgroup indices equal mod 8), whose L2 then serves their repeated
+// reads of the head's rows.
+//
+// No MFMA for the rank-1 write either: on gfx950 an f32 MFMA does not overlap
+// independent VALU work (their times add), and the 4x4x1 form costs about as
+// much as the four VALU FMAs it would replace.
 //
 // Beside the scan, all HBM- or latency-bound: the pre-scan row ops (short
 // conv, norms, gate, beta) that produce the scan's inputs; the conv-ring
