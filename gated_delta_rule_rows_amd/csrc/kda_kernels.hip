@@ -1084,14 +1084,14 @@ kda_scan_kernel(ScanArgs a) {
     using TL = Tile<R, C>;
     // the batched arm stages its one row: 2.4 KB of LDS instead of 36.6 KB
     __shared__ Stage<R, TABLE ? 1 : kTMax> Ls[DUAL ? 2 : 1];
+    unsigned long long head_blocks = gridDim.x;
     if constexpr (TAILC != 0) {
-        static_assert(C == 4 && !DUAL && !TABLE, "the tail split serves whole-head launches");
-        const unsigned long long head_blocks =
-            static_cast<unsigned long long>(a.n_head_chains) * TL::BLOCKS;
+        static_assert((C == 4 || (C == 2 && TAILC == 1)) && !DUAL && !TABLE,
+                      "a split tail follows whole heads, or half heads with 4-way parts");
+        head_blocks = static_cast<unsigned long long>(a.n_head_chains) * TL::BLOCKS;
         if (blockIdx.x >= head_blocks) {
-            // head_blocks is a multiple of the chip's 4 x CUs slots (1,024
-            // on MI355X), so there the tail index and the workgroup index
-            // agree mod 8
+            // head_blocks is a multiple of the CU count (256 on MI355X), so
+            // there the tail index and the workgroup index agree mod 8
             constexpr int kSplit = Tile<R, TAILC>::BLOCKS;
             unsigned long long head;
             int part;
@@ -1113,7 +1113,7 @@ kda_scan_kernel(ScanArgs a) {
     }
     unsigned long long head;
     int part;
-    split_index<TL::BLOCKS>(bid, gridDim.x, head, part);
+    split_index<TL::BLOCKS>(bid, head_blocks, head, part);
     scan_chain<R, C, BF16, MA, MB, TABLE, DUAL>(a, Ls, static_cast<size_t>(head), part);
 }
 
@@ -1549,14 +1549,16 @@ int chip_cus() {
     return cus;
 }
 
-template <int TAILC, bool BF16, Rows MA, Rows MB>
+// a.n_head_chains chains with CH value columns per lane, then `tail` chains
+// split TAILC-wide (2 or 4 workgroups each), in one launch
+template <int CH, int TAILC, bool BF16, Rows MA, Rows MB>
 hipError_t launch_split_tail(const ScanArgs& a, long long tail, hipStream_t stream) {
-    using TL = Tile<kKeysPerLane, 4>;
-    const unsigned long long tb = static_cast<unsigned long long>(a.n_head_chains) +
+    using TL = Tile<kKeysPerLane, CH>;
+    const unsigned long long tb = static_cast<unsigned long long>(a.n_head_chains) * TL::BLOCKS +
                                   static_cast<unsigned long long>(tail) *
                                       Tile<kKeysPerLane, TAILC>::BLOCKS;
     if (tb > 0x7FFFFFFFull) return hipErrorInvalidValue;
-    kda_scan_kernel<kKeysPerLane, 4, BF16, MA, MB, false, false, TAILC>
+    kda_scan_kernel<kKeysPerLane, CH, BF16, MA, MB, false, false, TAILC>
         <<<dim3(static_cast<unsigned>(tb)), dim3(TL::THREADS), 0, stream>>>(a);
     return hipGetLastError();
 }
@@ -1598,8 +1600,21 @@ hipError_t launch_tiled(const ScanArgs& a0, hipStream_t stream) {
         const long long tail = a.n_chains % slots;
         if (a.n_chains > slots && tail > 0 && tail <= cus / 2) {
             a.n_head_chains = a.n_chains - tail;
-            return tail <= cus / 4 ? launch_split_tail<1, BF16, MA, MB>(a, tail, stream)
-                                   : launch_split_tail<2, BF16, MA, MB>(a, tail, stream);
+            return tail <= cus / 4 ? launch_split_tail<4, 1, BF16, MA, MB>(a, tail, stream)
+                                   : launch_split_tail<4, 2, BF16, MA, MB>(a, tail, stream);
+        }
+    }
+    if constexpr (C == 2 && !TABLE) {
+        // Half heads past one chain per CU: with up to CUs/4 chains more,
+        // those split 4 ways, one quarter-head workgroup per CU at most, so
+        // no CU runs three half heads.  The TP=8 share (272 chains) measured
+        // 27.3 -> 25.2 us; a larger tail put two quarter heads on some CUs
+        // and was slower.
+        const long long cus = chip_cus();
+        const long long tail = a.n_chains - cus;
+        if (tail > 0 && tail <= cus / 4) {
+            a.n_head_chains = cus;
+            return launch_split_tail<2, 1, BF16, MA, MB>(a, tail, stream);
         }
     }
     kda_scan_kernel<kKeysPerLane, C, BF16, MA, MB, TABLE, false, 0>

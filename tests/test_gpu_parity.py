@@ -546,10 +546,13 @@ def _per_layers(fn, L, chunk):
     return [fn(l0, min(l0 + chunk, L)) for l0 in range(0, L, chunk)]
 
 
-@pytest.mark.parametrize("chunk,bf16,L", [(1, False, 34), (4, False, 34), (8, False, 34),
-                                          (1, True, 34), (4, True, 34), (1, False, 17),
-                                          (8, False, 24), (17, False, 68)])
-def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L):
+@pytest.mark.parametrize("chunk,bf16,L,H", [(1, False, 34, 64), (4, False, 34, 64),
+                                            (8, False, 34, 64), (1, True, 34, 64),
+                                            (4, True, 34, 64), (1, False, 17, 64),
+                                            (8, False, 24, 64), (17, False, 68, 64),
+                                            (1, False, 34, 8), (17, True, 34, 8),
+                                            (5, False, 25, 12)])
+def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L, H):
     # 1 layer = 64 chains (4 workgroups per head), 4 layers = 256 chains
     # (2 per head), 8 layers = 512 chains (1 per head): every tiling must
     # give the bits of the full launch, for the scan, both replays and the
@@ -557,7 +560,9 @@ def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L
     # its last 128 chains run 2 workgroups per head, at 17 layers its last 64
     # chains 4 per head.  24 layers (1,536 chains) and 68 layers (4,352
     # chains, 17-layer pieces of 1,088) end in tails too large to split.
-    T, H = 15, 64
+    # 34 x 8 = 272 and 25 x 12 = 300 chains run half heads on 256 chains and
+    # quarter heads on the rest, against pieces of 8 to 136 chains.
+    T = 15
     r = rand_rows(91, L, T, H, bf16=bf16)
     rows = rows_dev(r)
     s0 = dev(rand_state(92, L, H, 0.5))
