@@ -826,7 +826,7 @@ struct NoKeys {
 // each other's latency) reads each row's keys when it starts it.  The narrow
 // tilings run one wave per SIMD, so each row's key reads are issued during the
 // previous row (two register sets, used in turn: no copies between them).
-template <int R, int C, Rows M, bool PLAIN, bool PF, int TM>
+template <int R, int C, Rows M, bool PLAIN, int TM>
 __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C], int T,
                                          float* o, float* e_out, size_t o0, size_t ostride,
                                          int ig, int i0, int j0, gfloat* cols = nullptr,
@@ -844,7 +844,7 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
         ig = ((lane >> 4) & 3) | ((lane >> 1) & 4);
         i0 = ig * R;
     }
-    if constexpr (!DPP || !PF) {
+    if constexpr (!DPP) {
 #pragma unroll 1
         for (int t = 0; t < T; ++t) {
             RowKeys<DPP> x;   // a stash row reads its keys itself from LDS, four at a time
@@ -879,9 +879,7 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
 // kMaxPrev earlier rounds, oldest first, from the snapshot, then -- when
 // a.s_out is set -- that committed state is stored), then phase B (this
 // launch's rows).  Without FUSED the state after phase B is stored.
-// TAIL: the split tail of a whole-head launch, built within that launch's
-// register budget (no next-row prefetch).
-template <int R, int C, bool BF16, Rows MA, Rows MB, bool TABLE, bool DUAL, bool TAIL = false>
+template <int R, int C, bool BF16, Rows MA, Rows MB, bool TABLE, bool DUAL>
 __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1 : kTMax>* Ls,
                                            size_t chain, int blk) {
     using TL = Tile<R, C>;
@@ -992,9 +990,9 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         // the scan follows the replay and the snapshot store directly
         if (replay) stage_commit<R, C, MA, kTMax>(L, inA, p.T, tid);
         stage_commit<R, C, MB, kTMax>(LB, inB, b.T, tid);
-        if (replay) run_rows<R, C, MA, PLAIN, !TAIL>(L, s, p.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+        if (replay) run_rows<R, C, MA, PLAIN>(L, s, p.T, nullptr, nullptr, 0, 0, ig, i0, j0);
         if (a.s_out) store_state();   // the committed state: this round's snapshot
-        run_rows<R, C, MB, PLAIN, !TAIL>(LB, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0);
+        run_rows<R, C, MB, PLAIN>(LB, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0);
         return;
     } else if constexpr (FUSED) {
         // With at most one stash replay, this launch's row loads go out
@@ -1013,7 +1011,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
                 stage_commit<R, C, MA, kTMax>(L, inA, p0.T, tid);
                 stage_issue<R, C, BF16, MB, kTMax>(inB, b, tid);
                 asm volatile("" ::: "memory");   // keep those loads ahead of the replay
-                run_rows<R, C, MA, PLAIN, !TAIL>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+                run_rows<R, C, MA, PLAIN>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
             } else {
                 stage_issue<R, C, BF16, MB, kTMax>(inB, b, tid);
                 load_state();
@@ -1025,12 +1023,12 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         } else {
             const Src p0 = prev_src(0);
             stage<R, C, BF16, MA>(L, p0, tid, load_state);
-            run_rows<R, C, MA, PLAIN, !TAIL>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+            run_rows<R, C, MA, PLAIN>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
             __syncthreads();   // every wave is done with these staged rows
             for (int i = 1; i < a.n_prev; ++i) {
                 const Src pi = prev_src(i);
                 stage<R, C, BF16, MA>(L, pi, tid, [] {});
-                run_rows<R, C, MA, PLAIN, !TAIL>(L, s, pi.T, nullptr, nullptr, 0, 0, ig, i0, j0);
+                run_rows<R, C, MA, PLAIN>(L, s, pi.T, nullptr, nullptr, 0, 0, ig, i0, j0);
                 __syncthreads();
             }
             if (a.s_out) store_state();   // the committed state: this round's snapshot
@@ -1043,11 +1041,11 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
     if constexpr (MB == Rows::kFullCols) {
         // the last column is the state after all rows: no separate store
         static_assert(!FUSED && !TABLE, "state columns serve the plain scan");
-        run_rows<R, C, MB, PLAIN, !TAIL>(L, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0,
+        run_rows<R, C, MB, PLAIN>(L, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0,
                            (gfloat*)a.s_cols + chain * kDD, a.col_stride);
         return;
     }
-    run_rows<R, C, MB, PLAIN, !TAIL>(L, s, b.T, a.o, TABLE ? nullptr : a.e_out, o0, ostride, ig, i0, j0);
+    run_rows<R, C, MB, PLAIN>(L, s, b.T, a.o, TABLE ? nullptr : a.e_out, o0, ostride, ig, i0, j0);
     if constexpr (!FUSED) store_state();
 }
 
@@ -1096,7 +1094,7 @@ kda_scan_kernel(ScanArgs a) {
             unsigned long long head;
             int part;
             split_index<kSplit>(blockIdx.x - head_blocks, gridDim.x - head_blocks, head, part);
-            scan_chain<R, TAILC, BF16, MA, MB, TABLE, DUAL, true>(
+            scan_chain<R, TAILC, BF16, MA, MB, TABLE, DUAL>(
                 a, Ls, static_cast<size_t>(a.n_head_chains + head), part);
             return;
         }
