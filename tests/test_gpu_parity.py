@@ -610,6 +610,8 @@ def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L
     (2, [2, 7], True, False, True),          # recomputed replay, bf16
     (12, [4, 1, 12, 9], True, True, False),  # 768 chains, one workgroup per head
     (12, [6, 6], False, False, False),
+    (17, [3, 8], True, True, True),          # 1,088 chains: the last 64 split 4 ways
+    (34, [9, 2, 5], False, False, False),    # 2,176 chains: the last 128 split 2 ways
 ])
 def test_verify_round_multi_equals_replays_then_scan(L, keeps, store, stash, bf16):
     H, T = 64, 15
