@@ -387,26 +387,25 @@ __device__ __forceinline__ void stage_commit(Stage<R, TMAX>& L, const Staged<R, 
                     gq.x * kInvSqrtD, gq.y * kInvSqrtD, gq.z * kInvSqrtD, gq.w * kInvSqrtD);
             }
         }
+        // (q/sqrt(128)).k per row, from the registers: the 32 lanes of a half
+        // wave hold one row, 4 keys each; each lane's 4 keys in ascending
+        // order, then a fixed butterfly over the 32 lanes.  Every lane takes
+        // part (the loads were clamped into range), so the DPP and swap reads
+        // see defined values; only rows in range are written.
+        if constexpr (has_q(M)) {
+            const float4 gq = in.q[p], gk = in.k[p];
+            float d = fmaf(gq.x * kInvSqrtD, gk.x, 0.0f);
+            d = fmaf(gq.y * kInvSqrtD, gk.y, d);
+            d = fmaf(gq.z * kInvSqrtD, gk.z, d);
+            d = fmaf(gq.w * kInvSqrtD, gk.w, d);
+            d = group_sum<16>(d);
+            float d2 = d;
+            swap16(d, d2);   // even rows: (own, odd partner); odd rows: (even partner, own)
+            d = d + d2;
+            if (idx < T * (kD / 4) && (idx & 31) == 0) L.bq[idx >> 5].y = d;
+        }
     }
     __syncthreads();
-
-    // (q/sqrt(128)).k per row: one 16-lane DPP row per verify row, 8 keys per
-    // lane in ascending order, then a fixed butterfly
-    if constexpr (has_q(M)) {
-        const int wave = tid >> 6;
-        const int l16 = tid & 15;
-        for (int t = wave * 4 + ((tid & 63) >> 4); t < T; t += TL::WAVES * 4) {
-            float p = 0.0f;
-#pragma unroll
-            for (int m = 0; m < 8; ++m) {
-                const int kp = t * KR::kStride + KR::at(l16 * 8 + m);
-                p = fmaf(sq[kp], sk[kp], p);
-            }
-            p = group_sum<16>(p);
-            if (l16 == 0) L.bq[t].y = p;
-        }
-        __syncthreads();
-    }
 }
 
 // A phase's rows from HBM into LDS; `between` runs after the row loads are
