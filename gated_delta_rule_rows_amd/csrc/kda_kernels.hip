@@ -353,8 +353,9 @@ __device__ __forceinline__ void stage_fence(Staged<R, C, M, TMAX>& in) {
 }
 
 // Write a phase's rows to LDS in the scan's layout (decay, q/sqrt(128), beta v
-// or e), then (q/sqrt(128)).k per row.  Ends with every lane past a barrier.
-template <int R, int C, Rows M, int TMAX>
+// or e) with (q/sqrt(128)).k per row.  With SYNC, ends with every lane past a
+// barrier (without it, the caller places one before the rows are read).
+template <int R, int C, Rows M, int TMAX, bool SYNC = true>
 __device__ __forceinline__ void stage_commit(Stage<R, TMAX>& L, const Staged<R, C, M, TMAX>& in, int T,
                                              int tid) {
     using TL = Tile<R, C>;
@@ -405,7 +406,7 @@ __device__ __forceinline__ void stage_commit(Stage<R, TMAX>& L, const Staged<R, 
             if (idx < T * (kD / 4) && (idx & 31) == 0) L.bq[idx >> 5].y = d;
         }
     }
-    __syncthreads();
+    if constexpr (SYNC) __syncthreads();
 }
 
 // A phase's rows from HBM into LDS; `between` runs after the row loads are
@@ -987,7 +988,8 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         stage_fence<R, C, MB, kTMax>(inB);
         // both phases' rows go to LDS while the state is still arriving, so
         // the scan follows the replay and the snapshot store directly
-        if (replay) stage_commit<R, C, MA, kTMax>(L, inA, p.T, tid);
+        // two LDS areas: one barrier after both
+        if (replay) stage_commit<R, C, MA, kTMax, false>(L, inA, p.T, tid);
         stage_commit<R, C, MB, kTMax>(LB, inB, b.T, tid);
         if (replay) run_rows<R, C, MA, PLAIN>(L, s, p.T, nullptr, nullptr, 0, 0, ig, i0, j0);
         if (a.s_out) store_state();   // the committed state: this round's snapshot
