@@ -664,6 +664,21 @@ constexpr bool plain_layout() {
     return C == 4 && (TABLE || M == Rows::kFullCols);
 }
 
+// o and e stores of the narrow tilings (C < 4): buffer stores from the
+// chain's first row, one byte offset per lane, advanced a row at a time.  The
+// lanes that do not store a value carry bit 31 in their offset; the resource
+// covers 2^31 bytes, so their stores fall out of range and are dropped.  No
+// exec-mask branch and no 64-bit address arithmetic per row: at one wave per
+// SIMD every instruction of a row costs an issue slot.  A missing output gets
+// an empty range, which drops every lane.
+struct NarrowStores {
+    __amdgpu_buffer_rsrc_t o, e;
+    uint32_t oo, eo;   // this lane's byte offsets in the current row
+    uint32_t step;     // bytes from one row to the next
+    __device__ __forceinline__ void next() { oo += step; eo += step; }
+};
+constexpr int kBufferWords3 = 0x00020000;   // raw buffer, 32-bit data format
+
 // One row t of one phase over the staged rows L.  The lane's key group starts
 // at i0, its columns at j0 (ig: its key group, used by the plain layout).
 // kFullCols: `cols` addresses this chain's state in column 0, and row t's
@@ -672,7 +687,7 @@ template <int R, int C, Rows M, bool PLAIN, int TM, bool PFK, typename K, typena
 __device__ __forceinline__ void row_step(const Stage<R, TM>& L, const K& x, float (&s)[R][C], int t,
                                          float* o, float* e_out, size_t o0, size_t ostride,
                                          int ig, int i0, int j0, gfloat* cols, size_t col_stride,
-                                         F&& next_keys) {
+                                         F&& next_keys, NarrowStores& ns) {
     const float* sve = reinterpret_cast<const float*>(L.ve);
     const int lane = threadIdx.x & 63;
     constexpr bool Q = has_q(M);
@@ -759,55 +774,39 @@ __device__ __forceinline__ void row_step(const Stage<R, TM>& L, const K& x, floa
         load_cols<4>(slot, e);
     } else if constexpr (C == 2) {
         // column c = lane bit 4 (row & 1)
-        const uint32_t col = static_cast<uint32_t>(j0 + ((lane >> 4) & 1));
-        const size_t row = o0 + t * ostride;
+        static_assert(PFK, "the narrow tilings read keys ahead");
         float ec;
         if constexpr (Q) {
             // rows 0, 1 end with u of columns 0, 1; rows 2, 3 with w
             const float sums[4] = {u[0], u[1], w[0], w[1]};
             const float x4 = reduce_scatter4(sums);
-            ec = fmaf(nbt, x4, PFK ? ve1 : sve[t * kD + col]);         // valid in rows 0, 1
+            ec = fmaf(nbt, x4, ve1);                 // valid in rows 0, 1
             float e2 = ec;
             swap32(ec, e2);                          // rows 2, 3 take e from rows 0, 1
             const float ov = fmaf(ec, bq.y, x4);     // valid in rows 2, 3
-            if ((lane & 0x28) == 0x20) {
-                gfloat* orow = (gfloat*)(o + row);
-                asm volatile("" : "+s"(orow));
-                orow[col] = ov;
-            }
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, ov), ns.o, ns.oo, 0, 0);
         } else {
-            ec = fmaf(nbt, sum_groups2(u[0], u[1]), PFK ? ve1 : sve[t * kD + col]);
+            ec = fmaf(nbt, sum_groups2(u[0], u[1]), ve1);
         }
-        if (e_out != nullptr && (lane & 0x28) == 0) {
-            gfloat* erow = (gfloat*)(e_out + row);
-            asm volatile("" : "+s"(erow));
-            erow[col] = ec;
-        }
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, ec), ns.e, ns.eo, 0, 0);
+        ns.next();
         gather_pair16(ec, e[1]);
         e[0] = ec;
     } else {
-        const uint32_t col = static_cast<uint32_t>(j0);
-        const size_t row = o0 + t * ostride;
+        static_assert(PFK, "the narrow tilings read keys ahead");
         if constexpr (Q) {
             const float x2 = sum_groups2(u[0], w[0]);   // even rows u, odd rows w
-            float ec = fmaf(nbt, x2, PFK ? ve1 : sve[t * kD + col]);       // valid in even rows
+            float ec = fmaf(nbt, x2, ve1);              // valid in even rows
             float odd;
             gather_pair16(ec, odd);                     // ec: the even row's e, in all rows
             const float ov = fmaf(ec, bq.y, x2);        // valid in odd rows
-            if ((lane & 0x38) == 0x10) {
-                gfloat* orow = (gfloat*)(o + row);
-                asm volatile("" : "+s"(orow));
-                orow[col] = ov;
-            }
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, ov), ns.o, ns.oo, 0, 0);
             e[0] = ec;
         } else {
-            e[0] = fmaf(nbt, sum_groups(u[0]), PFK ? ve1 : sve[t * kD + col]);
+            e[0] = fmaf(nbt, sum_groups(u[0]), ve1);
         }
-        if (e_out != nullptr && (lane & 0x38) == 0) {
-            gfloat* erow = (gfloat*)(e_out + row);
-            asm volatile("" : "+s"(erow));
-            erow[col] = e[0];
-        }
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, e[0]), ns.e, ns.eo, 0, 0);
+        ns.next();
     }
     // delta-rule write: S = S' + k e^T
     write_rows<C>(x, s, e);
@@ -845,12 +844,13 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
         i0 = ig * R;
     }
     if constexpr (!DPP) {
+        NarrowStores none;   // the whole-head tiling stores through its own path
 #pragma unroll 1
         for (int t = 0; t < T; ++t) {
             RowKeys<DPP> x;   // a stash row reads its keys itself from LDS, four at a time
             if constexpr (M != Rows::kStash || DPP) x.template read<R, Q, TM>(L, t, i0, n);
             row_step<R, C, M, PLAIN, TM, false>(L, x, s, t, o, e_out, o0, ostride, ig, i0, j0,
-                                                cols, col_stride, NoKeys{});
+                                                cols, col_stride, NoKeys{}, none);
         }
     } else {
         // The next row's keys go out at the start of each row, after that
@@ -858,6 +858,22 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
         // index keeps the reads unconditional, which lets the compiler count
         // them exactly instead of waiting on them at once).
         if (T <= 0) return;
+        // o from the lanes with (lane & 0x38) == 0x10 (C = 1) or (lane & 0x28)
+        // == 0x20 (C = 2), e from those where the same bits are 0.  The
+        // launcher keeps T * H * 512 bytes under 2^31.
+        NarrowStores ns;
+        {
+            const int lane = threadIdx.x & 63;
+            constexpr int kMask = C == 2 ? 0x28 : 0x38, kOdd = C == 2 ? 0x20 : 0x10;
+            constexpr uint32_t kOut = 0x80000000u;
+            const uint32_t col4 = static_cast<uint32_t>(j0 + (C == 2 ? ((lane >> 4) & 1) : 0)) * 4;
+            ns.o = __builtin_amdgcn_make_buffer_rsrc(o ? o + o0 : nullptr, 0, o ? kOut : 0, kBufferWords3);
+            ns.e = __builtin_amdgcn_make_buffer_rsrc(e_out ? e_out + o0 : nullptr, 0, e_out ? kOut : 0,
+                                                     kBufferWords3);
+            ns.oo = col4 | ((lane & kMask) == kOdd ? 0u : kOut);
+            ns.eo = col4 | ((lane & kMask) == 0 ? 0u : kOut);
+            ns.step = static_cast<uint32_t>(ostride * 4);
+        }
         RowKeys<true> xa, xb;
         xa.template read<R, Q, TM>(L, 0, i0, n);
 #pragma unroll 1
@@ -865,12 +881,12 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
             row_step<R, C, M, PLAIN, TM, true>(L, xa, s, t, o, e_out, o0, ostride, ig, i0, j0,
                                                cols, col_stride, [&] {
                 xb.template read<R, Q, TM>(L, min(t + 1, T - 1), i0, n);
-            });
+            }, ns);
             if (t + 1 >= T) break;
             row_step<R, C, M, PLAIN, TM, true>(L, xb, s, t + 1, o, e_out, o0, ostride, ig, i0,
                                                j0, cols, col_stride, [&] {
                 xa.template read<R, Q, TM>(L, min(t + 2, T - 1), i0, n);
-            });
+            }, ns);
         }
     }
 }
@@ -991,6 +1007,10 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         // two LDS areas: one barrier after both
         if (replay) stage_commit<R, C, MA, kTMax, false>(L, inA, p.T, tid);
         stage_commit<R, C, MB, kTMax>(LB, inB, b.T, tid);
+        // the state has arrived during the commits: one wait for all of it
+        // here, instead of a wait per state row that the row loop would issue
+        // again on every pass (vmcnt 0; expcnt and lgkmcnt left at their maxima)
+        __builtin_amdgcn_s_waitcnt(0x0F70);
         if (replay) run_rows<R, C, MA, PLAIN>(L, s, p.T, nullptr, nullptr, 0, 0, ig, i0, j0);
         if (a.s_out) store_state();   // the committed state: this round's snapshot
         run_rows<R, C, MB, PLAIN>(LB, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0);
@@ -1595,11 +1615,14 @@ hipError_t launch_tiled(const ScanArgs& a0, hipStream_t stream) {
             return hipGetLastError();
         }
     }
+    // the narrow tilings store o and e at 32-bit offsets from a chain's first
+    // row (launches below 512 chains always qualify: H < 512)
+    const bool narrow_ok = static_cast<unsigned long long>(a.T) * a.H * kD * 4 < (1ull << 31);
     if constexpr (C == 4 && !TABLE) {
         const long long cus = chip_cus();
         const long long slots = 4 * cus;
         const long long tail = a.n_chains % slots;
-        if (a.n_chains > slots && tail > 0 && tail <= cus / 2) {
+        if (narrow_ok && a.n_chains > slots && tail > 0 && tail <= cus / 2) {
             a.n_head_chains = a.n_chains - tail;
             return tail <= cus / 4 ? launch_split_tail<4, 1, BF16, MA, MB>(a, tail, stream)
                                    : launch_split_tail<4, 2, BF16, MA, MB>(a, tail, stream);
@@ -1613,7 +1636,7 @@ hipError_t launch_tiled(const ScanArgs& a0, hipStream_t stream) {
         // and was slower.
         const long long cus = chip_cus();
         const long long tail = a.n_chains - cus;
-        if (tail > 0 && tail <= cus / 4) {
+        if (narrow_ok && tail > 0 && tail <= cus / 4) {
             a.n_head_chains = cus;
             return launch_split_tail<2, 1, BF16, MA, MB>(a, tail, stream);
         }
