@@ -1009,7 +1009,8 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         stage_commit<R, C, MB, kTMax>(LB, inB, b.T, tid);
         // the state has arrived during the commits: one wait for all of it
         // here, instead of a wait per state row that the row loop would issue
-        // again on every pass (vmcnt 0; expcnt and lgkmcnt left at their maxima)
+        // again on every pass (vmcnt 0; expcnt and lgkmcnt left at their
+        // maxima; no stores are in flight yet)
         __builtin_amdgcn_s_waitcnt(0x0F70);
         if (replay) run_rows<R, C, MA, PLAIN>(L, s, p.T, nullptr, nullptr, 0, 0, ig, i0, j0);
         if (a.s_out) store_state();   // the committed state: this round's snapshot
@@ -1030,6 +1031,8 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
                 load_state();
                 stage_fence<R, C, MA, kTMax>(inA);
                 stage_commit<R, C, MA, kTMax>(L, inA, p0.T, tid);
+                // narrow tilings: one wait for the state (see the dual stage)
+                if constexpr (C < 4) __builtin_amdgcn_s_waitcnt(0x0F70);
                 stage_issue<R, C, BF16, MB, kTMax>(inB, b, tid);
                 asm volatile("" ::: "memory");   // keep those loads ahead of the replay
                 run_rows<R, C, MA, PLAIN>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
@@ -1044,6 +1047,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         } else {
             const Src p0 = prev_src(0);
             stage<R, C, BF16, MA>(L, p0, tid, load_state);
+            if constexpr (C < 4) __builtin_amdgcn_s_waitcnt(0x0F70);
             run_rows<R, C, MA, PLAIN>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
             __syncthreads();   // every wave is done with these staged rows
             for (int i = 1; i < a.n_prev; ++i) {
