@@ -1109,8 +1109,7 @@ kda_scan_kernel(ScanArgs a) {
     __shared__ Stage<R, TABLE ? 1 : kTMax> Ls[DUAL ? 2 : 1];
     unsigned long long head_blocks = gridDim.x;
     if constexpr (TAILC != 0) {
-        static_assert((C == 4 || (C == 2 && TAILC == 1)) && !DUAL && !TABLE,
-                      "a split tail follows whole heads, or half heads with 4-way parts");
+        static_assert(C == 4 && !DUAL && !TABLE, "a split tail follows whole heads");
         head_blocks = static_cast<unsigned long long>(a.n_head_chains) * TL::BLOCKS;
         if (blockIdx.x >= head_blocks) {
             // head_blocks is a multiple of the CU count (256 on MI355X), so
@@ -1620,29 +1619,27 @@ hipError_t launch_tiled(const ScanArgs& a0, hipStream_t stream) {
         }
     }
     // the narrow tilings store o and e at 32-bit offsets from a chain's first
-    // row (launches below 512 chains always qualify: H < 512)
+    // row (the narrow launches, at most one chain per CU, always qualify)
     const bool narrow_ok = static_cast<unsigned long long>(a.T) * a.H * kD * 4 < (1ull << 31);
     if constexpr (C == 4 && !TABLE) {
         const long long cus = chip_cus();
         const long long slots = 4 * cus;
-        const long long tail = a.n_chains % slots;
-        if (narrow_ok && a.n_chains > slots && tail > 0 && tail <= cus / 2) {
-            a.n_head_chains = a.n_chains - tail;
-            return tail <= cus / 4 ? launch_split_tail<4, 1, BF16, MA, MB>(a, tail, stream)
-                                   : launch_split_tail<4, 2, BF16, MA, MB>(a, tail, stream);
-        }
-    }
-    if constexpr (C == 2 && !TABLE) {
-        // Half heads past one chain per CU: with up to CUs/4 chains more,
-        // those split 4 ways, one quarter-head workgroup per CU at most, so
-        // no CU runs three half heads.  The TP=8 share (272 chains) measured
-        // 27.3 -> 25.2 us; a larger tail put two quarter heads on some CUs
-        // and was slower.
-        const long long cus = chip_cus();
-        const long long tail = a.n_chains - cus;
-        if (narrow_ok && tail > 0 && tail <= cus / 4) {
-            a.n_head_chains = cus;
-            return launch_split_tail<2, 1, BF16, MA, MB>(a, tail, stream);
+        if (a.n_chains <= slots) {
+            // up to one fill: whole rounds of one chain per CU, then a tail
+            // of at most CUs/4 chains split 4 ways (a 2-way split of a larger
+            // tail measured slower than whole heads: 384 chains 24.9 vs 24.1 us)
+            const long long tail = a.n_chains % cus;
+            if (narrow_ok && a.n_chains > cus && tail > 0 && tail <= cus / 4) {
+                a.n_head_chains = a.n_chains - tail;
+                return launch_split_tail<4, 1, BF16, MA, MB>(a, tail, stream);
+            }
+        } else {
+            const long long tail = a.n_chains % slots;
+            if (narrow_ok && tail > 0 && tail <= cus / 2) {
+                a.n_head_chains = a.n_chains - tail;
+                return tail <= cus / 4 ? launch_split_tail<4, 1, BF16, MA, MB>(a, tail, stream)
+                                       : launch_split_tail<4, 2, BF16, MA, MB>(a, tail, stream);
+            }
         }
     }
     kda_scan_kernel<kKeysPerLane, C, BF16, MA, MB, TABLE, false, 0>
@@ -1650,16 +1647,22 @@ hipError_t launch_tiled(const ScanArgs& a0, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Chains below which a head is split over more workgroups: a launch should
-// reach every CU (256) with at least two workgroups where it can.
-constexpr long long kSplitBy4Below = 256;   // C = 1: 4 workgroups per head
-constexpr long long kSplitBy2Below = 512;   // C = 2: 2 workgroups per head
+// The tiling by chain count n: up to CUs/2 chains a head splits over 4
+// workgroups (C = 1), up to CUs over 2 (C = 2) -- at most 2 workgroups per CU
+// either way -- and past that whole heads (C = 4), whose last partial round
+// of one chain per CU splits 4 ways when it is at most CUs/4 chains.  Against
+// half heads up to 512 chains and quarter heads up to 256, in one process:
+// 240 chains 22.8 -> 18.3 us, 272 (the TP = 8 share) 23.7 -> 20.9, 384 27.7 ->
+// 23.9, 448 31.5 -> 25.1, 544 35.6 -> 31.9; 128, 256, 640 and 768 unchanged.
+// Half heads lose once every CU has a chain: their DPP key operands cost
+// about 1.2x, and whole heads hide latency with 4 columns per lane.
 
 template <bool BF16, Rows MA, Rows MB, bool TABLE>
 hipError_t launch_one(const ScanArgs& a, hipStream_t stream) {
     if constexpr (!TABLE) {
-        if (a.n_chains < kSplitBy4Below) return launch_tiled<1, BF16, MA, MB, TABLE>(a, stream);
-        if (a.n_chains < kSplitBy2Below) return launch_tiled<2, BF16, MA, MB, TABLE>(a, stream);
+        const long long cus = chip_cus();
+        if (a.n_chains <= cus / 2) return launch_tiled<1, BF16, MA, MB, TABLE>(a, stream);
+        if (a.n_chains <= cus) return launch_tiled<2, BF16, MA, MB, TABLE>(a, stream);
     }
     return launch_tiled<4, BF16, MA, MB, TABLE>(a, stream);
 }

@@ -48,7 +48,7 @@ def state(seed, L, H):
     (1, 1, 8, False),      # 1 chain: 4 workgroups per head
     (3, 5, 15, True),
     (4, 64, 15, False),    # 256 chains: 2 per head
-    (34, 8, 15, False),    # 272 chains: 256 at 2 per head, the last 16 at 4 per head
+    (34, 8, 15, False),    # 272 chains: 256 whole heads, the last 16 at 4 per head
     (8, 64, 12, False),    # 512 chains: whole heads, one fill
     (17, 64, 15, True),    # 1,088 chains: whole heads, tail split 4 ways
     (34, 64, 15, False),   # 2,176 chains: whole heads, tail split 2 ways

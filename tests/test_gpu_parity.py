@@ -551,7 +551,8 @@ def _per_layers(fn, L, chunk):
                                             (4, True, 34, 64), (1, False, 17, 64),
                                             (8, False, 24, 64), (17, False, 68, 64),
                                             (1, False, 34, 8), (17, True, 34, 8),
-                                            (5, False, 25, 12)])
+                                            (5, False, 25, 12), (17, False, 34, 16),
+                                            (4, False, 28, 16), (6, True, 40, 6)])
 def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L, H):
     # 1 layer = 64 chains (4 workgroups per head), 4 layers = 256 chains
     # (2 per head), 8 layers = 512 chains (1 per head): every tiling must
@@ -560,8 +561,11 @@ def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L
     # its last 128 chains run 2 workgroups per head, at 17 layers its last 64
     # chains 4 per head.  24 layers (1,536 chains) and 68 layers (4,352
     # chains, 17-layer pieces of 1,088) end in tails too large to split.
-    # 34 x 8 = 272 and 25 x 12 = 300 chains run half heads on 256 chains and
-    # quarter heads on the rest, against pieces of 8 to 136 chains.
+    # 34 x 8 = 272 and 25 x 12 = 300 chains run whole heads on 256 chains and
+    # quarter heads on the rest, against pieces of 8 to 136 chains; 34 x 16 =
+    # 544 chains two rounds of whole heads and 32 chains at 4 per head
+    # (pieces of 272), 28 x 16 = 448 chains whole heads only (pieces of 64),
+    # 40 x 6 = 240 chains half heads (pieces of 36, quarter heads).
     T = 15
     r = rand_rows(91, L, T, H, bf16=bf16)
     rows = rows_dev(r)
