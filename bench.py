@@ -308,7 +308,8 @@ def kernel_label(name: str):
         else:
             kind = "replay_stash"
         tile = "" if c == "4" else f"_c{c}" + ("_dual" if dual else "")
-        return kind + tile + ("_bf16" if bf == "true" else "")
+        tail = {"1": "_t4", "2": "_t2"}.get(parts[7] if len(parts) > 7 else "0", "")
+        return kind + tile + tail + ("_bf16" if bf == "true" else "")
     for key, label in (("kda_copy_kernel", "copy"), ("kda_argmax_part_kernel", "accept_argmax"),
                        ("kda_accept_finish_kernel", "accept_finish"),
                        ("kda_row_ops_kernel", "row_ops"), ("kda_reroll_kernel", "conv_reroll"),
@@ -319,8 +320,9 @@ def kernel_label(name: str):
 
 
 def _is_headline_kernel(label) -> bool:
-    """The fused round at the whole-head tiling with f32 rows: the headline's kernel."""
-    return label in ("round_stash", "round_recompute")
+    """The fused round at the whole-head tiling with f32 rows: the headline's kernel
+    (34 x 64 = 2,176 chains: two fills of 1,024 and 128 chains split 2 ways)."""
+    return label in ("round_stash_t2", "round_recompute_t2")
 
 
 def _last_json(path):
@@ -417,14 +419,17 @@ def layer_counters(before: str, after: str, before_sha: str) -> None:
     """profiles/one_layer_round_counters.md: the one-layer fused launch (64
     heads, 4 workgroups per head) under the SQ passes of two kernel sources."""
     after_sha = _last_json(os.path.join(after, "valu_a.log"))["config"]["kernel_source_sha256_16"]
-    keep = {"round_stash_c1_dual", "round_stash_c2", "round_stash"}
+    keep = {"round_stash_c1_dual", "round_stash_c2", "round_stash", "round_stash_t4",
+            "round_stash_t2"}
     with open(os.path.join(ROOT, "profiles", "one_layer_round_counters.md"), "w") as f:
         f.write("# SQ counters: the one-layer fused round (1 layer x 64 heads, T=15, keep_prev 8, "
                 "f32), one MI355X\n\nThe kernel of the per-layer HIP graph round "
                 "(`round_stash_c1_dual`: 4 workgroups per head, one wave per SIMD), before and "
                 "after the quad key broadcast, the reordered staging and the next row's key reads "
                 "issued at the start of each row; the 34-layer fused round "
-                "(`round_stash`) and the TP=8 share's tiling (`round_stash_c2`) beside them.  "
+                "(`round_stash_t2`, `round_stash` in sources before the tail label) and the "
+                "TP=8 share's tiling (`round_stash_t4`: whole heads and 16 chains split 4 "
+                "ways; `round_stash_c2` before) beside them.  "
                 "Commands: the two `valu_*` runs of `PROF_RUNS` in bench.py, for each source.  "
                 "Reduced by `python bench.py --layer-counters BEFORE AFTER SHA`.\n\n"
                 "wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; the other columns as in "
@@ -434,7 +439,8 @@ def layer_counters(before: str, after: str, before_sha: str) -> None:
         for title, d, sha in (("Before", before, before_sha), ("After", after, after_sha)):
             rows = _valu_rows(d, keep)
             f.write(f"## {title}: kernel source sha256[:16] `{sha}`\n\n" + VALU_HEAD)
-            for k in ("round_stash_c1_dual", "round_stash_c2", "round_stash"):
+            for k in ("round_stash_c1_dual", "round_stash_c2", "round_stash_t4", "round_stash",
+                      "round_stash_t2"):
                 if k in rows:
                     f.write(_valu_line(k, rows[k]))
             f.write("\n")
@@ -517,7 +523,10 @@ def profile_summary(d: str, out: str = None) -> None:
                 "previous round's kept rows from the stash plane, store, scan of 15 rows; whole "
                 "heads, 2176 chains); `round_recompute` = the same without a stash (the first "
                 "round); `_c1`, `_c2` = 4 or 2 workgroups per head, `_dual` = both phases staged "
-                "up front (the one-layer launches); `scan` = kda_scan_rows (T=15); `replay` = "
+                "up front (the one-layer launches); `_t2`, `_t4` = whole heads whose last chains "
+                "run 2 or 4 workgroups per head (2,176 chains: the last 128 at 2 per head; the "
+                "TP=8 share's 272: the last 16 at 4 per head); `scan` = kda_scan_rows (T=15); "
+                "`replay` = "
                 "kda_replay (T=keep); `copy` = kda_snapshot's copy; `fill` = torch's zero_() "
                 "of the flush buffer and of state buffers; torch's `reduce_kernel` is the "
                 "flush's read pass.\n")
@@ -608,8 +617,9 @@ def profile_summary(d: str, out: str = None) -> None:
                 "- wait = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES: the share of wave cycles spent "
                 "waiting on a memory counter;\n"
                 "- LDS bank conflicts = SQ_LDS_BANK_CONFLICT / 256 CUs / cycles.\n\n" + VALU_HEAD)
-        order = ["round_stash", "round_recompute", "scan", "replay", "round_stash_c1_dual",
-                 "round_stash_c2", "round_stash_c2_dual", "batched", "scan_columns", "row_ops"]
+        order = ["round_stash_t2", "round_recompute_t2", "scan_t2", "replay_t2",
+                 "round_stash_c1_dual", "round_stash_t4", "round_stash_c2_dual", "batched",
+                 "scan_columns_t2", "row_ops"]
         for k in order + sorted(set(rows) - set(order)):
             if k in rows:
                 f.write(_valu_line(k, rows[k]))

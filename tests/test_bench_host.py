@@ -25,9 +25,9 @@ LAYER = SCAN.format(c=1, bf="false", ma=3, mb=1, table="false", dual="true", tai
 
 
 def test_kernel_labels():
-    assert bench.kernel_label(ROUND) == "round_stash"
-    assert bench.kernel_label(ROUND_REC) == "round_recompute"
-    assert bench.kernel_label(SCAN_K) == "scan"
+    assert bench.kernel_label(ROUND) == "round_stash_t2"
+    assert bench.kernel_label(ROUND_REC) == "round_recompute_t2"
+    assert bench.kernel_label(SCAN_K) == "scan_t2"
     assert bench.kernel_label(LAYER) == "round_stash_c1_dual"
     assert bench.kernel_label(SCAN.format(c=2, bf="true", ma=0, mb=2, table="false",
                                           dual="false", tail=0)) == "replay_c2_bf16"
@@ -35,6 +35,10 @@ def test_kernel_labels():
                                           dual="false", tail=0)) == "batched"
     assert bench.kernel_label(SCAN.format(c=4, bf="false", ma=0, mb=4, table="false",
                                           dual="false", tail=0)) == "scan_columns"
+    assert bench.kernel_label(SCAN.format(c=4, bf="false", ma=3, mb=1, table="false",
+                                          dual="false", tail=1)) == "round_stash_t4"
+    assert bench.kernel_label(SCAN.format(c=4, bf="true", ma=3, mb=1, table="false",
+                                          dual="false", tail=2)) == "round_stash_t2_bf16"
     assert bench.kernel_label(COPY) == "copy"
     assert bench.kernel_label(FILL) == "fill"
     assert bench.kernel_label("void some_other_kernel(int)") is None
@@ -126,7 +130,7 @@ def test_profile_summary_reduces_synthetic_runs(tmp_path):
     assert "median 4.0 us, min 4.0, max 4.0" in md
     assert f"The {K} timed rounds" in md
     assert "3 dispatches, mean 11.00 us" in md
-    assert "| round_stash | 25 | 95.0 |" in md
+    assert "| round_stash_t2 | 25 | 95.0 |" in md
     assert "ratio" in open(out / "verify_k14_traffic.md").read()
 
 
