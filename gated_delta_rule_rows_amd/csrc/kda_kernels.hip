@@ -679,6 +679,10 @@ struct NarrowStores {
 };
 constexpr int kBufferWords3 = 0x00020000;   // raw buffer, 32-bit data format
 
+// s_waitcnt immediate that waits for vector memory only: vmcnt 0, expcnt and
+// lgkmcnt at their maxima (gfx9 field layout).
+constexpr int kWaitVmem = 0x0F70;
+
 // One row t of one phase over the staged rows L.  The lane's key group starts
 // at i0, its columns at j0 (ig: its key group, used by the plain layout).
 // kFullCols: `cols` addresses this chain's state in column 0, and row t's
@@ -1011,7 +1015,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         // here, instead of a wait per state row that the row loop would issue
         // again on every pass (vmcnt 0; expcnt and lgkmcnt left at their
         // maxima; no stores are in flight yet)
-        __builtin_amdgcn_s_waitcnt(0x0F70);
+        __builtin_amdgcn_s_waitcnt(kWaitVmem);
         if (replay) run_rows<R, C, MA, PLAIN>(L, s, p.T, nullptr, nullptr, 0, 0, ig, i0, j0);
         if (a.s_out) store_state();   // the committed state: this round's snapshot
         run_rows<R, C, MB, PLAIN>(LB, s, b.T, a.o, a.e_out, o0, ostride, ig, i0, j0);
@@ -1032,7 +1036,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
                 stage_fence<R, C, MA, kTMax>(inA);
                 stage_commit<R, C, MA, kTMax>(L, inA, p0.T, tid);
                 // narrow tilings: one wait for the state (see the dual stage)
-                if constexpr (C < 4) __builtin_amdgcn_s_waitcnt(0x0F70);
+                if constexpr (C < 4) __builtin_amdgcn_s_waitcnt(kWaitVmem);
                 stage_issue<R, C, BF16, MB, kTMax>(inB, b, tid);
                 asm volatile("" ::: "memory");   // keep those loads ahead of the replay
                 run_rows<R, C, MA, PLAIN>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
@@ -1047,7 +1051,7 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Stage<R, TABLE ? 1
         } else {
             const Src p0 = prev_src(0);
             stage<R, C, BF16, MA>(L, p0, tid, load_state);
-            if constexpr (C < 4) __builtin_amdgcn_s_waitcnt(0x0F70);
+            if constexpr (C < 4) __builtin_amdgcn_s_waitcnt(kWaitVmem);
             run_rows<R, C, MA, PLAIN>(L, s, p0.T, nullptr, nullptr, 0, 0, ig, i0, j0);
             __syncthreads();   // every wave is done with these staged rows
             for (int i = 1; i < a.n_prev; ++i) {
@@ -1618,10 +1622,10 @@ hipError_t launch_tiled(const ScanArgs& a0, hipStream_t stream) {
             return hipGetLastError();
         }
     }
-    // the narrow tilings store o and e at 32-bit offsets from a chain's first
-    // row (the narrow launches, at most one chain per CU, always qualify)
-    const bool narrow_ok = static_cast<unsigned long long>(a.T) * a.H * kD * 4 < (1ull << 31);
     if constexpr (C == 4 && !TABLE) {
+        // a split tail stores o and e at 32-bit offsets from a chain's first
+        // row (the narrow launches, at most one chain per CU, always fit)
+        const bool narrow_ok = static_cast<unsigned long long>(a.T) * a.H * kD * 4 < (1ull << 31);
         const long long cus = chip_cus();
         const long long slots = 4 * cus;
         if (a.n_chains <= slots) {
