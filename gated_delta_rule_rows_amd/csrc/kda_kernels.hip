@@ -286,11 +286,16 @@ enum class Rows {
 constexpr bool has_q(Rows m) { return m == Rows::kFull || m == Rows::kFullCols; }
 
 // Up to TM rows of one phase, staged in LDS (the batched arm stages one).
+// The key-layout arrays of a multi-row stage hold one spare row past TM: the
+// narrow tilings read the next row's keys during each row, and after the last
+// row that read lands there (its values are never used).  The batched arm's
+// one-row stage has none (it runs whole heads).
 template <int R, int TM = kTMax>
 struct Stage {
-    float4 d[TM * KeyRow<R>::kStride / 4];   // exp(clamp(g)), key layout
-    float4 k[TM * KeyRow<R>::kStride / 4];   // k, key layout
-    float4 q[TM * KeyRow<R>::kStride / 4];   // q / sqrt(128), key layout (kFull)
+    static constexpr int kRows = TM > 1 ? TM + 1 : TM;
+    float4 d[kRows * KeyRow<R>::kStride / 4];   // exp(clamp(g)), key layout
+    float4 k[kRows * KeyRow<R>::kStride / 4];   // k, key layout
+    float4 q[kRows * KeyRow<R>::kStride / 4];   // q / sqrt(128), key layout (kFull)
     float4 ve[TM * kD / 4];                  // beta * v, or e for kStash; [t][j]
     float2 bq[TM];                           // beta, (q / sqrt(128)) . k: one LDS read
 };
@@ -858,9 +863,9 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
         }
     } else {
         // The next row's keys go out at the start of each row, after that
-        // row's own reads; the last row reads its own keys again (a clamped
-        // index keeps the reads unconditional, which lets the compiler count
-        // them exactly instead of waiting on them at once).
+        // row's own reads, unconditionally (the compiler then counts them
+        // exactly instead of waiting on them at once): after the last row the
+        // read lands in the stage's spare row.
         if (T <= 0) return;
         // o from the lanes with (lane & 0x38) == 0x10 (C = 1) or (lane & 0x28)
         // == 0x20 (C = 2), e from those where the same bits are 0.  The
@@ -884,12 +889,12 @@ __device__ __forceinline__ void run_rows(const Stage<R, TM>& L, float (&s)[R][C]
         for (int t = 0; t < T; t += 2) {
             row_step<R, C, M, PLAIN, TM, true>(L, xa, s, t, o, e_out, o0, ostride, ig, i0, j0,
                                                cols, col_stride, [&] {
-                xb.template read<R, Q, TM>(L, min(t + 1, T - 1), i0, n);
+                xb.template read<R, Q, TM>(L, t + 1, i0, n);
             }, ns);
             if (t + 1 >= T) break;
             row_step<R, C, M, PLAIN, TM, true>(L, xb, s, t + 1, o, e_out, o0, ostride, ig, i0,
                                                j0, cols, col_stride, [&] {
-                xa.template read<R, Q, TM>(L, min(t + 2, T - 1), i0, n);
+                xa.template read<R, Q, TM>(L, t + 2, i0, n);   // t + 2 <= T
             }, ns);
         }
     }
@@ -1109,7 +1114,7 @@ __global__ void __launch_bounds__((Tile<R, C>::THREADS))
 __attribute__((amdgpu_waves_per_eu(DUAL ? 2 : 4)))   // DUAL: LDS allows 2 workgroups per CU
 kda_scan_kernel(ScanArgs a) {
     using TL = Tile<R, C>;
-    // the batched arm stages its one row: 2.4 KB of LDS instead of 36.6 KB
+    // the batched arm stages its one row: 2.4 KB of LDS instead of 38.5 KB
     __shared__ Stage<R, TABLE ? 1 : kTMax> Ls[DUAL ? 2 : 1];
     unsigned long long head_blocks = gridDim.x;
     if constexpr (TAILC != 0) {
