@@ -34,7 +34,7 @@ def same(a, b):
 
 
 @pytest.mark.parametrize("L,H,stash", [(1, 64, True), (4, 64, False), (34, 64, True),
-                                       (2, 3, False)])
+                                       (2, 3, False), (34, 8, True)])
 def test_verify_round_dev_equals_host_keep(L, H, stash):
     print(f"devkeep round L={L} H={H} stash={stash}", flush=True)
     T_prev, T = 12, 15
