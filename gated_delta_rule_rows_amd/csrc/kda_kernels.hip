@@ -70,6 +70,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 #include <mutex>
 #include <type_traits>
@@ -1572,16 +1573,23 @@ constexpr unsigned long long kDualStageMaxBlocks = 512;
 // VGPRs, 4 waves per SIMD).  A launch of more chains than that runs in fills;
 // when its last fill is sparse, its chains are split so that the fill has
 // about one workgroup per CU: 4 ways up to CUs/4 chains, 2 ways up to CUs/2.
+// CUs of the current device, read once per device (a process may drive
+// devices of different sizes, e.g. partitions); 256 if it cannot be read.  It
+// picks tilings only: every tiling gives the same bits.
 int chip_cus() {
-    static int cus = [] {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        return n;
-    }();
-    return cus;
+    constexpr int kCached = 64;
+    static std::atomic<int> cache[kCached];   // 0: not read yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+    if (dev < kCached) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    if (dev < kCached) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 // a.n_head_chains chains with CH value columns per lane, then `tail` chains
