@@ -1569,10 +1569,6 @@ __global__ void __launch_bounds__(64 * kTMax) kda_accept_finish_kernel(AcceptArg
 // 74 KB of LDS each, so two workgroups per CU): they fit in one pass.
 constexpr unsigned long long kDualStageMaxBlocks = 512;
 
-// The chip's CUs; whole-head workgroups resident at once are 4 per CU (128
-// VGPRs, 4 waves per SIMD).  A launch of more chains than that runs in fills;
-// when its last fill is sparse, its chains are split so that the fill has
-// about one workgroup per CU: 4 ways up to CUs/4 chains, 2 ways up to CUs/2.
 // CUs of the current device, read once per device (a process may drive
 // devices of different sizes, e.g. partitions); 256 if it cannot be read.  It
 // picks tilings only: every tiling gives the same bits.
@@ -1653,6 +1649,9 @@ hipError_t launch_tiled(const ScanArgs& a0, hipStream_t stream) {
                 return launch_split_tail<4, 1, BF16, MA, MB>(a, tail, stream);
             }
         } else {
+            // several fills of 4 whole heads per CU (128 VGPRs, 4 waves per
+            // SIMD): a sparse last fill splits 4 ways up to CUs/4 chains, 2
+            // ways up to CUs/2, so that it has about one workgroup per CU
             const long long tail = a.n_chains % slots;
             if (narrow_ok && tail > 0 && tail <= cus / 2) {
                 a.n_head_chains = a.n_chains - tail;
