@@ -612,6 +612,7 @@ def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L
     (2, [5], True, True, False),             # one round, two stage areas
     (2, [3, 0, 8], False, True, False),      # a round with nothing kept is skipped
     (2, [2, 7], True, False, True),          # recomputed replay, bf16
+    (3, [5, 9], True, True, False),          # 192 chains: 2 workgroups per head, one stage area
     (12, [4, 1, 12, 9], True, True, False),  # 768 chains, one workgroup per head
     (12, [6, 6], False, False, False),
     (17, [3, 8], True, True, True),          # 1,088 chains: the last 64 split 4 ways
