@@ -552,7 +552,8 @@ def _per_layers(fn, L, chunk):
                                             (8, False, 24, 64), (17, False, 68, 64),
                                             (1, False, 34, 8), (17, True, 34, 8),
                                             (5, False, 25, 12), (17, False, 34, 16),
-                                            (4, False, 28, 16), (6, True, 40, 6)])
+                                            (4, False, 28, 16), (6, True, 40, 6),
+                                            (100, False, 300, 1), (3, False, 41, 7)])
 def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L, H):
     # 1 layer = 64 chains (4 workgroups per head), 4 layers = 256 chains
     # (2 per head), 8 layers = 512 chains (1 per head): every tiling must
@@ -565,7 +566,8 @@ def test_layer_chunked_launches_match_the_full_launch_bit_for_bit(chunk, bf16, L
     # quarter heads on the rest, against pieces of 8 to 136 chains; 34 x 16 =
     # 544 chains two rounds of whole heads and 32 chains at 4 per head
     # (pieces of 272), 28 x 16 = 448 chains whole heads only (pieces of 64),
-    # 40 x 6 = 240 chains half heads (pieces of 36, quarter heads).
+    # 40 x 6 = 240 chains half heads (pieces of 36, quarter heads); one head
+    # per layer (300 x 1) and an odd head count (41 x 7 = 287) in split tails.
     T = 15
     r = rand_rows(91, L, T, H, bf16=bf16)
     rows = rows_dev(r)
