@@ -640,7 +640,7 @@ def main() -> int:
     ap.add_argument("--per-layer-rounds", type=int, default=16,
                     help="rounds of 34 per-layer fused launches replayed from a HIP graph")
     ap.add_argument("--tp-share-rounds", type=int, default=32,
-                    help="fused rounds of one TP=8 rank's share (8 heads x 34 layers)")
+                    help="fused rounds of one TP=8 and one TP=4 rank's share (8 and 16 heads x 34 layers)")
     ap.add_argument("--batched-steps", type=int, default=8,
                     help="batched-decode steps (B=15, t=1, 34 layers) timed back to back")
     ap.add_argument("--serving-steps", type=int, default=32,
@@ -1008,10 +1008,11 @@ def main() -> int:
                              "each between its own events; warm: back to back, no flush"}
         del graph
 
-    # one tensor-parallel rank's share at TP = 8: 8 heads x 34 layers per launch
-    tp_share = None
-    if args.tp_share_rounds > 0:
-        Ht = H // 8
+    # one tensor-parallel rank's share: H / tp heads x 34 layers per launch (TP = 8:
+    # 272 chains, whole heads on 256 of them and the rest at 4 workgroups per head;
+    # TP = 4: 544 chains), fused rounds back to back
+    def tp_share_of(tp):
+        Ht = H // tp
         r_tp = synth.rows(w.seed, 0, L, T, Ht)
         tp_rows = [torch.from_numpy(r_tp[n]).cuda() for n in names]
         tp_snap = torch.zeros(L, Ht, D, D, device="cuda")
@@ -1034,10 +1035,14 @@ def main() -> int:
         torch.cuda.synchronize()
         tp_us = a.elapsed_time(b) * 1e3 / args.tp_share_rounds
         tp_bytes = L * Ht * round_bytes_per_head(8, T)
-        tp_share = {"heads": Ht, "layers": L, "chains": L * Ht, "keep_prev": 8,
-                    "us_per_round": tp_us, "rows_heads_per_s": T * Ht * L / (tp_us * 1e-6),
-                    "gbps": tp_bytes / (tp_us * 1e-6) / 1e9}
-        del tp_rows, tp_snap, tp_nxt, tp_o, tp_e
+        return {"heads": Ht, "layers": L, "chains": L * Ht, "keep_prev": 8,
+                "us_per_round": tp_us, "rows_heads_per_s": T * Ht * L / (tp_us * 1e-6),
+                "gbps": tp_bytes / (tp_us * 1e-6) / 1e9}
+
+    tp_share = tp4_share = None
+    if args.tp_share_rounds > 0:
+        tp_share = tp_share_of(8)
+        tp4_share = tp_share_of(4)
 
     # batched-decode arm: 15 sessions x 34 layers x 64 heads, one row each, in place
     batched = None
@@ -1406,6 +1411,7 @@ def main() -> int:
         "verify_loop": verify_loop,
         "per_layer_graph": per_layer,
         "tp8_share": tp_share,
+        "tp4_share": tp4_share,
         "batched": batched,
         "serving_mix": serving,
         "copy_ceiling_gbps": copy_gbps,
