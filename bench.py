@@ -267,8 +267,8 @@ def host_cpu():
 # run's stdout, whose last line is that run's bench line) into profiles/.
 
 PROF_SHORT = ("--steps 8 --warmup 2 --no-cpu-baseline --columns-rounds 2 --per-layer-rounds 2 "
-              "--tp-share-rounds 2 --batched-steps 2 --serving-steps 2 --accept-launches 2 "
-              "--loop-rounds 0 --copy-launches 2")
+              "--tp-share-rounds 2 --tp4-share-rounds 0 --batched-steps 2 --serving-steps 2 "
+              "--accept-launches 2 --loop-rounds 0 --copy-launches 2")
 PROF_RUNS = {
     "kt": "rocprofv3 --kernel-trace --stats -d DIR/kt -o kt -f csv -- "
           "python3 bench.py --gpus 1 --steps 20 --warmup 5",
@@ -525,7 +525,8 @@ def profile_summary(d: str, out: str = None) -> None:
                 "round); `_c1`, `_c2` = 4 or 2 workgroups per head, `_dual` = both phases staged "
                 "up front (the one-layer launches); `_t2`, `_t4` = whole heads whose last chains "
                 "run 2 or 4 workgroups per head (2,176 chains: the last 128 at 2 per head; the "
-                "TP=8 share's 272: the last 16 at 4 per head); `scan` = kda_scan_rows (T=15); "
+                "TP=8 share's 272: the last 16 at 4 per head; in the plain run also the TP=4 "
+                "share's 544: the last 32 at 4 per head); `scan` = kda_scan_rows (T=15); "
                 "`replay` = "
                 "kda_replay (T=keep); `copy` = kda_snapshot's copy; `fill` = torch's zero_() "
                 "of the flush buffer and of state buffers; torch's `reduce_kernel` is the "
@@ -640,7 +641,9 @@ def main() -> int:
     ap.add_argument("--per-layer-rounds", type=int, default=16,
                     help="rounds of 34 per-layer fused launches replayed from a HIP graph")
     ap.add_argument("--tp-share-rounds", type=int, default=32,
-                    help="fused rounds of one TP=8 and one TP=4 rank's share (8 and 16 heads x 34 layers)")
+                    help="fused rounds of one TP=8 rank's share (8 heads x 34 layers)")
+    ap.add_argument("--tp4-share-rounds", type=int, default=32,
+                    help="fused rounds of one TP=4 rank's share (16 heads x 34 layers)")
     ap.add_argument("--batched-steps", type=int, default=8,
                     help="batched-decode steps (B=15, t=1, 34 layers) timed back to back")
     ap.add_argument("--serving-steps", type=int, default=32,
@@ -1011,7 +1014,7 @@ def main() -> int:
     # one tensor-parallel rank's share: H / tp heads x 34 layers per launch (TP = 8:
     # 272 chains, whole heads on 256 of them and the rest at 4 workgroups per head;
     # TP = 4: 544 chains), fused rounds back to back
-    def tp_share_of(tp):
+    def tp_share_of(tp, rounds):
         Ht = H // tp
         r_tp = synth.rows(w.seed, 0, L, T, Ht)
         tp_rows = [torch.from_numpy(r_tp[n]).cuda() for n in names]
@@ -1029,20 +1032,18 @@ def main() -> int:
         torch.cuda.synchronize()
         a, b = ev(), ev()
         a.record(stream)
-        for _ in range(args.tp_share_rounds):
+        for _ in range(rounds):
             tp_round()
         b.record(stream)
         torch.cuda.synchronize()
-        tp_us = a.elapsed_time(b) * 1e3 / args.tp_share_rounds
+        tp_us = a.elapsed_time(b) * 1e3 / rounds
         tp_bytes = L * Ht * round_bytes_per_head(8, T)
         return {"heads": Ht, "layers": L, "chains": L * Ht, "keep_prev": 8,
                 "us_per_round": tp_us, "rows_heads_per_s": T * Ht * L / (tp_us * 1e-6),
                 "gbps": tp_bytes / (tp_us * 1e-6) / 1e9}
 
-    tp_share = tp4_share = None
-    if args.tp_share_rounds > 0:
-        tp_share = tp_share_of(8)
-        tp4_share = tp_share_of(4)
+    tp_share = tp_share_of(8, args.tp_share_rounds) if args.tp_share_rounds > 0 else None
+    tp4_share = tp_share_of(4, args.tp4_share_rounds) if args.tp4_share_rounds > 0 else None
 
     # batched-decode arm: 15 sessions x 34 layers x 64 heads, one row each, in place
     batched = None
